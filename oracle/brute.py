@@ -1,0 +1,211 @@
+"""Scalar brute force of the LampAttention forward pass for tiny inputs.
+
+Test infrastructure.  This is a second, independent formulation of the method
+of "LampAttention: Look-Ahead Mixed-Precision FlashAttention for Dedicated
+Accelerators" (abstract: 8-bit key-query products and exponentials, adaptive
+16-bit recompute of sensitive sub-blocks; tables 1-6: sub-blocks of tiles),
+under the same readings as ``oracle.lamp`` but sharing none of its code: every
+rounding is done here on exact rationals (``fractions.Fraction``), the e4m3
+rounding picks the nearest entry of the enumerated code table, and everything
+runs in plain Python loops, one entry at a time.  It exists to catch indexing,
+broadcasting and rounding mistakes in the vectorised oracle, and is only
+usable for a few hundred keys.
+"""
+import bisect
+import math
+from fractions import Fraction
+
+LOG2E = 1.4426950408889634
+
+
+def _floor_log2(a):
+    """floor(log2 a) for a positive Fraction, exactly."""
+    e = a.numerator.bit_length() - a.denominator.bit_length()
+    if Fraction(2) ** e > a:
+        e -= 1
+    elif Fraction(2) ** (e + 1) <= a:
+        e += 1
+    return e
+
+
+def _round_binary(a, prec, emin):
+    """Round a Fraction to a binary format with ``prec`` significant bits and
+    smallest normal exponent ``emin`` (nearest, ties to even).  No overflow."""
+    if a == 0:
+        return Fraction(0)
+    sign = -1 if a < 0 else 1
+    a = abs(a)
+    e = max(_floor_log2(a), emin)
+    unit = Fraction(2) ** (e - prec + 1)
+    n = a / unit
+    q, rem = divmod(n.numerator, n.denominator)
+    twice = 2 * rem
+    if twice > n.denominator or (twice == n.denominator and q % 2 == 1):
+        q += 1
+    return sign * q * unit
+
+
+def to_f32(a):
+    """Nearest fp32 value of an exact rational (inf beyond the range)."""
+    r = _round_binary(Fraction(a), 24, -126)
+    if abs(r) >= Fraction(2) ** 128:
+        return math.inf if r > 0 else -math.inf
+    return r
+
+
+def to_bf16(a):
+    """Nearest bfloat16 value of an exact rational."""
+    return _round_binary(Fraction(a), 8, -126)
+
+
+def _e4m3_table():
+    """Positive finite e4m3fn values, indexed by code 0..126."""
+    vals = []
+    for code in range(127):
+        ef, m = code >> 3, code & 7
+        if ef == 0:
+            vals.append(Fraction(m, 512))
+        else:
+            vals.append((1 + Fraction(m, 8)) * Fraction(2) ** (ef - 7))
+    return vals
+
+
+E4M3_TABLE = _e4m3_table()
+
+
+def to_e4m3(a):
+    """Nearest e4m3fn value (ties to the even code), saturating at 448."""
+    a = Fraction(a)
+    mag = abs(a)
+    hi = bisect.bisect_left(E4M3_TABLE, mag)      # first code with value >= mag
+    if hi == len(E4M3_TABLE):
+        v = E4M3_TABLE[-1]                          # beyond 448: saturate
+    elif hi == 0 or E4M3_TABLE[hi] == mag:
+        v = E4M3_TABLE[hi]
+    else:
+        lo = hi - 1
+        dl, dh = mag - E4M3_TABLE[lo], E4M3_TABLE[hi] - mag
+        if dl < dh or (dl == dh and lo % 2 == 0):
+            v = E4M3_TABLE[lo]
+        else:
+            v = E4M3_TABLE[hi]
+    return -v if a < 0 else v
+
+
+def _exp2_f32(x):
+    """fp32 exp2 of an fp32 argument (fp64 pow rounded once more to fp32)."""
+    if x == -math.inf:
+        return Fraction(0)
+    try:
+        return to_f32(Fraction(math.pow(2.0, float(x))))
+    except OverflowError:
+        return math.inf
+
+
+def _bf16(bits):
+    """Exact value of a bfloat16 bit pattern."""
+    bits = int(bits)
+    sign = -1 if bits & 0x8000 else 1
+    ef = (bits >> 7) & 0xFF
+    m = bits & 0x7F
+    if ef == 0:
+        return sign * Fraction(m, 128) * Fraction(2) ** -126
+    return sign * (1 + Fraction(m, 128)) * Fraction(2) ** (ef - 127)
+
+
+def brute_lamp(q_bits, k_bits, v_bits, causal, window, delta, tau):
+    """Whole forward pass; returns (out as nested lists of float, mask dict).
+
+    mask[(b, hq, r, t)] = byte for visited tiles only.
+    """
+    B, Hq, S, D = (len(q_bits), len(q_bits[0]), len(q_bits[0][0]), len(q_bits[0][0][0]))
+    Hkv = len(k_bits[0])
+    G = Hq // Hkv
+    q = [[[[_bf16(x) for x in row] for row in h] for h in bb] for bb in q_bits]
+    k = [[[[_bf16(x) for x in row] for row in h] for h in bb] for bb in k_bits]
+    v = [[[[_bf16(x) for x in row] for row in h] for h in bb] for bb in v_bits]
+
+    def scales(t, b, h):
+        a = max(abs(x) for row in t[b][h] for x in row)
+        if a == 0:
+            return Fraction(1), Fraction(1)
+        return to_f32(a / 448), to_f32(Fraction(448) / a)
+
+    def quant(t, b, h):
+        _, inv = scales(t, b, h)
+        return [[to_e4m3(to_f32(x * inv)) for x in row] for row in t[b][h]]
+
+    L = Fraction(LOG2E / math.sqrt(D))                     # fp64 value, exact
+    c16 = to_f32(L)
+    T2 = to_f32(Fraction(16 * float(tau) * LOG2E)) if math.isfinite(16 * float(tau) * LOG2E) \
+        else (math.inf if tau > 0 else -math.inf)
+
+    def vis(i, j):
+        if i >= S or j >= S:
+            return False
+        if causal and j > i:
+            return False
+        if window > 0 and i - j >= window:
+            return False
+        return True
+
+    nT = (S + 63) // 64
+    out = [[[[0.0] * D for _ in range(S)] for _ in range(Hq)] for _ in range(B)]
+    mask = {}
+    for b in range(B):
+        for hq in range(Hq):
+            hk = hq // G
+            q8, k8 = quant(q, b, hq), quant(k, b, hk)
+            sq, _ = scales(q, b, hq)
+            sk, _ = scales(k, b, hk)
+            c8 = to_f32(Fraction(float(sq) * float(sk) * float(L)))   # fp64 product, then fp32
+            for r in range(nT):
+                rows = [i for i in range(64 * r, 64 * r + 64) if i < S]
+                m = {i: -math.inf for i in rows}
+                ell = {i: Fraction(0) for i in rows}
+                acc_o = {i: [Fraction(0)] * D for i in rows}
+                for t in range(nT):
+                    keys = list(range(64 * t, 64 * t + 64))
+                    if not any(vis(i, j) for i in rows for j in keys):
+                        continue
+                    acc8, s2 = {}, {}
+                    for i in rows:
+                        for j in keys:
+                            if vis(i, j):
+                                a = sum(q8[i][d] * k8[j][d] for d in range(D))
+                                acc8[i, j] = to_f32(a)
+                                s2[i, j] = to_f32(acc8[i, j] * c8)
+                    m_new = {}
+                    for i in rows:
+                        cand = [s2[i, j] for j in keys if (i, j) in s2]
+                        m_new[i] = max([m[i]] + cand) if cand else m[i]
+                    p, flags = {}, [False] * 4
+                    for (i, j), a in acc8.items():
+                        e = _exp2_f32(to_f32(a * c8 - m_new[i]))
+                        p8 = to_e4m3(e)
+                        p[i, j] = p8
+                        active = (delta <= 0) or (p8 >= Fraction(delta))
+                        if active and abs(s2[i, j]) >= T2:
+                            flags[(j - 64 * t) // 16] = True
+                    for (i, j) in list(p):
+                        c = (j - 64 * t) // 16
+                        if flags[c]:
+                            a16 = to_f32(sum(q[b][hq][i][d] * k[b][hk][j][d] for d in range(D)))
+                            p[i, j] = to_bf16(_exp2_f32(to_f32(a16 * c16 - m_new[i])))
+                    for i in rows:
+                        if m_new[i] == -math.inf:
+                            continue
+                        alpha = Fraction(0) if m[i] == -math.inf else \
+                            Fraction(math.pow(2.0, float(m[i] - m_new[i])))
+                        ell[i] = alpha * ell[i]
+                        acc_o[i] = [alpha * o for o in acc_o[i]]
+                        for j in keys:
+                            if (i, j) in p:
+                                ell[i] += p[i, j]
+                                vj = v[b][hk][j]
+                                acc_o[i] = [o + p[i, j] * vj[d] for d, o in enumerate(acc_o[i])]
+                        m[i] = m_new[i]
+                    mask[b, hq, r, t] = 0x80 | sum(int(f) << c for c, f in enumerate(flags))
+                for i in rows:
+                    out[b][hq][i] = [float(to_f32(o / ell[i])) for o in acc_o[i]]
+    return out, mask

@@ -1,0 +1,349 @@
+"""LampAttention forward pass, step by step (oracle; test infrastructure).
+
+Source: "LampAttention: Look-Ahead Mixed-Precision FlashAttention for
+Dedicated Accelerators".  The abstract fixes the pipeline: a FlashAttention
+whose key-query products are accumulated and whose exponentials are evaluated
+in 8-bit formats, after which sensitive sub-blocks are identified adaptively
+and recomputed in 16-bit formats.  The title calls the identification
+"look-ahead".  Tables 1-6 count "16-bit sub-blocks per tile" (0 / 1 / 2+), so
+the decision unit is a sub-block of a tile.  Every table and figure caption
+runs the method with two parameters, delta = 2^-8 and tau = 2^-1; figures 6
+and 7 contrast delta = 2^-8 with a "disabled first stage", so delta belongs to
+a first stage of the test and tau to a second.
+
+The pages give no formula, format or tile size.  The readings taken here
+(each one a plain choice the rest of the pages supports):
+
+* geometry: 64 x 64 tiles of (query rows, keys), each split into four
+  64 x 16 sub-blocks; KV tiles of a row block are visited in ascending order;
+* 8-bit format e4m3fn for Q, K and the exponentials; per-(batch, head)
+  amax/448 scales for Q and K; the 8-bit key-query products are summed
+  exactly and rounded once to fp32 (no 8-bit accumulator exists on the GPU,
+  and the logit itself is not re-rounded to 8 bits);
+* 16-bit format bf16 (the inputs' own format) for the recompute, with its
+  exponentials rounded to bf16;
+* logits are kept in the log2 domain: s = acc * c with c = log2(e)/sqrt(D)
+  times the two scales; the running row max comes from the 8-bit logits only
+  (the recompute reuses it, so a 16-bit weight may exceed 1);
+* first stage (delta): an entry is active iff its 8-bit exponential p8 >= delta
+  (delta <= 0 disables the stage: every visible entry is active);
+* second stage (tau): an active entry is sensitive iff its logit magnitude is
+  at least T2 = 16 * tau * log2(e) in the log2 domain -- the first-order
+  relative error of exp(s) under an 8-bit logit error of relative size 2^-4
+  (the e4m3 unit roundoff) is 2^-4 * |s|, compared with tau;
+* a sub-block is flagged (recomputed in 16-bit) iff it holds a sensitive entry.
+
+Masking: causal (key j visible to query i iff j <= i) and an optional sliding
+window W (additionally i - j < W).  GQA: query head hq reads kv head hq // G.
+"""
+import math
+
+import numpy as np
+
+from .formats import (bf16_bits_to_f64, e4m3_encode, exp2_f32, fl32, fma32,
+                      round_bf16, round_e4m3)
+
+LOG2E = 1.4426950408889634          # fp64 nearest to log2(e)
+BR = 64                             # query rows per tile
+BC = 64                             # keys per tile
+SBW = 16                            # keys per sub-block
+NSB = BC // SBW                     # sub-blocks per tile
+
+
+# --------------------------------------------------------------------------
+# Step 1-2: per-head scales and e4m3 quantisation of Q and K
+# --------------------------------------------------------------------------
+def head_scales(bits):
+    """amax scales per (batch, head) of a bf16 tensor [B, H, S, D].
+
+    a = max |x| over the head's slab (exact).  If a == 0 the scale and its
+    inverse are 1, otherwise scale = fl32(a / 448) and inv = fl32(448 / a).
+    """
+    x = bf16_bits_to_f64(bits)
+    a = np.abs(x).max(axis=(2, 3))
+    safe = np.where(a > 0, a, 1.0)
+    scale = np.where(a > 0, fl32(safe / 448.0), 1.0)
+    inv = np.where(a > 0, fl32(448.0 / safe), 1.0)
+    return scale, inv
+
+
+def quantize(bits):
+    """e4m3 quantisation of a bf16 tensor with per-head amax scales.
+
+    x8 = E4M3(fl32(x * inv)).  Returns (values, byte codes, scale, inv).
+    """
+    x = bf16_bits_to_f64(bits)
+    scale, inv = head_scales(bits)
+    y = fl32(x * inv[:, :, None, None])
+    vals = round_e4m3(y)
+    return vals, e4m3_encode(vals), scale, inv
+
+
+# --------------------------------------------------------------------------
+# Step 3: constants of one (batch, query head)
+# --------------------------------------------------------------------------
+def log2_scale(D):
+    """L_D = log2(e) / sqrt(D) in fp64 (the softmax scale in the log2 domain)."""
+    return LOG2E / math.sqrt(D)
+
+
+def logit_constants(D, sq, sk):
+    """c8 multiplies the 8-bit accumulator, c16 the 16-bit one (both fp32)."""
+    L = log2_scale(D)
+    c8 = float(fl32(float(sq) * float(sk) * L))
+    c16 = float(fl32(L))
+    return c8, c16
+
+
+def tau_threshold(tau):
+    """T2 = fl32(16 * tau * log2 e); +inf disables the second stage, <= 0 passes all."""
+    with np.errstate(over="ignore"):
+        return float(fl32(16.0 * float(tau) * LOG2E))
+
+
+# --------------------------------------------------------------------------
+# Geometry
+# --------------------------------------------------------------------------
+def visible(rows, cols, causal, window):
+    """vis[i, j] for query indices ``rows`` and key indices ``cols``."""
+    i = rows[:, None]
+    j = cols[None, :]
+    v = np.ones((rows.size, cols.size), dtype=bool)
+    if causal:
+        v &= j <= i
+    if window > 0:
+        v &= (i - j) < window
+    return v
+
+
+def n_tiles(S):
+    return (S + BC - 1) // BC
+
+
+# --------------------------------------------------------------------------
+# Step 4: the two-stage look-ahead test of one tile
+# --------------------------------------------------------------------------
+def stage_one(p8, vis, delta):
+    """Active entries: visible and (first stage disabled or p8 >= delta)."""
+    if delta <= 0:
+        return vis.copy()
+    return vis & (p8 >= delta)
+
+
+def stage_two(active, s2, T2):
+    """Sensitive entries: active and |s2| >= T2."""
+    return active & (np.abs(s2) >= T2)
+
+
+def subblock_flags(sens):
+    """flag[c] = some sensitive entry among keys [16c, 16c + 16) of the tile."""
+    n = sens.shape[1]
+    return [bool(sens[:, c * SBW:min((c + 1) * SBW, n)].any()) if c * SBW < n else False
+            for c in range(NSB)]
+
+
+def _ulp_step(x, k):
+    """Move fp32 values k representable steps (k may be negative)."""
+    y = np.asarray(x, dtype=np.float64).astype(np.float32)
+    target = np.float32(np.inf) if k > 0 else np.float32(-np.inf)
+    for _ in range(abs(k)):
+        y = np.nextafter(y, target)
+    return y.astype(np.float64)
+
+
+def fragile_flags(e, s2, vis, delta, T2, k):
+    """Per sub-block: could moving each test statistic by k fp32 ulps flip the flag?
+
+    Both stages are monotone in their statistic (the fp32 exponential e and
+    |s2|), so the flag computed with every statistic pushed down by k ulps and
+    the flag with every statistic pushed up bound all flags reachable by such
+    perturbations.
+    """
+    res = []
+    for sgn in (-k, k):
+        e_k = _ulp_step(e, sgn)
+        s_k = _ulp_step(np.abs(s2), sgn)
+        act = stage_one(round_e4m3(e_k), vis, delta)
+        res.append(subblock_flags(act & (s_k >= T2)))
+    return [lo != hi for lo, hi in zip(*res)]
+
+
+# --------------------------------------------------------------------------
+# The forward pass of one unit (batch b, query head hq, row block r)
+# --------------------------------------------------------------------------
+def run_unit(ctx, b, hq, r, flag_override=None, trace=None):
+    """Process one 64-row query block through its visible KV tiles.
+
+    Returns (out rows fp32 values [n, D], {t: mask byte}).  ``flag_override``
+    maps t -> 4-bit flags replacing the computed ones (used to replay a run
+    whose flags are given).  ``trace`` (a list) receives per-tile records.
+    """
+    S, D, G = ctx["S"], ctx["D"], ctx["G"]
+    hk = hq // G
+    rows = np.arange(r * BR, min(r * BR + BR, S))
+    nr = rows.size
+    c8, c16 = logit_constants(D, ctx["sq"][b, hq], ctx["sk"][b, hk])
+    T2 = ctx["T2"]
+    delta = ctx["delta"]
+    q8 = ctx["q8"][b, hq, rows]           # e4m3 values (fp64)
+    q16 = ctx["q16"][b, hq, rows]         # bf16 values (fp64)
+
+    m = np.full(nr, -np.inf)              # running row max (8-bit logits, log2 domain)
+    ell = np.zeros(nr)                    # running sum of weights (fp64)
+    O = np.zeros((nr, D))                 # running weighted sum of V rows (fp64)
+    mask = {}
+    for t in range(n_tiles(S)):
+        cols = np.arange(t * BC, min(t * BC + BC, S))
+        vis = visible(rows, cols, ctx["causal"], ctx["window"])
+        if not vis.any():
+            continue
+        k8 = ctx["k8"][b, hk, cols]
+        # (a) 8-bit products, summed exactly (all partial sums are multiples of
+        #     2^-18 below 2^26, so fp64 holds them exactly), rounded to fp32.
+        acc8 = fl32(q8 @ k8.T)
+        s2 = np.where(vis, fl32(acc8 * c8), -np.inf)
+        # (b) running max over the 8-bit logits of this tile
+        m_new = np.maximum(m, s2.max(axis=1))
+        live = m_new > -np.inf
+        safe_m = np.where(live, m_new, 0.0)
+        # (c) 8-bit exponentials against the running max
+        x = np.where(vis, fma32(acc8, c8, -safe_m[:, None]), -np.inf)
+        e = np.where(vis, exp2_f32(x), 0.0)
+        p8 = round_e4m3(e)
+        # (d) look-ahead test, first and second stage
+        active = stage_one(p8, vis, delta)
+        sens = stage_two(active, s2, T2)
+        flags = subblock_flags(sens)
+        if flag_override is not None and t in flag_override:
+            flags = [bool((flag_override[t] >> c) & 1) for c in range(NSB)]
+        # (e) flagged sub-blocks are recomputed in 16-bit
+        p = np.where(vis, p8, 0.0)
+        for c in range(NSB):
+            if not flags[c]:
+                continue
+            sub = slice(c * SBW, min((c + 1) * SBW, cols.size))
+            k16 = ctx["k16"][b, hk, cols[sub]]
+            acc16 = fl32(q16 @ k16.T)
+            x16 = fma32(acc16, c16, -safe_m[:, None])
+            p16 = round_bf16(exp2_f32(x16))
+            p[:, sub] = np.where(vis[:, sub], p16, 0.0)
+        # (f) online-softmax rescale and P.V
+        alpha = np.where(np.isneginf(m), 0.0, np.exp2(m - safe_m))
+        alpha = np.where(live, alpha, 1.0)
+        ell = alpha * ell + p.sum(axis=1)
+        O = alpha[:, None] * O + p @ ctx["v"][b, hk, cols]
+        m = m_new
+        # (g) mask byte: bit 7 = tile visited, bit c = sub-block c in 16-bit
+        byte = 0x80
+        for c in range(NSB):
+            byte |= int(flags[c]) << c
+        mask[t] = byte
+        if trace is not None:
+            trace.append(dict(t=t, cols=cols, vis=vis, acc8=acc8, s2=s2, e=e,
+                              p8=p8, p=p, flags=flags, m_new=m_new.copy(), T2=T2))
+    # Step 5: normalise
+    out = fl32(O / ell[:, None])
+    if trace is not None:
+        trace.append(dict(final=True, m=m, ell=ell, O=O))
+    return out, mask
+
+
+# --------------------------------------------------------------------------
+# Whole forward pass
+# --------------------------------------------------------------------------
+def prepare(q_bits, k_bits, v_bits, causal, window, delta, tau):
+    """Quantise Q and K and collect everything the units read."""
+    B, Hq, S, D = q_bits.shape
+    Hkv = k_bits.shape[1]
+    assert Hq % Hkv == 0 and k_bits.shape == v_bits.shape == (B, Hkv, S, D)
+    q8, _, sq, _ = quantize(q_bits)
+    k8, _, sk, _ = quantize(k_bits)
+    return dict(B=B, Hq=Hq, Hkv=Hkv, S=S, D=D, G=Hq // Hkv,
+                causal=bool(causal), window=int(window),
+                delta=float(delta), T2=tau_threshold(tau),
+                q8=q8, k8=k8, sq=sq, sk=sk,
+                q16=bf16_bits_to_f64(q_bits), k16=bf16_bits_to_f64(k_bits),
+                v=bf16_bits_to_f64(v_bits))
+
+
+def all_units(B, Hq, S):
+    nr = n_tiles(S)
+    return [(b, h, r) for b in range(B) for h in range(Hq) for r in range(nr)]
+
+
+def lamp_forward(q_bits, k_bits, v_bits, causal=True, window=0, delta=2.0 ** -8,
+                 tau=2.0 ** -1, units=None, flag_override=None):
+    """The LampAttention forward pass over ``units`` (default: all).
+
+    q_bits [B, Hq, S, D], k_bits / v_bits [B, Hkv, S, D]: bf16 bit patterns.
+    Returns (out fp32 [B, Hq, S, D] (rows of units not computed are NaN),
+    mask uint8 [B, Hq, nT, nT]).  ``flag_override`` is a mask array of the
+    same shape whose low 4 bits replace the computed flags of visited tiles.
+    """
+    ctx = prepare(q_bits, k_bits, v_bits, causal, window, delta, tau)
+    B, Hq, S, D = ctx["B"], ctx["Hq"], ctx["S"], ctx["D"]
+    nT = n_tiles(S)
+    out = np.full((B, Hq, S, D), np.nan, dtype=np.float32)
+    mask = np.zeros((B, Hq, nT, nT), dtype=np.uint8)
+    for (b, hq, r) in (units if units is not None else all_units(B, Hq, S)):
+        ov = None
+        if flag_override is not None:
+            ov = {t: int(flag_override[b, hq, r, t]) & 0xF for t in range(nT)}
+        o, mk = run_unit(ctx, b, hq, r, flag_override=ov)
+        out[b, hq, r * BR:r * BR + o.shape[0]] = o.astype(np.float32)
+        for t, byte in mk.items():
+            mask[b, hq, r, t] = byte
+    return out, mask
+
+
+def unit_fragility(ctx, b, hq, r, k=1):
+    """For one unit: {t: 4-bit set of sub-blocks whose flag is within k ulps}."""
+    trace = []
+    run_unit(ctx, b, hq, r, trace=trace)
+    res = {}
+    for rec in trace:
+        if rec.get("final"):
+            continue
+        fr = fragile_flags(rec["e"], rec["s2"], rec["vis"], ctx["delta"], rec["T2"], k)
+        res[rec["t"]] = sum(int(f) << c for c, f in enumerate(fr))
+    return res
+
+
+# --------------------------------------------------------------------------
+# Counters reported with every run (tables 1-6 "16-bit sub-blocks per tile")
+# --------------------------------------------------------------------------
+def subblock_stats(mask, S, causal, window):
+    """Histogram and recompute fractions from a mask, by brute force on vis.
+
+    Returns dict(hist=[n0..n4] over visited tiles, visited_tiles,
+    visited_subblocks, flagged_subblocks, visible_entries,
+    flagged_entries, r_sb, r_e, pages_buckets=[0, 1, 2+] fractions).
+    """
+    B, Hq, nT, _ = mask.shape
+    hist = np.zeros(5, dtype=np.int64)
+    vsb = fsb = ve = fe = 0
+    for r in range(nT):
+        rows = np.arange(r * BR, min(r * BR + BR, S))
+        for t in range(nT):
+            cols = np.arange(t * BC, min(t * BC + BC, S))
+            vis = visible(rows, cols, causal, window)
+            if not vis.any():
+                continue
+            counts = [int(vis[:, c * SBW:(c + 1) * SBW].sum()) for c in range(NSB)]
+            bytes_ = mask[:, :, r, t].astype(np.int64)
+            for c in range(NSB):
+                if counts[c] == 0:
+                    continue
+                bit = (bytes_ >> c) & 1
+                vsb += B * Hq
+                fsb += int(bit.sum())
+                ve += counts[c] * B * Hq
+                fe += counts[c] * int(bit.sum())
+            pc = sum(((bytes_ >> c) & 1) for c in range(NSB))
+            for n in range(5):
+                hist[n] += int((pc == n).sum())
+    vt = int(hist.sum())
+    return dict(hist=hist.tolist(), visited_tiles=vt, visited_subblocks=vsb,
+                flagged_subblocks=fsb, visible_entries=ve, flagged_entries=fe,
+                r_sb=fsb / vsb if vsb else 0.0, r_e=fe / ve if ve else 0.0,
+                pages_buckets=[hist[0] / vt, hist[1] / vt, hist[2:].sum() / vt] if vt else [0, 0, 0])
