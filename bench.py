@@ -1,0 +1,198 @@
+"""Bench of the LampAttention forward pass on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload qwen3-8b]
+                    [--delta D] [--tau T] [--no-cpu-baseline]
+
+A step is one lamp_attn_fwd call (quantisation pass, V transpose and the fused
+attention kernel) over one batch of seeded synthetic input already resident
+in HBM.  Prints one JSON line with the throughput, the roofline of the
+dominant kernel (the fused attention kernel, timed with HIP events on the
+stream it is launched on), the recompute statistics and the CPU oracle timed
+on a bounded sample of the same workload.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "attn fwd TFLOP/s + % blended FP8/bf16 roofline; 16-bit sub-block fraction"
+PEAK_FP8 = 5.0e15          # MI355X dense FP8 matrix FLOP/s
+PEAK_BF16 = 2.5e15         # MI355X dense bf16 matrix FLOP/s
+PEAK_HBM = 8.0e12          # MI355X HBM3E bytes/s
+
+
+def visible_pairs_per_head(S, causal, window):
+    """Exact count of visible (query, key) pairs of one head."""
+    i = np.arange(S, dtype=np.int64)
+    hi = i if causal else np.full(S, S - 1)
+    lo = np.maximum(0, i - window + 1) if window > 0 else np.zeros(S, dtype=np.int64)
+    return int(np.maximum(0, hi - lo + 1).sum())
+
+
+def unit_pairs(r, S, causal, window):
+    i = np.arange(r * 64, min(r * 64 + 64, S), dtype=np.int64)
+    hi = i if causal else np.full(i.size, S - 1)
+    lo = np.maximum(0, i - window + 1) if window > 0 else np.zeros(i.size, dtype=np.int64)
+    return int(np.maximum(0, hi - lo + 1).sum())
+
+
+_CTX = None
+
+
+def _oracle_unit(unit):
+    """Worker: one (b, hq, r) unit through the oracle (CPU baseline only).
+    The oracle context is inherited from the parent through fork."""
+    from oracle import lamp as L
+    L.run_unit(_CTX, *unit)
+    return unit
+
+
+def cpu_baseline(q, k, v, cfg, delta, tau, budget_s, cores):
+    """Time the oracle on sampled units of the same workload (reported baseline)."""
+    global _CTX
+    import multiprocessing as mp
+    from threadpoolctl import threadpool_limits
+    from oracle import lamp as L
+    threadpool_limits(1)
+    _CTX = L.prepare(q, k, v, cfg["causal"], cfg["window"], delta, tau)
+    B, Hq, S, D = q.shape
+    nT = L.n_tiles(S)
+    rng = np.random.default_rng(123)
+    # first a calibration unit, then as many random units as fit the budget
+    units = [(int(rng.integers(B)), int(rng.integers(Hq)), int(rng.integers(nT)))
+             for _ in range(4096)]
+    t0 = time.perf_counter()
+    _oracle_unit(units[0])
+    one = max(time.perf_counter() - t0, 1e-3)
+    n = max(cores, min(len(units), int(budget_s * cores / one)))
+    sample = units[:n]
+    t0 = time.perf_counter()
+    if cores > 1:
+        with mp.get_context("fork").Pool(cores) as pool:
+            for _ in pool.imap_unordered(_oracle_unit, sample, chunksize=1):
+                pass
+    else:
+        for u in sample:
+            _oracle_unit(u)
+    wall = time.perf_counter() - t0
+    flops = sum(4.0 * D * unit_pairs(r, S, cfg["causal"], cfg["window"]) for (_, _, r) in sample)
+    return dict(value=flops / wall / 1e12, unit="TFLOP/s", cores=cores, kind="oracle",
+                sample=f"{len(sample)} random (batch, head, 64-row block) units of the same "
+                       f"workload ({flops / 1e9:.2f} GFLOP nominal), {wall:.1f} s wall",
+                wall_s=wall)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="qwen3-8b")
+    ap.add_argument("--delta", type=float, default=2.0 ** -8)
+    ap.add_argument("--tau", type=float, default=2.0 ** -1)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=15.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
+              "the path is single-GPU by design", file=sys.stderr)
+        sys.exit(2)
+
+    from inputs import make_config_inputs
+
+    q, k, v, cfg = make_config_inputs(args.workload)
+    B, Hq, S, D = q.shape
+    Hkv = k.shape[1]
+    causal, window = cfg["causal"], cfg["window"]
+
+    # The CPU baseline runs first, in worker processes forked before this
+    # process touches the GPU.
+    cb = None
+    if not args.no_cpu_baseline:
+        cores = max(1, min(len(os.sched_getaffinity(0)), 16))
+        cb = cpu_baseline(q, k, v, cfg, args.delta, args.tau, args.cpu_budget, cores)
+        cb.pop("wall_s", None)
+
+    import torch
+    import mixed_precision_attention_lamp_amd as lamp
+    dev = torch.device("cuda:0")
+
+    def dev_t(x):
+        return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    qd, kd, vd = dev_t(q), dev_t(k), dev_t(v)
+    nT = lamp.n_tiles(S)
+    out = torch.empty((B, Hq, S, D), dtype=torch.float32, device=dev)
+    mask = torch.empty((B, Hq, nT, nT), dtype=torch.uint8, device=dev)
+
+    def step():
+        lamp.lamp_attn_fwd(qd, kd, vd, out, causal, window, args.delta, args.tau, mask)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    lamp.lamp_set_timing(1)
+    lamp.lamp_read_timing()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for _ in range(args.steps):
+        step()
+    end.record()
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(end)
+    prep_ms, attn_ms, ncalls = lamp.lamp_read_timing()
+    lamp.lamp_set_timing(0)
+    ms_per_step = total_ms / args.steps
+    attn_ms_avg = attn_ms / max(ncalls, 1)
+    prep_ms_avg = prep_ms / max(ncalls, 1)
+
+    stats = lamp.subblock_stats(mask, S, causal, window)
+    pairs = visible_pairs_per_head(S, causal, window) * B * Hq
+    assert pairs == stats["visible_entries"], (pairs, stats["visible_entries"])
+    f_nom = 4.0 * D * pairs
+    f_qk8 = 2.0 * D * pairs
+    f_pv = 2.0 * D * pairs
+    f_qk16 = 2.0 * D * stats["flagged_entries"]
+    f_alg = f_qk8 + f_pv + f_qk16
+    t_mfma = f_qk8 / PEAK_FP8 + (f_pv + f_qk16) / PEAK_BF16
+    blended_peak = f_alg / t_mfma
+    nq, nk = B * Hq * S * D, B * Hkv * S * D
+    quant_bytes = 3.0 * (nq + nk)
+    t_roof = t_mfma + quant_bytes / PEAK_HBM
+    achieved = f_alg / (attn_ms_avg * 1e-3)
+    res = {
+        "metric": METRIC,
+        "value": f_nom / (ms_per_step * 1e-3) / 1e12,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "e4m3+bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{args.workload}: {cfg['desc']}", "B": B, "Hq": Hq, "Hkv": Hkv,
+                   "S": S, "D": D, "causal": causal, "window": window,
+                   "delta": args.delta, "tau": args.tau},
+        "roofline": {"bound": "mfma", "achieved": achieved / 1e12, "peak": blended_peak / 1e12,
+                     "unit": "TFLOP/s", "frac": achieved / blended_peak, "traffic": None},
+        "blended_roofline_frac": t_roof / (ms_per_step * 1e-3),
+        "kernel_ms": {"attention": attn_ms_avg, "quantise_and_transpose": prep_ms_avg},
+        "recompute": {"r_sb": stats["r_sb"], "r_e": stats["r_e"], "hist_0_to_4": stats["hist"],
+                      "tiles_0_1_2plus": stats["pages_buckets"]},
+    }
+    res["cpu_baseline"] = cb
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

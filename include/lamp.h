@@ -1,0 +1,136 @@
+/*
+ * lamp.h -- C ABI of the MI355X (gfx950) LampAttention forward pass.
+ *
+ * The method is the one of "LampAttention: Look-Ahead Mixed-Precision
+ * FlashAttention for Dedicated Accelerators" (abstract): a FlashAttention whose
+ * key-query products are accumulated and whose exponentials are evaluated in
+ * 8-bit formats; sensitive sub-blocks are then identified (look-ahead test with
+ * parameters delta and tau, figure 1-8 captions) and recomputed in 16-bit
+ * formats.  Tables 1-6 report the number of 16-bit sub-blocks per tile.
+ *
+ * Readings this library implements (the pages give no formula, format or size):
+ *   - tiles of 64 query rows x 64 keys, four 64 x 16 sub-blocks per tile;
+ *   - 8-bit = OCP e4m3fn with per-(batch, head) amax/448 scales for Q and K;
+ *     products summed in fp32, exponentials rounded to e4m3;
+ *   - 16-bit = bf16 operands, fp32 accumulation, exponentials rounded to bf16;
+ *   - logits in the log2 domain; running row max from the 8-bit logits;
+ *   - first stage: p8 >= delta (delta <= 0 disables it);
+ *     second stage: |s| >= 16 * tau * log2(e) (log2-domain logit);
+ *     a sub-block is recomputed iff some entry passes both stages.
+ *
+ * Conventions for every entry point
+ *   - Tensors are caller-owned, contiguous, row-major.  Q is [B, Hq, S, D],
+ *     K and V are [B, Hkv, S, D], all bf16 (raw 16-bit patterns).  Query head
+ *     hq reads kv head hq / (Hq / Hkv).  Device pointers must be 16-byte aligned.
+ *   - Calls are asynchronous on the library's current stream (lamp_set_stream);
+ *     outputs are valid after that stream is synchronised.  A device fault
+ *     surfaces at that synchronisation, not at the call.
+ *   - Arguments are validated before any HIP call; on a validation error
+ *     nothing is launched and nothing is written.  The return value is LAMP_OK
+ *     or a negative error code; lamp_last_error() gives a message.
+ *   - The library owns one device workspace per device (Q8, K8, a transposed
+ *     copy of V, scales); it only grows, and lamp_release_workspace() frees it.
+ *   - Inputs must be finite.  Not thread-safe for concurrent calls sharing a
+ *     device; the stream and the last error are per host thread.
+ */
+#ifndef LAMP_H
+#define LAMP_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+    LAMP_OK = 0,
+    LAMP_ERR_INVALID = -1,      /* bad pointer, size, flag or parameter */
+    LAMP_ERR_UNSUPPORTED = -2,  /* valid request this build does not handle (e.g. D not in {64,128}) */
+    LAMP_ERR_HIP = -3,          /* a HIP runtime call failed (message has hipGetErrorString) */
+    LAMP_ERR_NOMEM = -4         /* workspace allocation failed or exceeded LAMP_WORKSPACE_LIMIT_BYTES */
+};
+
+/* Forward pass.  ("LampAttention", abstract; tables 1-6 for the mask.)
+ *   q, k, v   bf16 device tensors as above.
+ *   out       fp32 device tensor [B, Hq, S, D]: softmax(QK^T/sqrt(D)) V as computed
+ *             by the method.
+ *   causal    0 or 1: key j is visible to query i iff j <= i.
+ *   window    0 = none; > 0 requires causal = 1 and additionally i - j < window.
+ *   delta     first-stage threshold on the 8-bit exponential; <= 0 disables the stage.
+ *   tau       second-stage parameter; +inf disables it (pure 8-bit attention);
+ *             tau <= 0 with delta <= 0 sends every visited sub-block to 16-bit.
+ *   subblock_mask_out  nullable; uint8 device tensor [B, Hq, nT, nT], nT = ceil(S/64).
+ *             Byte (b, hq, r, t): bit 7 = tile (query rows 64r.., keys 64t..) visited,
+ *             bit c (0..3) = sub-block c (keys 64t+16c .. 64t+16c+15) recomputed in
+ *             16-bit; 0 for tiles that hold no visible entry.
+ * Sizes: B, Hq, Hkv, S >= 1; Hq % Hkv == 0; D in {64, 128}; B*Hq*S*D < 2^31. */
+int lamp_attn_fwd(const void* q, const void* k, const void* v, float* out,
+                  int B, int Hq, int Hkv, int S, int D,
+                  int causal, int window, float delta, float tau,
+                  uint8_t* subblock_mask_out);
+
+/* Per-tile count of 16-bit sub-blocks, reduced on the device ("16-bit sub-blocks
+ * per tile", tables 1-6).  mask is the output of lamp_attn_fwd for the same
+ * B, Hq, S, causal, window.  stats_out: int64 device array of LAMP_STATS_LEN:
+ *   [0..4] tiles with 0..4 sub-blocks in 16-bit (visited tiles only),
+ *   [5] visited tiles, [6] visited sub-blocks (holding a visible entry),
+ *   [7] sub-blocks in 16-bit, [8] visible entries, [9] visible entries in
+ *   16-bit sub-blocks.  Overwritten, not accumulated. */
+#define LAMP_STATS_LEN 10
+int lamp_subblock_stats(const uint8_t* subblock_mask, int B, int Hq, int S,
+                        int causal, int window, int64_t* stats_out);
+
+/* The quantisation step on its own (per-head amax scales, e4m3 codes), for tests.
+ * q8 [B,Hq,S,D] and k8 [B,Hkv,S,D] receive e4m3fn byte codes; q_scale [B*Hq] and
+ * k_scale [B*Hkv] receive fl32(amax/448) (1 for an all-zero head).  Device pointers. */
+int lamp_quantize_qk(const void* q, const void* k, int B, int Hq, int Hkv, int S, int D,
+                     uint8_t* q8, uint8_t* k8, float* q_scale, float* k_scale);
+
+/* The device conversions the kernels use, applied elementwise, for tests:
+ *   e4m3[i]  = e4m3fn code of x[i] (nearest even, magnitudes clamped to 448 first),
+ *   e4m3_bf16[i] = bf16 pattern of the value of that code,
+ *   bf16[i]  = bf16 pattern of x[i] (nearest even),
+ *   exp2[i]  = the device fp32 exp2 of x[i].
+ * All device pointers (any may be null), n elements. */
+int lamp_debug_convert(const float* x, int64_t n, uint8_t* e4m3, uint16_t* e4m3_bf16,
+                       uint16_t* bf16, float* exp2);
+
+/* lamp_attn_fwd plus a dump of its per-entry intermediates, for tests on small
+ * shapes (S <= 2048).  For every visible (query i, key j) of head (b, hq):
+ *   acc8_out [B, Hq, S, S] fp32: the 8-bit accumulator sum_d Q8[i,d] K8[j,d];
+ *   p_out    [B, Hq, S, S] bf16 bits: the weight that entered P.V (the 8-bit
+ *            exponential, or the 16-bit one for a recomputed sub-block), relative to
+ *            the running row max at that tile.
+ * Entries of tiles that are not visited are not written. */
+int lamp_debug_attn_dump(const void* q, const void* k, const void* v, float* out,
+                         int B, int Hq, int Hkv, int S, int D,
+                         int causal, int window, float delta, float tau,
+                         uint8_t* subblock_mask_out, float* acc8_out, uint16_t* p_out);
+
+/* Per-kernel timing with HIP events recorded on the library's stream, for
+ * benches.  While enabled (enable = 1), every lamp_attn_fwd call records one
+ * event before its quantisation/transpose kernels, one between them and the
+ * attention kernel and one after it.  lamp_read_timing waits for those
+ * events, returns the summed milliseconds of the two phases and the number of
+ * calls, and starts a new accumulation.  Event objects are created on first
+ * use and reused; at most 4096 calls are recorded between two reads. */
+int lamp_set_timing(int enable);
+int lamp_read_timing(double* prep_ms, double* attn_ms, int* n_calls);
+
+/* Stream for subsequent calls from this host thread (a hipStream_t; null = default). */
+int lamp_set_stream(void* hip_stream);
+
+/* Message of the last non-OK return on this host thread ("" if none). */
+const char* lamp_last_error(void);
+
+/* Free the device workspace (synchronises the device first). */
+void lamp_release_workspace(void);
+
+/* Library version: major * 10000 + minor * 100 + patch. */
+int lamp_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LAMP_H */

@@ -1,0 +1,161 @@
+"""ctypes binding of liblamp.so (include/lamp.h): argument marshalling only.
+
+Every function here has the name of the C entry point it calls.  Tensors are
+torch tensors on the GPU; torch provides device memory and the current
+stream, nothing else.  There is no fallback: if the HIP library is not built,
+or a call fails, a RuntimeError is raised.
+"""
+import ctypes
+import os
+import re
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "liblamp.so")
+HEADER = os.path.join(os.path.dirname(PKG), "include", "lamp.h")
+
+LAMP_OK = 0
+LAMP_ERR_INVALID = -1
+LAMP_ERR_UNSUPPORTED = -2
+LAMP_ERR_HIP = -3
+LAMP_ERR_NOMEM = -4
+LAMP_STATS_LEN = 10
+
+_lib = None
+
+
+class LampError(RuntimeError):
+    def __init__(self, code, msg):
+        super().__init__(f"lamp error {code}: {msg}")
+        self.code = code
+
+
+def load():
+    """Load liblamp.so once (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                           "`python -m mixed_precision_attention_lamp_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i32, f32, i64 = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_int64
+    lib.lamp_attn_fwd.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, f32, f32, vp]
+    lib.lamp_attn_fwd.restype = i32
+    lib.lamp_debug_attn_dump.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, f32, f32,
+                                         vp, vp, vp]
+    lib.lamp_debug_attn_dump.restype = i32
+    lib.lamp_subblock_stats.argtypes = [vp, i32, i32, i32, i32, i32, vp]
+    lib.lamp_subblock_stats.restype = i32
+    lib.lamp_quantize_qk.argtypes = [vp, vp, i32, i32, i32, i32, i32, vp, vp, vp, vp]
+    lib.lamp_quantize_qk.restype = i32
+    lib.lamp_debug_convert.argtypes = [vp, i64, vp, vp, vp, vp]
+    lib.lamp_debug_convert.restype = i32
+    lib.lamp_set_timing.argtypes = [i32]
+    lib.lamp_set_timing.restype = i32
+    lib.lamp_read_timing.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double),
+                                     ctypes.POINTER(ctypes.c_int)]
+    lib.lamp_read_timing.restype = i32
+    lib.lamp_set_stream.argtypes = [vp]
+    lib.lamp_set_stream.restype = i32
+    lib.lamp_last_error.argtypes = []
+    lib.lamp_last_error.restype = ctypes.c_char_p
+    lib.lamp_release_workspace.argtypes = []
+    lib.lamp_release_workspace.restype = None
+    lib.lamp_version.argtypes = []
+    lib.lamp_version.restype = i32
+    _lib = lib
+    return lib
+
+
+def declared_symbols():
+    """Names of the functions include/lamp.h declares."""
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(lamp_\w+)\s*\(", text, re.M)))
+
+
+def _check(rc):
+    if rc != LAMP_OK:
+        raise LampError(rc, load().lamp_last_error().decode())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _sync_stream(lib):
+    import torch
+    lib.lamp_set_stream(ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+
+
+def lamp_version():
+    return load().lamp_version()
+
+
+def lamp_last_error():
+    return load().lamp_last_error().decode()
+
+
+def lamp_release_workspace():
+    load().lamp_release_workspace()
+
+
+def lamp_set_stream(stream):
+    """stream: a torch.cuda.Stream (or None for the default stream)."""
+    _check(load().lamp_set_stream(None if stream is None else ctypes.c_void_p(stream.cuda_stream)))
+
+
+def lamp_set_timing(enable):
+    _check(load().lamp_set_timing(int(enable)))
+
+
+def lamp_read_timing():
+    """(prep_ms_total, attn_ms_total, n_calls) since the last read."""
+    a, b, n = ctypes.c_double(), ctypes.c_double(), ctypes.c_int()
+    _check(load().lamp_read_timing(ctypes.byref(a), ctypes.byref(b), ctypes.byref(n)))
+    return a.value, b.value, n.value
+
+
+def lamp_attn_fwd(q, k, v, out, causal=1, window=0, delta=2.0 ** -8, tau=2.0 ** -1,
+                  subblock_mask_out=None):
+    """q [B,Hq,S,D], k/v [B,Hkv,S,D] bf16; out [B,Hq,S,D] fp32; optional uint8 mask."""
+    lib = load()
+    B, Hq, S, D = q.shape
+    Hkv = k.shape[1]
+    _sync_stream(lib)
+    _check(lib.lamp_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, Hq, Hkv, S, D,
+                             int(causal), int(window), float(delta), float(tau),
+                             _ptr(subblock_mask_out)))
+
+
+def lamp_debug_attn_dump(q, k, v, out, causal, window, delta, tau, subblock_mask_out,
+                         acc8_out, p_out):
+    lib = load()
+    B, Hq, S, D = q.shape
+    Hkv = k.shape[1]
+    _sync_stream(lib)
+    _check(lib.lamp_debug_attn_dump(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, Hq, Hkv, S, D,
+                                    int(causal), int(window), float(delta), float(tau),
+                                    _ptr(subblock_mask_out), _ptr(acc8_out), _ptr(p_out)))
+
+
+def lamp_subblock_stats(subblock_mask, B, Hq, S, causal, window, stats_out):
+    lib = load()
+    _sync_stream(lib)
+    _check(lib.lamp_subblock_stats(_ptr(subblock_mask), B, Hq, S, int(causal), int(window),
+                                   _ptr(stats_out)))
+
+
+def lamp_quantize_qk(q, k, q8, k8, q_scale, k_scale):
+    lib = load()
+    B, Hq, S, D = q.shape
+    Hkv = k.shape[1]
+    _sync_stream(lib)
+    _check(lib.lamp_quantize_qk(_ptr(q), _ptr(k), B, Hq, Hkv, S, D, _ptr(q8), _ptr(k8),
+                                _ptr(q_scale), _ptr(k_scale)))
+
+
+def lamp_debug_convert(x, e4m3=None, e4m3_bf16=None, bf16=None, exp2=None):
+    lib = load()
+    _sync_stream(lib)
+    _check(lib.lamp_debug_convert(_ptr(x), x.numel(), _ptr(e4m3), _ptr(e4m3_bf16), _ptr(bf16),
+                                  _ptr(exp2)))

@@ -1,0 +1,80 @@
+// Device helpers shared by the gfx950 kernels of the LampAttention forward pass.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <type_traits>
+
+namespace lamp {
+
+// Tile geometry ("16-bit sub-blocks per tile", tables 1-6): 64 query rows by
+// 64 keys, split into four sub-blocks of 16 keys.
+constexpr int kTileRows = 64;
+constexpr int kTileKeys = 64;
+constexpr int kSubKeys = 16;
+constexpr int kSubBlocks = kTileKeys / kSubKeys;
+constexpr float kE4M3Max = 448.0f;
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float bf16_bits_to_float(uint32_t h) {
+    return __uint_as_float(h << 16);
+}
+
+// Two fp32 values -> two e4m3fn codes in the low (hi = false) or high half of
+// `old`.  Magnitudes are clamped to 448 first: any value in (448, 464) rounds
+// to 448 under round-to-nearest-even, and nothing here is larger.
+template <bool Hi>
+__device__ __forceinline__ uint32_t cvt_pk_e4m3(float a, float b, uint32_t old) {
+    a = __builtin_fminf(__builtin_fmaxf(a, -kE4M3Max), kE4M3Max);
+    b = __builtin_fminf(__builtin_fmaxf(b, -kE4M3Max), kE4M3Max);
+    return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, (int)old, Hi);
+}
+
+// Same without the clamp, for values known to lie in [0, 1 + 2^-20].
+template <bool Hi>
+__device__ __forceinline__ uint32_t cvt_pk_e4m3_unit(float a, float b, uint32_t old) {
+    return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, (int)old, Hi);
+}
+
+// Two e4m3 codes (low or high 16 bits of w) -> two bf16 values, exact.
+template <bool Hi>
+__device__ __forceinline__ uint32_t e4m3x2_to_bf16x2(uint32_t w) {
+    v2bf r = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, Hi);
+    return __builtin_bit_cast(uint32_t, r);
+}
+
+// fp32 -> bf16, round to nearest even (hardware conversion).
+__device__ __forceinline__ uint32_t f32x2_to_bf16x2(float a, float b) {
+    v2bf r;
+    r[0] = (__bf16)a;
+    r[1] = (__bf16)b;
+    return __builtin_bit_cast(uint32_t, r);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Workgroup barrier that orders LDS only: waits for this wave's LDS operations
+// (lgkmcnt = 0) but not for its outstanding global loads, then s_barrier.
+// (__syncthreads() also drains vmcnt, which would stall on prefetches.)
+__device__ __forceinline__ void lds_barrier() {
+    __asm__ __volatile__("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// Lane mask of a predicate, kept in scalar registers.
+__device__ __forceinline__ uint64_t wave_ballot(bool p) { return __builtin_amdgcn_ballot_w64(p); }
+
+// Cross-lane max over the four 16-lane groups of a wave (lanes l, l^16, l^32, l^48).
+__device__ __forceinline__ float max_over_lane_groups(float x) {
+    x = __builtin_fmaxf(x, __shfl_xor(x, 16, 64));
+    x = __builtin_fmaxf(x, __shfl_xor(x, 32, 64));
+    return x;
+}
+
+}  // namespace lamp

@@ -1,0 +1,59 @@
+// Host-side launchers of the gfx950 kernels (defined in the .hip files).
+// All return a hipError_t from the launch; none allocates memory.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace lamp {
+
+// Geometry of one forward call, shared by the launchers.
+struct Shape {
+    int B, Hq, Hkv, S, D;
+    int nT;      // ceil(S / 64)
+    int S_pad;   // nT * 64
+};
+
+// Bytes of amax partial maxima for a slab of S*D bf16 values.
+int amax_chunks(int S, int D);
+
+// Quantisation pass (Q and K): per-(batch, head) amax partial maxima, then
+// scales and e4m3 codes.  q8 / k8 are written with `rows_out` rows per head
+// (rows >= S are zero).  partial must hold (B*Hq + B*Hkv) * amax_chunks(S, D)
+// uint32 values.
+hipError_t launch_quantize(const Shape& sh, const uint16_t* q, const uint16_t* k,
+                           uint32_t* partial, float* q_scale, float* k_scale,
+                           uint8_t* q8, uint8_t* k8, int rows_out, hipStream_t st);
+
+// V [B, Hkv, S, D] -> vt [B, Hkv, nT, D, 64] (keys of each tile transposed and
+// permuted into the order the P.V matrix-core operand reads; padding keys 0).
+hipError_t launch_transpose_v(const Shape& sh, const uint16_t* v, uint16_t* vt, hipStream_t st);
+
+struct AttnParams {
+    const uint8_t* q8;      // [B, Hq, S_pad, D] e4m3 codes
+    const uint8_t* k8;      // [B, Hkv, S_pad, D]
+    const uint16_t* q16;    // [B, Hq, S, D] bf16 (caller's Q)
+    const uint16_t* k16;    // [B, Hkv, S, D] bf16 (caller's K)
+    const uint16_t* vt;     // [B, Hkv, nT, D, 64] bf16
+    const float* q_scale;   // [B * Hq]
+    const float* k_scale;   // [B * Hkv]
+    float* out;             // [B, Hq, S, D]
+    uint8_t* mask;          // [B, Hq, nT, nT] or null
+    float* dump_s = nullptr;     // debug dump of 8-bit accumulators [B, Hq, S, S]
+    uint16_t* dump_p = nullptr;  // debug dump of final bf16 weights [B, Hq, S, S]
+    double log2e_over_sqrt_d;
+    float e_delta;          // smallest fp32 exponential that rounds to an e4m3 value >= delta
+    float t2;               // second-stage threshold on |log2-domain logit|
+    int causal, window;
+};
+
+hipError_t launch_attention(const Shape& sh, const AttnParams& p, hipStream_t st);
+
+// Sub-block statistics of a mask (see lamp_subblock_stats).
+hipError_t launch_subblock_stats(const uint8_t* mask, int B, int Hq, int S, int causal,
+                                 int window, int64_t* stats, hipStream_t st);
+
+hipError_t launch_debug_convert(const float* x, int64_t n, uint8_t* e4m3, uint16_t* e4m3_bf16,
+                                uint16_t* bf16, float* exp2, hipStream_t st);
+
+}  // namespace lamp

@@ -1,0 +1,328 @@
+// Host side of the C ABI declared in include/lamp.h: argument validation,
+// workspace, stream and launch order of the LampAttention forward pass.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <mutex>
+#include <string>
+
+#include "kernels.hpp"
+#include "lamp.h"
+
+namespace {
+
+constexpr double kLog2e = 1.4426950408889634;   // fp64 nearest to log2(e)
+constexpr int kMaxDevices = 64;
+
+thread_local hipStream_t g_stream = nullptr;
+thread_local std::string g_error;
+
+struct Workspace {
+    void* ptr = nullptr;
+    size_t bytes = 0;
+};
+std::mutex g_ws_mutex;
+Workspace g_ws[kMaxDevices];
+
+// Event timing of lamp_attn_fwd phases (lamp_set_timing / lamp_read_timing).
+constexpr int kMaxTimed = 4096;
+thread_local bool g_timing = false;
+thread_local int g_n_timed = 0;
+thread_local hipEvent_t g_events[kMaxTimed][3];
+
+int fail(int code, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_error = buf;
+    return code;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+    return fail(LAMP_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+size_t workspace_limit() {
+    const char* s = std::getenv("LAMP_WORKSPACE_LIMIT_BYTES");
+    if (!s || !*s) return SIZE_MAX;
+    return (size_t)std::strtoull(s, nullptr, 10);
+}
+
+// Returns LAMP_OK and a device pointer to at least `bytes` of workspace on the
+// current device.  Grows only; the old buffer is freed after a device-wide
+// synchronisation, since kernels on any stream may still read it.
+int get_workspace(size_t bytes, void** out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    if (dev < 0 || dev >= kMaxDevices) return fail(LAMP_ERR_UNSUPPORTED, "device index %d", dev);
+    if (bytes > workspace_limit())
+        return fail(LAMP_ERR_NOMEM, "workspace of %zu bytes exceeds LAMP_WORKSPACE_LIMIT_BYTES", bytes);
+    std::lock_guard<std::mutex> lock(g_ws_mutex);
+    Workspace& ws = g_ws[dev];
+    if (ws.bytes < bytes) {
+        if (ws.ptr) {
+            e = hipDeviceSynchronize();
+            if (e != hipSuccess) return hip_fail(e, "hipDeviceSynchronize");
+            hipFree(ws.ptr);
+            ws.ptr = nullptr;
+            ws.bytes = 0;
+        }
+        void* p = nullptr;
+        e = hipMalloc(&p, bytes);
+        if (e != hipSuccess) {
+            (void)hipGetLastError();
+            return fail(LAMP_ERR_NOMEM, "hipMalloc(%zu): %s", bytes, hipGetErrorString(e));
+        }
+        ws.ptr = p;
+        ws.bytes = bytes;
+    }
+    *out = ws.ptr;
+    return LAMP_OK;
+}
+
+int check_sizes(int B, int Hq, int Hkv, int S, int D) {
+    if (B < 1 || Hq < 1 || Hkv < 1 || S < 1 || D < 1)
+        return fail(LAMP_ERR_INVALID, "sizes must be >= 1 (B=%d Hq=%d Hkv=%d S=%d D=%d)", B, Hq, Hkv, S, D);
+    if (Hq % Hkv != 0) return fail(LAMP_ERR_INVALID, "Hq (%d) must be a multiple of Hkv (%d)", Hq, Hkv);
+    if (D != 64 && D != 128) return fail(LAMP_ERR_UNSUPPORTED, "head dimension D=%d (supported: 64, 128)", D);
+    const int64_t nT = (S + 63) / 64;
+    const int64_t elems = (int64_t)B * Hq * nT * 64 * D;
+    if (elems >= ((int64_t)1 << 31))
+        return fail(LAMP_ERR_UNSUPPORTED, "B*Hq*S*D = %lld exceeds 2^31", (long long)elems);
+    return LAMP_OK;
+}
+
+lamp::Shape make_shape(int B, int Hq, int Hkv, int S, int D) {
+    lamp::Shape sh;
+    sh.B = B; sh.Hq = Hq; sh.Hkv = Hkv; sh.S = S; sh.D = D;
+    sh.nT = (S + 63) / 64;
+    sh.S_pad = sh.nT * 64;
+    return sh;
+}
+
+// Positive finite e4m3fn values by code 1..126.
+double e4m3_value(int code) {
+    const int ef = code >> 3, m = code & 7;
+    return ef == 0 ? m * std::ldexp(1.0, -9) : (1.0 + m / 8.0) * std::ldexp(1.0, ef - 7);
+}
+
+// Smallest fp32 e such that rounding e to e4m3 (nearest, ties to even) gives a
+// value >= delta.  The first stage compares the fp32 exponential against it,
+// which is the same as comparing its 8-bit rounding against delta.
+float exponential_threshold(float delta) {
+    if (!(delta > 0.0f)) return -INFINITY;
+    int c = 1;
+    while (c <= 126 && e4m3_value(c) < (double)delta) ++c;
+    if (c > 126) return INFINITY;
+    const double below = c == 1 ? 0.0 : e4m3_value(c - 1);
+    const float mid = (float)((below + e4m3_value(c)) * 0.5);   // exact: 5 significant bits
+    return (c % 2 == 0) ? mid : std::nextafter(mid, INFINITY);
+}
+
+struct Layout {
+    size_t partial, q_scale, k_scale, q8, k8, vt, total;
+};
+
+Layout workspace_layout(const lamp::Shape& sh) {
+    Layout L;
+    size_t off = 0;
+    auto take = [&](size_t bytes) { size_t o = off; off = round_up(off + bytes, 256); return o; };
+    const size_t nslab = (size_t)sh.B * (sh.Hq + sh.Hkv);
+    L.partial = take(nslab * lamp::amax_chunks(sh.S, sh.D) * sizeof(uint32_t));
+    L.q_scale = take((size_t)sh.B * sh.Hq * sizeof(float));
+    L.k_scale = take((size_t)sh.B * sh.Hkv * sizeof(float));
+    L.q8 = take((size_t)sh.B * sh.Hq * sh.S_pad * sh.D);
+    L.k8 = take((size_t)sh.B * sh.Hkv * sh.S_pad * sh.D);
+    L.vt = take((size_t)sh.B * sh.Hkv * sh.nT * sh.D * 64 * sizeof(uint16_t));
+    L.total = off;
+    return L;
+}
+
+}  // namespace
+
+static int attn_fwd_impl(const void* q, const void* k, const void* v, float* out, int B, int Hq, int Hkv,
+                         int S, int D, int causal, int window, float delta, float tau,
+                         uint8_t* subblock_mask_out, float* dump_s, uint16_t* dump_p) {
+    if (!q || !k || !v || !out) return fail(LAMP_ERR_INVALID, "q, k, v and out must be non-null");
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
+        return fail(LAMP_ERR_INVALID, "q, k, v and out must be 16-byte aligned");
+    int rc = check_sizes(B, Hq, Hkv, S, D);
+    if (rc != LAMP_OK) return rc;
+    if (causal != 0 && causal != 1) return fail(LAMP_ERR_INVALID, "causal must be 0 or 1 (got %d)", causal);
+    if (window < 0) return fail(LAMP_ERR_INVALID, "window must be >= 0 (got %d)", window);
+    if (window > 0 && !causal) return fail(LAMP_ERR_INVALID, "a sliding window requires causal = 1");
+    if (std::isnan(delta) || std::isnan(tau)) return fail(LAMP_ERR_INVALID, "delta and tau must not be NaN");
+
+    const lamp::Shape sh = make_shape(B, Hq, Hkv, S, D);
+    const Layout L = workspace_layout(sh);
+    void* ws = nullptr;
+    rc = get_workspace(L.total, &ws);
+    if (rc != LAMP_OK) return rc;
+    uint8_t* base = static_cast<uint8_t*>(ws);
+
+    const uint16_t* q16 = static_cast<const uint16_t*>(q);
+    const uint16_t* k16 = static_cast<const uint16_t*>(k);
+    const uint16_t* v16 = static_cast<const uint16_t*>(v);
+    auto* partial = reinterpret_cast<uint32_t*>(base + L.partial);
+    auto* q_scale = reinterpret_cast<float*>(base + L.q_scale);
+    auto* k_scale = reinterpret_cast<float*>(base + L.k_scale);
+    auto* q8 = base + L.q8;
+    auto* k8 = base + L.k8;
+    auto* vt = reinterpret_cast<uint16_t*>(base + L.vt);
+
+    hipEvent_t* ev = nullptr;
+    if (g_timing && g_n_timed < kMaxTimed) {
+        ev = g_events[g_n_timed];
+        for (int i = 0; i < 3 && ev; ++i)
+            if (!ev[i] && hipEventCreate(&ev[i]) != hipSuccess) ev = nullptr;
+        if (ev) ++g_n_timed;
+    }
+    if (ev) (void)hipEventRecord(ev[0], g_stream);
+    hipError_t e = lamp::launch_quantize(sh, q16, k16, partial, q_scale, k_scale, q8, k8, sh.S_pad, g_stream);
+    if (e != hipSuccess) return hip_fail(e, "quantise launch");
+    e = lamp::launch_transpose_v(sh, v16, vt, g_stream);
+    if (e != hipSuccess) return hip_fail(e, "transpose launch");
+    if (ev) (void)hipEventRecord(ev[1], g_stream);
+
+    lamp::AttnParams p;
+    p.q8 = q8; p.k8 = k8; p.q16 = q16; p.k16 = k16; p.vt = vt;
+    p.q_scale = q_scale; p.k_scale = k_scale;
+    p.out = out; p.mask = subblock_mask_out;
+    p.log2e_over_sqrt_d = kLog2e / std::sqrt((double)D);
+    p.e_delta = exponential_threshold(delta);
+    p.t2 = (float)(16.0 * (double)tau * kLog2e);
+    p.causal = causal; p.window = window;
+    p.dump_s = dump_s; p.dump_p = dump_p;
+    e = lamp::launch_attention(sh, p, g_stream);
+    if (e != hipSuccess) return hip_fail(e, "attention launch");
+    if (ev) (void)hipEventRecord(ev[2], g_stream);
+    return LAMP_OK;
+}
+
+extern "C" {
+
+int lamp_attn_fwd(const void* q, const void* k, const void* v, float* out, int B, int Hq, int Hkv,
+                  int S, int D, int causal, int window, float delta, float tau,
+                  uint8_t* subblock_mask_out) {
+    return attn_fwd_impl(q, k, v, out, B, Hq, Hkv, S, D, causal, window, delta, tau, subblock_mask_out,
+                         nullptr, nullptr);
+}
+
+int lamp_debug_attn_dump(const void* q, const void* k, const void* v, float* out, int B, int Hq, int Hkv,
+                         int S, int D, int causal, int window, float delta, float tau,
+                         uint8_t* subblock_mask_out, float* acc8_out, uint16_t* p_out) {
+    if (!acc8_out || !p_out) return fail(LAMP_ERR_INVALID, "acc8_out and p_out must be non-null");
+    if (S > 2048) return fail(LAMP_ERR_UNSUPPORTED, "debug dump needs S <= 2048 (got %d)", S);
+    return attn_fwd_impl(q, k, v, out, B, Hq, Hkv, S, D, causal, window, delta, tau, subblock_mask_out,
+                         acc8_out, p_out);
+}
+
+int lamp_set_timing(int enable) {
+    if (enable != 0 && enable != 1) return fail(LAMP_ERR_INVALID, "enable must be 0 or 1");
+    g_timing = enable != 0;
+    return LAMP_OK;
+}
+
+int lamp_read_timing(double* prep_ms, double* attn_ms, int* n_calls) {
+    if (!prep_ms || !attn_ms || !n_calls) return fail(LAMP_ERR_INVALID, "outputs must be non-null");
+    double a = 0.0, b = 0.0;
+    for (int i = 0; i < g_n_timed; ++i) {
+        hipEvent_t* ev = g_events[i];
+        hipError_t e = hipEventSynchronize(ev[2]);
+        if (e != hipSuccess) return hip_fail(e, "hipEventSynchronize");
+        float x = 0.f, y = 0.f;
+        e = hipEventElapsedTime(&x, ev[0], ev[1]);
+        if (e != hipSuccess) return hip_fail(e, "hipEventElapsedTime");
+        e = hipEventElapsedTime(&y, ev[1], ev[2]);
+        if (e != hipSuccess) return hip_fail(e, "hipEventElapsedTime");
+        a += x;
+        b += y;
+    }
+    *prep_ms = a;
+    *attn_ms = b;
+    *n_calls = g_n_timed;
+    g_n_timed = 0;
+    return LAMP_OK;
+}
+
+int lamp_subblock_stats(const uint8_t* subblock_mask, int B, int Hq, int S, int causal, int window,
+                        int64_t* stats_out) {
+    if (!subblock_mask || !stats_out) return fail(LAMP_ERR_INVALID, "mask and stats_out must be non-null");
+    if (B < 1 || Hq < 1 || S < 1) return fail(LAMP_ERR_INVALID, "sizes must be >= 1");
+    if (causal != 0 && causal != 1) return fail(LAMP_ERR_INVALID, "causal must be 0 or 1");
+    if (window < 0 || (window > 0 && !causal)) return fail(LAMP_ERR_INVALID, "bad window");
+    if ((reinterpret_cast<uintptr_t>(stats_out) & 7u) != 0) return fail(LAMP_ERR_INVALID, "stats_out must be 8-byte aligned");
+    hipError_t e = lamp::launch_subblock_stats(subblock_mask, B, Hq, S, causal, window, stats_out, g_stream);
+    if (e != hipSuccess) return hip_fail(e, "stats launch");
+    return LAMP_OK;
+}
+
+int lamp_quantize_qk(const void* q, const void* k, int B, int Hq, int Hkv, int S, int D, uint8_t* q8,
+                     uint8_t* k8, float* q_scale, float* k_scale) {
+    if (!q || !k || !q8 || !k8 || !q_scale || !k_scale)
+        return fail(LAMP_ERR_INVALID, "all pointers must be non-null");
+    if (!aligned16(q) || !aligned16(k) || !aligned16(q8) || !aligned16(k8))
+        return fail(LAMP_ERR_INVALID, "q, k, q8 and k8 must be 16-byte aligned");
+    int rc = check_sizes(B, Hq, Hkv, S, D);
+    if (rc != LAMP_OK) return rc;
+    const lamp::Shape sh = make_shape(B, Hq, Hkv, S, D);
+    const Layout L = workspace_layout(sh);
+    void* ws = nullptr;
+    rc = get_workspace(L.total, &ws);
+    if (rc != LAMP_OK) return rc;
+    auto* partial = reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(ws) + L.partial);
+    hipError_t e = lamp::launch_quantize(sh, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                                         partial, q_scale, k_scale, q8, k8, S, g_stream);
+    if (e != hipSuccess) return hip_fail(e, "quantise launch");
+    return LAMP_OK;
+}
+
+int lamp_debug_convert(const float* x, int64_t n, uint8_t* e4m3, uint16_t* e4m3_bf16, uint16_t* bf16,
+                       float* exp2) {
+    if (n < 0) return fail(LAMP_ERR_INVALID, "n must be >= 0");
+    if (n == 0) return LAMP_OK;
+    if (!x) return fail(LAMP_ERR_INVALID, "x must be non-null");
+    hipError_t e = lamp::launch_debug_convert(x, n, e4m3, e4m3_bf16, bf16, exp2, g_stream);
+    if (e != hipSuccess) return hip_fail(e, "convert launch");
+    return LAMP_OK;
+}
+
+int lamp_set_stream(void* hip_stream) {
+    g_stream = static_cast<hipStream_t>(hip_stream);
+    return LAMP_OK;
+}
+
+const char* lamp_last_error(void) { return g_error.c_str(); }
+
+void lamp_release_workspace(void) {
+    std::lock_guard<std::mutex> lock(g_ws_mutex);
+    bool any = false;
+    for (auto& ws : g_ws) any |= ws.ptr != nullptr;
+    if (!any) return;
+    (void)hipDeviceSynchronize();
+    int cur = 0;
+    (void)hipGetDevice(&cur);
+    for (int d = 0; d < kMaxDevices; ++d) {
+        if (!g_ws[d].ptr) continue;
+        (void)hipSetDevice(d);
+        (void)hipFree(g_ws[d].ptr);
+        g_ws[d].ptr = nullptr;
+        g_ws[d].bytes = 0;
+    }
+    (void)hipSetDevice(cur);
+}
+
+int lamp_version(void) { return 100; }
+
+}  // extern "C"

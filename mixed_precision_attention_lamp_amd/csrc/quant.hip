@@ -1,0 +1,206 @@
+// Quantisation pass of the LampAttention forward pass on gfx950.
+//
+// "LampAttention: Look-Ahead Mixed-Precision FlashAttention for Dedicated
+// Accelerators" (abstract) accumulates key-query products in an 8-bit format.
+// Here Q and K are quantised to e4m3fn with one scale per (batch, head):
+// scale = fl32(amax / 448), codes = E4M3(fl32(x * fl32(448 / amax))).  The pass
+// is bound by HBM bandwidth: each bf16 value is read twice (amax, then
+// quantise; the second read is served mostly from the last-level cache) and
+// one byte is written.  V is transposed per 64-key tile here as well, so that
+// the attention kernel can stage it straight into the layout of the P.V
+// matrix-core operand.
+#include <hip/hip_runtime.h>
+
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace lamp {
+
+namespace {
+
+constexpr int kChunk = 32768;      // bf16 values per amax / quantise block
+constexpr int kThreads = 256;
+
+__device__ __forceinline__ uint32_t max_bf16_mag(u32x4 w) {
+    uint32_t m = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        m = max(m, w[i] & 0x7FFFu);
+        m = max(m, (w[i] >> 16) & 0x7FFFu);
+    }
+    return m;
+}
+
+__device__ __forceinline__ uint32_t block_max_u32(uint32_t v, uint32_t* red) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, off, 64));
+    const int wave = threadIdx.x >> 6;
+    if ((threadIdx.x & 63) == 0) red[wave] = v;
+    __syncthreads();
+    v = red[0];
+#pragma unroll
+    for (int w = 1; w < kThreads / 64; ++w) v = max(v, red[w]);
+    return v;
+}
+
+// blockIdx.y = slab (Q heads first, then K heads); blockIdx.x = chunk.
+__global__ __launch_bounds__(kThreads) void amax_kernel(const uint16_t* __restrict__ q,
+                                                        const uint16_t* __restrict__ k,
+                                                        uint32_t* __restrict__ partial,
+                                                        int n_q_slabs, int slab_len, int nch) {
+    __shared__ uint32_t red[kThreads / 64];
+    const int slab = blockIdx.y;
+    const uint16_t* src = slab < n_q_slabs ? q + (size_t)slab * slab_len
+                                           : k + (size_t)(slab - n_q_slabs) * slab_len;
+    const int begin = blockIdx.x * kChunk;
+    const int end = min(begin + kChunk, slab_len);
+    uint32_t m = 0;
+    for (int i = begin + threadIdx.x * 8; i < end; i += kThreads * 8)
+        m = max(m, max_bf16_mag(*reinterpret_cast<const u32x4*>(src + i)));
+    m = block_max_u32(m, red);
+    if (threadIdx.x == 0) partial[(size_t)slab * nch + blockIdx.x] = m;
+}
+
+// blockIdx.y = slab, blockIdx.x = output chunk.  Output slabs have rows_out
+// rows of D codes; rows >= S are written as zero.
+__global__ __launch_bounds__(kThreads) void quantize_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+    const uint32_t* __restrict__ partial, float* __restrict__ q_scale, float* __restrict__ k_scale,
+    uint8_t* __restrict__ q8, uint8_t* __restrict__ k8, int n_q_slabs, int S, int D, int nch,
+    int rows_out) {
+    __shared__ uint32_t red[kThreads / 64];
+    const int slab = blockIdx.y;
+    const bool is_q = slab < n_q_slabs;
+    const int hs = is_q ? slab : slab - n_q_slabs;
+    const uint16_t* src = (is_q ? q : k) + (size_t)hs * S * D;
+    uint8_t* dst = (is_q ? q8 : k8) + (size_t)hs * rows_out * D;
+
+    uint32_t m = 0;
+    for (int i = threadIdx.x; i < nch; i += kThreads) m = max(m, partial[(size_t)slab * nch + i]);
+    m = block_max_u32(m, red);
+    const float amax = bf16_bits_to_float(m);
+    float scale = 1.0f, inv = 1.0f;
+    if (amax > 0.0f) {
+        // fp64 quotients rounded once to fp32 are the correctly rounded fp32 quotients
+        scale = (float)((double)amax / 448.0);
+        inv = (float)(448.0 / (double)amax);
+    }
+    if (blockIdx.x == 0 && threadIdx.x == 0) (is_q ? q_scale : k_scale)[hs] = scale;
+
+    const int in_len = S * D;
+    const int out_len = rows_out * D;
+    const int begin = blockIdx.x * kChunk;
+    const int end = min(begin + kChunk, out_len);
+    for (int i = begin + threadIdx.x * 8; i < end; i += kThreads * 8) {
+        u32x2 o = {0u, 0u};
+        if (i < in_len) {
+            const u32x4 w = *reinterpret_cast<const u32x4*>(src + i);
+            float x[8];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                x[2 * j] = bf16_bits_to_float(w[j] & 0xFFFFu) * inv;
+                x[2 * j + 1] = bf16_bits_to_float(w[j] >> 16) * inv;
+            }
+            o[0] = cvt_pk_e4m3<true>(x[2], x[3], cvt_pk_e4m3<false>(x[0], x[1], 0u));
+            o[1] = cvt_pk_e4m3<true>(x[6], x[7], cvt_pk_e4m3<false>(x[4], x[5], 0u));
+        }
+        *reinterpret_cast<u32x2*>(dst + i) = o;
+    }
+}
+
+// One block per (tile, batch*kv head): V[64 keys][D] -> vt[D][64 positions].
+// Within each 32-key half, key 16*hi + 4*g + i goes to position 8*g + 4*hi + i:
+// lane group g of the P.V operand then reads 8 consecutive positions.
+template <int D>
+__global__ __launch_bounds__(kThreads) void transpose_v_kernel(const uint16_t* __restrict__ v,
+                                                               uint16_t* __restrict__ vt, int S,
+                                                               int nT) {
+    constexpr int kStride = D + 8;   // bf16 per LDS row
+    __shared__ uint16_t tile[kTileKeys * kStride];
+    const int t = blockIdx.x;
+    const int bh = blockIdx.y;
+    constexpr int kChunksPerRow = D / 8;
+#pragma unroll
+    for (int it = 0; it < kTileKeys * kChunksPerRow / kThreads; ++it) {
+        const int c = threadIdx.x + it * kThreads;
+        const int key = c / kChunksPerRow, col = c % kChunksPerRow;
+        const int gk = t * kTileKeys + key;
+        u32x4 w = {0u, 0u, 0u, 0u};
+        if (gk < S) w = *reinterpret_cast<const u32x4*>(v + ((size_t)bh * S + gk) * D + col * 8);
+        uint32_t* dst = reinterpret_cast<uint32_t*>(tile + key * kStride + col * 8);
+        dst[0] = w[0]; dst[1] = w[1]; dst[2] = w[2]; dst[3] = w[3];
+    }
+    __syncthreads();
+    uint16_t* out = vt + ((size_t)bh * nT + t) * D * kTileKeys;
+#pragma unroll
+    for (int it = 0; it < D * 8 / kThreads; ++it) {
+        const int w = threadIdx.x + it * kThreads;
+        const int d = w / 8, pb = w % 8;          // 8 positions 8*pb .. 8*pb+7
+        const int h = pb / 4, g = pb % 4;
+        uint32_t packed[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int p0 = 2 * j, p1 = 2 * j + 1;   // positions within the 8
+            const int k0 = 32 * h + 16 * (p0 / 4) + 4 * g + (p0 % 4);
+            const int k1 = 32 * h + 16 * (p1 / 4) + 4 * g + (p1 % 4);
+            packed[j] = (uint32_t)tile[k0 * kStride + d] | ((uint32_t)tile[k1 * kStride + d] << 16);
+        }
+        *reinterpret_cast<u32x4*>(out + d * kTileKeys + pb * 8) =
+            u32x4{packed[0], packed[1], packed[2], packed[3]};
+    }
+}
+
+__global__ void debug_convert_kernel(const float* __restrict__ x, int64_t n, uint8_t* e4m3,
+                                     uint16_t* e4m3_bf16, uint16_t* bf16, float* exp2) {
+    for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n;
+         i += (int64_t)gridDim.x * blockDim.x) {
+        const float v = x[i];
+        const uint32_t code = cvt_pk_e4m3<false>(v, 0.0f, 0u) & 0xFFu;
+        if (e4m3) e4m3[i] = (uint8_t)code;
+        if (e4m3_bf16) e4m3_bf16[i] = (uint16_t)(e4m3x2_to_bf16x2<false>(code) & 0xFFFFu);
+        if (bf16) bf16[i] = (uint16_t)(f32x2_to_bf16x2(v, 0.0f) & 0xFFFFu);
+        if (exp2) exp2[i] = fast_exp2(v);
+    }
+}
+
+}  // namespace
+
+int amax_chunks(int S, int D) { return (S * D + kChunk - 1) / kChunk; }
+
+hipError_t launch_quantize(const Shape& sh, const uint16_t* q, const uint16_t* k,
+                           uint32_t* partial, float* q_scale, float* k_scale, uint8_t* q8,
+                           uint8_t* k8, int rows_out, hipStream_t st) {
+    const int nq = sh.B * sh.Hq, nk = sh.B * sh.Hkv;
+    const int nch = amax_chunks(sh.S, sh.D);
+    hipLaunchKernelGGL(amax_kernel, dim3(nch, nq + nk), dim3(kThreads), 0, st, q, k, partial, nq,
+                       sh.S * sh.D, nch);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int nch_out = (rows_out * sh.D + kChunk - 1) / kChunk;
+    hipLaunchKernelGGL(quantize_kernel, dim3(nch_out, nq + nk), dim3(kThreads), 0, st, q, k,
+                       partial, q_scale, k_scale, q8, k8, nq, sh.S, sh.D, nch, rows_out);
+    return hipGetLastError();
+}
+
+hipError_t launch_transpose_v(const Shape& sh, const uint16_t* v, uint16_t* vt, hipStream_t st) {
+    const dim3 grid(sh.nT, sh.B * sh.Hkv);
+    if (sh.D == 64)
+        hipLaunchKernelGGL(transpose_v_kernel<64>, grid, dim3(kThreads), 0, st, v, vt, sh.S, sh.nT);
+    else if (sh.D == 128)
+        hipLaunchKernelGGL(transpose_v_kernel<128>, grid, dim3(kThreads), 0, st, v, vt, sh.S, sh.nT);
+    else
+        hipLaunchKernelGGL(transpose_v_kernel<256>, grid, dim3(kThreads), 0, st, v, vt, sh.S, sh.nT);
+    return hipGetLastError();
+}
+
+hipError_t launch_debug_convert(const float* x, int64_t n, uint8_t* e4m3, uint16_t* e4m3_bf16,
+                                uint16_t* bf16, float* exp2, hipStream_t st) {
+    int64_t blocks = (n + kThreads - 1) / kThreads;
+    if (blocks > 8192) blocks = 8192;
+    if (blocks < 1) blocks = 1;
+    hipLaunchKernelGGL(debug_convert_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, st, x, n,
+                       e4m3, e4m3_bf16, bf16, exp2);
+    return hipGetLastError();
+}
+
+}  // namespace lamp

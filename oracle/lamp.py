@@ -218,6 +218,7 @@ def run_unit(ctx, b, hq, r, flag_override=None, trace=None):
             flags = [bool((flag_override[t] >> c) & 1) for c in range(NSB)]
         # (e) flagged sub-blocks are recomputed in 16-bit
         p = np.where(vis, p8, 0.0)
+        e16 = np.full(p.shape, np.nan)       # fp32 16-bit exponentials (diagnostics)
         for c in range(NSB):
             if not flags[c]:
                 continue
@@ -225,7 +226,8 @@ def run_unit(ctx, b, hq, r, flag_override=None, trace=None):
             k16 = ctx["k16"][b, hk, cols[sub]]
             acc16 = fl32(q16 @ k16.T)
             x16 = fma32(acc16, c16, -safe_m[:, None])
-            p16 = round_bf16(exp2_f32(x16))
+            e16[:, sub] = exp2_f32(x16)
+            p16 = round_bf16(e16[:, sub])
             p[:, sub] = np.where(vis[:, sub], p16, 0.0)
         # (f) online-softmax rescale and P.V
         alpha = np.where(np.isneginf(m), 0.0, np.exp2(m - safe_m))
@@ -240,7 +242,7 @@ def run_unit(ctx, b, hq, r, flag_override=None, trace=None):
         mask[t] = byte
         if trace is not None:
             trace.append(dict(t=t, cols=cols, vis=vis, acc8=acc8, s2=s2, e=e,
-                              p8=p8, p=p, flags=flags, m_new=m_new.copy(), T2=T2))
+                              p8=p8, p=p, e16=e16, flags=flags, m_new=m_new.copy(), T2=T2))
     # Step 5: normalise
     out = fl32(O / ell[:, None])
     if trace is not None:

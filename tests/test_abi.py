@@ -1,0 +1,93 @@
+"""The C ABI library loads, exports what include/lamp.h declares, and rejects
+bad arguments before touching HIP.  No GPU and no compute call."""
+import ctypes
+import math
+import subprocess
+
+import pytest
+import torch
+
+import mixed_precision_attention_lamp_amd as lamp
+from mixed_precision_attention_lamp_amd import _lib
+
+ALIGNED = 1 << 20          # any 16-byte aligned non-null address: never dereferenced
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return lamp.load()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = lamp.declared_symbols()
+    assert {"lamp_attn_fwd", "lamp_subblock_stats", "lamp_quantize_qk", "lamp_set_stream",
+            "lamp_last_error", "lamp_release_workspace", "lamp_version",
+            "lamp_debug_convert", "lamp_set_timing", "lamp_read_timing",
+            "lamp_debug_attn_dump"} <= set(names)
+    out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    for n in names:
+        assert n in exported, n
+        assert getattr(lib, n) is not None
+
+
+def test_version(lib):
+    assert lib.lamp_version() == 100
+
+
+def _fwd(lib, **kw):
+    args = dict(q=ALIGNED, k=ALIGNED, v=ALIGNED, out=ALIGNED, B=1, Hq=2, Hkv=1, S=128, D=128,
+                causal=1, window=0, delta=2.0 ** -8, tau=0.5, mask=None)
+    args.update(kw)
+    return lib.lamp_attn_fwd(args["q"], args["k"], args["v"], args["out"], args["B"], args["Hq"],
+                             args["Hkv"], args["S"], args["D"], args["causal"], args["window"],
+                             args["delta"], args["tau"], args["mask"])
+
+
+@pytest.mark.parametrize("kw,code,text", [
+    (dict(q=None), -1, "non-null"),
+    (dict(out=None), -1, "non-null"),
+    (dict(k=ALIGNED + 2), -1, "aligned"),
+    (dict(B=0), -1, ">= 1"),
+    (dict(S=-5), -1, ">= 1"),
+    (dict(Hq=3, Hkv=2), -1, "multiple"),
+    (dict(D=96), -2, "D=96"),
+    (dict(D=256), -2, "D=256"),
+    (dict(causal=2), -1, "causal"),
+    (dict(window=-1), -1, "window"),
+    (dict(window=16, causal=0), -1, "window"),
+    (dict(delta=math.nan), -1, "NaN"),
+    (dict(tau=math.nan), -1, "NaN"),
+    (dict(B=64, Hq=64, Hkv=8, S=65536, D=128), -2, "2^31"),
+])
+def test_attn_validation(lib, kw, code, text):
+    assert _fwd(lib, **kw) == code
+    assert text in lamp.lamp_last_error()
+
+
+def test_other_entry_points_validate(lib):
+    assert lib.lamp_quantize_qk(None, ALIGNED, 1, 1, 1, 64, 64, ALIGNED, ALIGNED, ALIGNED, ALIGNED) == -1
+    assert lib.lamp_subblock_stats(None, 1, 1, 64, 1, 0, ALIGNED) == -1
+    assert lib.lamp_subblock_stats(ALIGNED, 1, 1, 64, 0, 8, ALIGNED) == -1
+    assert lib.lamp_debug_convert(None, 10, None, None, None, None) == -1
+    assert lib.lamp_debug_convert(None, 0, None, None, None, None) == 0
+    assert lib.lamp_set_stream(None) == 0
+
+
+@pytest.mark.skipif(torch.cuda.is_available(), reason="checks the no-device error path")
+def test_valid_call_without_device_reports_hip_error(lib):
+    assert _fwd(lib) == -3
+    assert "hip" in lamp.lamp_last_error().lower()
+
+
+def test_binding_raises_on_error():
+    class Fake:
+        shape = (1, 1, 64, 96)
+
+        def data_ptr(self):
+            return ALIGNED
+    with pytest.raises(lamp.LampError) as ei:
+        lamp.lamp_attn_fwd.__wrapped__ if hasattr(lamp.lamp_attn_fwd, "__wrapped__") else None
+        _lib._check(_fwd(lamp.load(), D=96))
+    assert ei.value.code == -2

@@ -1,0 +1,267 @@
+"""HIP path vs the CPU oracle, through the C ABI (needs an MI355X).
+
+* device conversions (e4m3 rounding, e4m3 -> bf16, bf16 rounding, exp2)
+  against the oracle's software formats;
+* the quantisation pass, bit-exact;
+* the forward pass on small shapes that span several tiles and a ragged
+  tail, every masking mode, GQA groups of 1..8, the endpoints of delta / tau;
+* the full Qwen3-8B-shaped workload in the launch configuration the bench
+  times, on sampled units;
+* exact device-only invariants (determinism, V scaling, batch duplication);
+* the device histogram of 16-bit sub-blocks against the oracle's.
+"""
+import numpy as np
+import pytest
+import torch
+
+from inputs import make_config_inputs, make_inputs
+from oracle import lamp as L
+from oracle.formats import (bf16_bits_to_f64, e4m3_decode, e4m3_encode, exp2_f32, round_bf16,
+                            round_e4m3)
+
+from parity import (EPS_ACC8, assert_parity, compare, fragile_alternatives, run_gpu, say,
+                    to_device)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib():
+    import mixed_precision_attention_lamp_amd as lamp
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    lamp.load()
+    yield
+    torch.cuda.synchronize()
+
+
+# --------------------------------------------------------------------------
+# conversions
+# --------------------------------------------------------------------------
+def _conversion_points():
+    codes = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], dtype=np.uint8)
+    grid = np.unique(e4m3_decode(codes))
+    mids = (grid[:-1] + grid[1:]) / 2
+    pts = [grid, mids]
+    m32 = mids.astype(np.float32)
+    up, dn = m32.copy(), m32.copy()
+    for _ in range(3):
+        up = np.nextafter(up, np.float32(np.inf))
+        dn = np.nextafter(dn, np.float32(-np.inf))
+        pts += [up.astype(np.float64), dn.astype(np.float64)]
+    rng = np.random.default_rng(20)
+    pts += [rng.uniform(0, 1, 1 << 20), rng.uniform(-448, 448, 1 << 18),
+            rng.uniform(-2 ** -6, 2 ** -6, 1 << 18)]
+    x = np.concatenate(pts).astype(np.float32)
+    return x[np.abs(x) <= 448]
+
+
+def test_device_e4m3_and_bf16_conversions():
+    import mixed_precision_attention_lamp_amd as lamp
+    x = _conversion_points()
+    xd = torch.from_numpy(x).cuda()
+    n = x.size
+    e8 = torch.empty(n, dtype=torch.uint8, device="cuda")
+    e8b = torch.empty(n, dtype=torch.int16, device="cuda")
+    b16 = torch.empty(n, dtype=torch.int16, device="cuda")
+    ex = torch.empty(n, dtype=torch.float32, device="cuda")
+    lamp.lamp_debug_convert(xd, e8, e8b, b16, ex)
+    torch.cuda.synchronize()
+    want = round_e4m3(x.astype(np.float64))
+    got_codes = e8.cpu().numpy()
+    bad = np.nonzero(got_codes != e4m3_encode(want))[0]
+    say(f"[convert] e4m3 code mismatches {bad.size} of {n}")
+    assert bad.size == 0, list(zip(x[bad[:8]], got_codes[bad[:8]], e4m3_encode(want)[bad[:8]]))
+    dec = bf16_bits_to_f64(e8b.cpu().numpy().view(np.uint16))
+    assert np.array_equal(dec, want)
+    gb = bf16_bits_to_f64(b16.cpu().numpy().view(np.uint16))
+    assert np.array_equal(gb, round_bf16(x.astype(np.float64)))
+
+
+def test_device_exp2_error():
+    import mixed_precision_attention_lamp_amd as lamp
+    x = np.random.default_rng(21).uniform(-40, 0.5, 1 << 20).astype(np.float32)
+    xd = torch.from_numpy(x).cuda()
+    ex = torch.empty_like(xd)
+    lamp.lamp_debug_convert(xd, exp2=ex)
+    torch.cuda.synchronize()
+    g = ex.cpu().numpy()
+    ref = exp2_f32(x.astype(np.float64)).astype(np.float32)
+    ulps = np.abs(g.view(np.int32).astype(np.int64) - ref.view(np.int32).astype(np.int64))
+    say(f"[convert] exp2: max ulp error {ulps.max()}, fraction exact {np.mean(ulps == 0):.4f}")
+    assert ulps.max() <= 2
+
+
+# --------------------------------------------------------------------------
+# quantisation
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("shape", [(1, 1, 1, 256, 64, "sinks", 1), (2, 4, 2, 200, 128, "channels", 30),
+                                   (1, 8, 1, 67, 64, "plain", 31), (1, 2, 2, 4096, 128, "channels", 32)])
+def test_quantize_bit_exact(shape):
+    import mixed_precision_attention_lamp_amd as lamp
+    B, Hq, Hkv, S, D, st, seed = shape
+    q, k, v = make_inputs(B, Hq, Hkv, S, D, seed, st)
+    q[0, 0, :3] = 0                     # include zero rows
+    qd, kd = to_device(q), to_device(k)
+    q8 = torch.empty((B, Hq, S, D), dtype=torch.uint8, device="cuda")
+    k8 = torch.empty((B, Hkv, S, D), dtype=torch.uint8, device="cuda")
+    qs = torch.empty(B * Hq, dtype=torch.float32, device="cuda")
+    ks = torch.empty(B * Hkv, dtype=torch.float32, device="cuda")
+    lamp.lamp_quantize_qk(qd, kd, q8, k8, qs, ks)
+    torch.cuda.synchronize()
+    _, qc, sq, _ = L.quantize(q)
+    _, kc, sk, _ = L.quantize(k)
+    assert np.array_equal(q8.cpu().numpy(), qc)
+    assert np.array_equal(k8.cpu().numpy(), kc)
+    assert np.array_equal(qs.cpu().numpy().astype(np.float64), sq.reshape(-1))
+    assert np.array_equal(ks.cpu().numpy().astype(np.float64), sk.reshape(-1))
+
+
+# --------------------------------------------------------------------------
+# forward pass, small shapes
+# --------------------------------------------------------------------------
+SMALL = [
+    # B, Hq, Hkv, S, D, causal, window, delta, tau, structure, seed
+    (1, 1, 1, 256, 64, 1, 0, 2 ** -8, 2 ** -1, "sinks", 1),          # the tiny workload
+    (1, 4, 1, 300, 128, 1, 0, 2 ** -8, 2 ** -1, "channels", 40),    # G = 4, ragged tail
+    (2, 8, 1, 200, 128, 1, 0, 2 ** -8, 2 ** -3, "channels", 41),    # G = 8
+    (1, 4, 2, 190, 64, 1, 0, 2 ** -4, 2 ** -2, "channels", 42),     # G = 2
+    (1, 3, 3, 130, 128, 0, 0, 2 ** -8, 2 ** -1, "channels", 43),    # non-causal, G = 1
+    (1, 2, 2, 333, 128, 1, 100, 2 ** -8, 2 ** -1, "channels", 44),  # sliding window
+    (1, 4, 4, 257, 64, 1, 64, 0.0, 2 ** -2, "channels", 45),        # window, first stage off
+    (1, 2, 1, 65, 128, 1, 0, 2 ** -8, 2 ** -1, "sinks", 46),        # one full + one 1-row block
+    (1, 1, 1, 1, 64, 1, 0, 2 ** -8, 2 ** -1, "plain", 47),          # S = 1
+    (1, 4, 1, 500, 128, 1, 0, 2 ** -8, 2 ** -5, "channels+drift", 48),
+]
+
+
+@pytest.mark.parametrize("case", SMALL)
+def test_forward_parity_small(case):
+    B, Hq, Hkv, S, D, causal, window, delta, tau, st, seed = case
+    q, k, v = make_inputs(B, Hq, Hkv, S, D, seed, st)
+    rep = compare(q, k, v, causal, window, delta, tau, label=str(case))
+    assert_parity(rep)
+
+
+@pytest.mark.parametrize("ends", [(2 ** -8, np.inf), (0.0, 0.0), (0.0, np.inf), (2 ** -4, 2 ** -5)])
+def test_forward_parity_endpoints(ends):
+    delta, tau = ends
+    q, k, v = make_inputs(1, 4, 2, 260, 128, 50, "channels")
+    rep = compare(q, k, v, 1, 0, delta, tau, label=f"endpoint {ends}")
+    assert_parity(rep)
+    _, mask = run_gpu(q, k, v, 1, 0, delta, tau)
+    st = L.subblock_stats(mask, 260, True, 0)
+    if tau == np.inf:
+        assert st["flagged_subblocks"] == 0
+    if delta <= 0 and tau <= 0:
+        assert st["flagged_subblocks"] == st["visited_subblocks"]
+
+
+# --------------------------------------------------------------------------
+# per-entry dumps: 8-bit accumulators and the weights that enter P.V
+# --------------------------------------------------------------------------
+DUMP = [SMALL[0], SMALL[1], SMALL[5], (1, 3, 3, 130, 64, 0, 0, 0.0, 2 ** -2, "channels", 49),
+        (1, 2, 1, 260, 128, 1, 0, 0.0, 0.0, "channels", 50)]
+
+
+@pytest.mark.parametrize("case", DUMP)
+def test_dump_accumulators_and_weights(case):
+    """The FP8 matrix-core accumulators stay within the accumulation bound the
+    parity protocol assumes, and every weight that differs from the oracle's
+    is one whose exponential lies within its window of a rounding midpoint."""
+    import mixed_precision_attention_lamp_amd as lamp
+    B, Hq, Hkv, S, D, causal, window, delta, tau, st, seed = case
+    q, k, v = make_inputs(B, Hq, Hkv, S, D, seed, st)
+    qd, kd, vd = to_device(q), to_device(k), to_device(v)
+    nT = L.n_tiles(S)
+    out = torch.empty((B, Hq, S, D), dtype=torch.float32, device="cuda")
+    mask = torch.empty((B, Hq, nT, nT), dtype=torch.uint8, device="cuda")
+    acc = torch.full((B, Hq, S, S), float("nan"), dtype=torch.float32, device="cuda")
+    pw = torch.zeros((B, Hq, S, S), dtype=torch.int16, device="cuda")
+    lamp.lamp_debug_attn_dump(qd, kd, vd, out, causal, window, delta, tau, mask, acc, pw)
+    torch.cuda.synchronize()
+    acc_g = acc.cpu().numpy().astype(np.float64)
+    p_g = bf16_bits_to_f64(pw.cpu().numpy().view(np.uint16))
+    ctx = L.prepare(q, k, v, causal, window, delta, tau)
+    n_vis = n_acc_exact = n_p_bad = n_p_unexplained = n_fragile = 0
+    worst = 0.0
+    G = Hq // Hkv
+    for (b, h, r) in L.all_units(B, Hq, S):
+        trace = []
+        L.run_unit(ctx, b, h, r, trace=trace)
+        for rec in trace[:-1]:
+            rows = np.arange(r * 64, r * 64 + rec["vis"].shape[0])
+            vis = rec["vis"]
+            ga = acc_g[b, h][np.ix_(rows, rec["cols"])]
+            gp = p_g[b, h][np.ix_(rows, rec["cols"])]
+            q8 = ctx["q8"][b, h, rows]
+            k8 = ctx["k8"][b, h // G, rec["cols"]]
+            maxp = np.max(np.abs(q8[:, None, :] * k8[None, :, :]), axis=2)
+            exact = q8 @ k8.T
+            ratio = np.where(vis & (maxp > 0), np.abs(ga - exact) / np.where(maxp > 0, maxp, 1), 0.0)
+            worst = max(worst, float(ratio.max()))
+            n_vis += int(vis.sum())
+            n_acc_exact += int((vis & (ga == rec["acc8"])).sum())
+            alt = fragile_alternatives(ctx, b, h, r, rec)
+            bad = vis & (gp != rec["p"])
+            n_fragile += int((vis & (alt > 0)).sum())
+            n_p_bad += int(bad.sum())
+            n_p_unexplained += int((bad & (alt == 0)).sum())
+    say(f"[dump] {case}: visible {n_vis}; 8-bit accumulators equal to the exactly rounded sum "
+        f"{n_acc_exact}, worst error 2^{np.log2(max(worst, 1e-300)):.2f} max|q8 k8| "
+        f"(bound 2^{np.log2(EPS_ACC8):.1f}); weights differing {n_p_bad}, all within a midpoint "
+        f"window: {n_p_unexplained == 0} (entries in a window {n_fragile})")
+    assert worst <= EPS_ACC8
+    assert n_p_unexplained == 0
+
+
+# --------------------------------------------------------------------------
+# full-size Qwen3-8B-shaped workload, sampled units
+# --------------------------------------------------------------------------
+def _sample_units(B, Hq, S, n, seed):
+    nT = L.n_tiles(S)
+    rng = np.random.default_rng(seed)
+    units = {(0, 0, nT - 1), (B - 1, Hq - 1, 0), (0, Hq - 1, nT // 2), (B - 1, 0, nT - 1)}
+    while len(units) < n:
+        units.add((int(rng.integers(B)), int(rng.integers(Hq)), int(rng.integers(nT))))
+    return sorted(units)
+
+
+def test_forward_parity_qwen3_8b_full_size():
+    q, k, v, cfg = make_config_inputs("qwen3-8b")
+    units = _sample_units(cfg["B"], cfg["Hq"], cfg["S"], 12, 7)
+    rep = compare(q, k, v, cfg["causal"], cfg["window"], 2 ** -8, 2 ** -1, units=units,
+                  label="qwen3-8b sampled")
+    assert_parity(rep)
+
+
+# --------------------------------------------------------------------------
+# exact device-only invariants
+# --------------------------------------------------------------------------
+def test_deterministic_and_exact_invariants():
+    q, k, v = make_inputs(2, 4, 2, 320, 128, 60, "channels")
+    o1, m1 = run_gpu(q, k, v, 1, 0, 2 ** -8, 2 ** -2)
+    o2, m2 = run_gpu(q, k, v, 1, 0, 2 ** -8, 2 ** -2)
+    assert np.array_equal(o1, o2) and np.array_equal(m1, m2)
+    # scaling V by 2 scales the output exactly and leaves the mask alone
+    v2 = (torch.from_numpy(bf16_bits_to_f64(v) * 2).float().to(torch.bfloat16)
+          .view(torch.int16).numpy().view(np.uint16))
+    o3, m3 = run_gpu(q, k, v2, 1, 0, 2 ** -8, 2 ** -2)
+    assert np.array_equal(o3, 2 * o1) and np.array_equal(m3, m1)
+    # a duplicated batch gives identical halves
+    qq, kk, vv = (np.concatenate([x[:1], x[:1]]) for x in (q, k, v))
+    o4, m4 = run_gpu(qq, kk, vv, 1, 0, 2 ** -8, 2 ** -2)
+    assert np.array_equal(o4[0], o4[1]) and np.array_equal(m4[0], m4[1])
+    assert np.array_equal(o4[0], o1[0])
+
+
+def test_device_stats_match_oracle_counts():
+    import mixed_precision_attention_lamp_amd as lamp
+    for (S, causal, window) in ((300, 1, 0), (333, 1, 100), (130, 0, 0)):
+        q, k, v = make_inputs(1, 4, 2, S, 64, 70 + S, "channels")
+        qd, kd, vd = to_device(q), to_device(k), to_device(v)
+        _, mask = lamp.attention(qd, kd, vd, causal, window, 2 ** -8, 2 ** -3)
+        dev = lamp.subblock_stats(mask, S, causal, window)
+        host = L.subblock_stats(mask.cpu().numpy(), S, causal, window)
+        for key in ("hist", "visited_tiles", "visited_subblocks", "flagged_subblocks",
+                    "visible_entries", "flagged_entries"):
+            assert dev[key] == host[key], (key, dev[key], host[key])
