@@ -19,6 +19,10 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "liblamp.so")
 SOURCES = ["quant.hip", "attn.hip", "stats.hip", "lamp_api.cpp"]
+# Device sources: inputs are finite (documented in lamp.h), so max/min need no
+# NaN quieting.  Not for lamp_api.cpp, whose argument checks test for NaN.
+DEVICE_FLAGS = {"quant.hip": ["-fno-honor-nans"], "attn.hip": ["-fno-honor-nans"],
+                "stats.hip": ["-fno-honor-nans"]}
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
@@ -32,7 +36,8 @@ FLAGS = [
 
 
 def _compile(src, obj):
-    cmd = [HIPCC, *FLAGS, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *FLAGS, *DEVICE_FLAGS.get(src, []), "-x", "hip", "-c", os.path.join(CSRC, src),
+           "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     noise = "is not a recognized feature for this target"
     err = "\n".join(l for l in r.stderr.splitlines() if noise not in l)

@@ -17,6 +17,16 @@
 //   7. a mask byte per tile records the flags ("16-bit sub-blocks per tile",
 //      tables 1-6).
 //
+// Schedule: the loop over KV tiles is software-pipelined.  In the iteration of
+// tile t a wave issues the P.V products of tile t-1 on the matrix cores in the
+// same straight-line block as the vector work of tile t (max, exponentials,
+// 8-bit rounding), so that the two overlap; after the sub-block test and the
+// 16-bit recompute of tile t it issues the Q.K^T products of tile t+1, which
+// run under the rescale, the LDS stores and the barrier.  Tiles are staged through registers into unpadded LDS
+// layouts whose 16-byte chunks are XOR-swizzled by row (conflict-free operand
+// reads); K8 runs two tiles ahead of the vector work (two LDS slots), K16 one
+// and V^T zero (one slot each).  Q8 and Q16 rows stay in each wave's LDS.
+//
 // Work decomposition: a workgroup of eight waves shares staged K/V tiles.  A
 // pair of waves owns one 64-row query block of one query head (32 rows each,
 // so that the fp32 output accumulator stays in architectural registers, where
@@ -28,6 +38,8 @@
 // makes the row max a register reduction plus two cross-lane steps and lets
 // the exponentials feed the P.V operand in place.
 #include <hip/hip_runtime.h>
+
+#include <cmath>
 
 #include "common.hpp"
 #include "kernels.hpp"
@@ -54,8 +66,9 @@ struct AttnArgs {
     float* dump_s;       // debug: [B, Hq, S, S] 8-bit accumulators (or null)
     uint16_t* dump_p;    // debug: [B, Hq, S, S] final bf16 weights (or null)
     double l_d;          // log2(e) / sqrt(D), fp64
-    float e_delta;
+    float x_delta;       // first stage: exp2 argument threshold (log2 of the e4m3 boundary)
     float t2;
+    int test_mode;       // 0: no test (second stage off), 1: both stages, 2: second stage only
     int B, Hq, Hkv, S, nT, S_pad;
     int causal, window;
     int G;               // Hq / Hkv
@@ -68,26 +81,39 @@ struct AttnArgs {
 
 template <int D>
 struct Cfg {
-    static constexpr int kK8Stride = D + 16;          // bytes per staged K8 row
-    static constexpr int kK16Stride = 2 * D + 16;     // bytes per staged K16 / Q16 row
-    static constexpr int kVtStride = 2 * kTileKeys + 16;  // bytes per staged V^T row (64 keys)
-    static constexpr int kK8Bytes = kTileKeys * kK8Stride;
-    static constexpr int kK16Bytes = kTileKeys * kK16Stride;
-    static constexpr int kVtBytes = D * kVtStride;
-    static constexpr int kBufBytes = kK8Bytes + kK16Bytes + kVtBytes;
-    static constexpr int kQ16Bytes = kWaveRows * kK16Stride;   // per wave
-    static constexpr int kLdsBytes = 2 * kBufBytes + kWaves * kQ16Bytes;
-    // 16-byte chunks of one staged tile
-    static constexpr int kK8Chunks = kTileKeys * D / 16;
-    static constexpr int kK16Chunks = kTileKeys * D * 2 / 16;
-    static constexpr int kVtChunks = D * kTileKeys * 2 / 16;
-    static constexpr int kK8It = (kK8Chunks + kThreads - 1) / kThreads;
-    static constexpr int kK16It = (kK16Chunks + kThreads - 1) / kThreads;
-    static constexpr int kVtIt = (kVtChunks + kThreads - 1) / kThreads;
-    static constexpr int kStage = kK8It + kK16It + kVtIt;
+    static constexpr int kK8Row = D;                   // bytes per staged row
+    static constexpr int kK16Row = 2 * D;
+    static constexpr int kVtRow = 2 * kTileKeys;
+    static constexpr int kK8Bytes = kTileKeys * kK8Row;
+    static constexpr int kK16Bytes = kTileKeys * kK16Row;
+    static constexpr int kVtBytes = D * kVtRow;
+    static constexpr int kQ16Bytes = kWaveRows * kK16Row;      // per wave
+    static constexpr int kQ8Bytes = kWaveRows * kK8Row;        // per wave
+    static constexpr int kK8Off = 0;                            // two slots
+    static constexpr int kK16Off = 2 * kK8Bytes;                // one slot
+    static constexpr int kVtOff = kK16Off + kK16Bytes;          // one slot
+    static constexpr int kQ16Off = kVtOff + kVtBytes;
+    static constexpr int kQ8Off = kQ16Off + kWaves * kQ16Bytes;
+    static constexpr int kLdsBytes = kQ8Off + kWaves * kQ8Bytes;
     static constexpr int kDB = D / 16;        // 16-wide output column blocks
     static constexpr int kDC = D / 32;        // 32-deep bf16 matrix-core steps
 };
+
+// XOR swizzle of the 16-byte chunks of a staged row (NC chunks per row): the
+// 16 lanes of a lane group read 16 consecutive rows at one logical chunk and
+// hit distinct LDS banks.
+template <int NC>
+__device__ __forceinline__ int swz(int row) {
+    if constexpr (NC >= 16) return row & 15;
+    else if constexpr (NC == 8) return (row ^ (row >> 3)) & 7;
+    else return ((row >> 1) ^ (row >> 2)) & 3;
+}
+
+// Byte offset of logical chunk `chunk` of row `row` in a staged tile.
+template <int RowBytes>
+__device__ __forceinline__ int lds_off(int row, int chunk) {
+    return row * RowBytes + ((chunk ^ swz<RowBytes / 16>(row)) << 4);
+}
 
 __device__ __forceinline__ int tile_lo(int r, int window) {
     if (window <= 0) return 0;
@@ -138,10 +164,12 @@ __device__ float acc_threshold(float t2, float c8) {
     return a;
 }
 
-template <int D, bool kDump>
+// kMode: 0 = no test (second stage off), 1 = both stages, 2 = second stage only.
+template <int D, bool kDump, int kMode>
 __global__ __launch_bounds__(kThreads, 1) void lamp_attn_kernel(AttnArgs a) {
     using C = Cfg<D>;
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+    __shared__ uint32_t flag_lds[kWaves];    // 4-bit flag sets exchanged by wave pairs
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6;
@@ -173,39 +201,103 @@ __global__ __launch_bounds__(kThreads, 1) void lamp_attn_kernel(AttnArgs a) {
     const size_t kv_head = (size_t)b * a.Hkv + hk;
     const size_t q_head = (size_t)b * a.Hq + hq;
 
-    uint8_t* q16_lds = lds + 2 * C::kBufBytes + wave * C::kQ16Bytes;
-    __shared__ uint32_t flag_lds[kWaves];    // 4-bit flag sets exchanged by wave pairs
+    uint8_t* q16_lds = lds + C::kQ16Off + wave * C::kQ16Bytes;
+    uint8_t* q8_lds = lds + C::kQ8Off + wave * C::kQ8Bytes;
 
-    // ---- prologue: Q16 rows into this wave's LDS, Q8 operand into registers -----
-    v8i qf[kQG];
-    float m_run[kQG], c8 = 0.0f, a2 = 0.0f;
+    // ---- staging: register loads at the start of an iteration, LDS stores at its end
+    // Thread tid owns the 16-byte chunks tid + kThreads*i of a tile, i.e. LDS
+    // bytes [16 c, 16 c + 16) of the swizzled layout, and loads the global chunk
+    // that belongs there.
+    constexpr int kK8Ch = C::kK8Bytes / 16 / kThreads;     // chunks per thread and tile
+    constexpr int kK16Ch = C::kK16Bytes / 16 / kThreads;
+    constexpr int kVtCh = C::kVtBytes / 16 / kThreads;
+    static_assert(kK16Ch >= 1 && kVtCh >= 1, "tile smaller than one chunk per thread");
+    constexpr int kK8ChMin = kK8Ch > 0 ? kK8Ch : 1;
+    u32x4 st_k8[kK8ChMin], st_k16[kK16Ch], st_vt[kVtCh];
+    auto load_k8 = [&](int t) __attribute__((always_inline)) {
+        const uint8_t* src = a.k8 + (kv_head * a.S_pad + (size_t)t * kTileKeys) * D;
+        constexpr int kNC = C::kK8Row / 16;
+#pragma unroll
+        for (int i = 0; i < kK8ChMin; ++i) {
+            const int p = min((tid + i * kThreads) * 16, C::kK8Bytes - 16);
+            const int row = p / C::kK8Row, slot = (p % C::kK8Row) >> 4;
+            st_k8[i] = *reinterpret_cast<const u32x4*>(src + row * C::kK8Row + ((slot ^ swz<kNC>(row)) << 4));
+        }
+    };
+    auto store_k8 = [&](int t) __attribute__((always_inline)) {
+        uint8_t* base = lds + C::kK8Off + (t & 1) * C::kK8Bytes;
+#pragma unroll
+        for (int i = 0; i < kK8ChMin; ++i) {
+            const int p = (tid + i * kThreads) * 16;
+            if (p < C::kK8Bytes) *reinterpret_cast<u32x4*>(base + p) = st_k8[i];
+        }
+    };
+    auto load_k16 = [&](int t) __attribute__((always_inline)) {
+        constexpr int kNC = C::kK16Row / 16;
+#pragma unroll
+        for (int i = 0; i < kK16Ch; ++i) {
+            const int p = (tid + i * kThreads) * 16;
+            const int row = p / C::kK16Row, slot = (p % C::kK16Row) >> 4;
+            // keys past the end reload the last key: they are masked out
+            const int key = min(t * kTileKeys + row, a.S - 1);
+            st_k16[i] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint8_t*>(a.k16 + (kv_head * a.S + key) * D) +
+                                                        ((slot ^ swz<kNC>(row)) << 4));
+        }
+    };
+    auto store_k16 = [&]() __attribute__((always_inline)) {
+        uint8_t* base = lds + C::kK16Off;
+#pragma unroll
+        for (int i = 0; i < kK16Ch; ++i) *reinterpret_cast<u32x4*>(base + (tid + i * kThreads) * 16) = st_k16[i];
+    };
+    auto load_vt = [&](int t) __attribute__((always_inline)) {
+        const uint8_t* src = reinterpret_cast<const uint8_t*>(a.vt + (kv_head * a.nT + t) * (size_t)D * kTileKeys);
+        constexpr int kNC = C::kVtRow / 16;
+#pragma unroll
+        for (int i = 0; i < kVtCh; ++i) {
+            const int p = (tid + i * kThreads) * 16;
+            const int row = p / C::kVtRow, slot = (p % C::kVtRow) >> 4;
+            st_vt[i] = *reinterpret_cast<const u32x4*>(src + row * C::kVtRow + ((slot ^ swz<kNC>(row)) << 4));
+        }
+    };
+    auto store_vt = [&]() __attribute__((always_inline)) {
+        uint8_t* base = lds + C::kVtOff;
+#pragma unroll
+        for (int i = 0; i < kVtCh; ++i) *reinterpret_cast<u32x4*>(base + (tid + i * kThreads) * 16) = st_vt[i];
+    };
+
+    // ---- prologue: this wave's Q16 and Q8 rows into its LDS -----------------------
+    float m_run[kQG], c8 = 0.0f, inv_c8 = 0.0f, a2 = 0.0f;
     const float c16 = (float)a.l_d;
+    {
+        constexpr int kNC = C::kK16Row / 16;
+        const int qmax = a.S - 1;
+#pragma unroll
+        for (int i = 0; i < C::kQ16Bytes / 1024; ++i) {
+            const int p = i * 1024 + lane * 16;
+            const int row = p / C::kK16Row, slot = (p % C::kK16Row) >> 4;
+            const int gq = min(row0 + row, qmax);    // rows past the end are never written out
+            *reinterpret_cast<u32x4*>(q16_lds + p) = *reinterpret_cast<const u32x4*>(
+                reinterpret_cast<const uint8_t*>(a.q16 + (q_head * a.S + gq) * D) + ((slot ^ swz<kNC>(row)) << 4));
+        }
+    }
+    {
+        constexpr int kNC = C::kK8Row / 16;
+        const int qmax = a.S_pad - 1;
+#pragma unroll
+        for (int i = 0; i < C::kQ8Bytes / 1024; ++i) {
+            const int p = i * 1024 + lane * 16;
+            const int row = p / C::kK8Row, slot = (p % C::kK8Row) >> 4;
+            const int gq = min(row0 + row, qmax);
+            *reinterpret_cast<u32x4*>(q8_lds + p) = *reinterpret_cast<const u32x4*>(
+                a.q8 + (q_head * a.S_pad + gq) * D + ((slot ^ swz<kNC>(row)) << 4));
+        }
+    }
+#pragma unroll
+    for (int qg = 0; qg < kQG; ++qg) m_run[qg] = -__builtin_inff();
     if (active) {
-        constexpr int kChunksPerRow = D / 8;
-#pragma unroll
-        for (int it = 0; it < kWaveRows * kChunksPerRow / 64; ++it) {
-            const int c = lane + it * 64;
-            const int row = c / kChunksPerRow, col = c % kChunksPerRow;
-            const int gq = row0 + row;
-            u32x4 w = {0u, 0u, 0u, 0u};
-            if (gq < a.S) w = *reinterpret_cast<const u32x4*>(a.q16 + (q_head * a.S + gq) * D + col * 8);
-            *reinterpret_cast<u32x4*>(q16_lds + row * C::kK16Stride + col * 16) = w;
-        }
-#pragma unroll
-        for (int qg = 0; qg < kQG; ++qg) {
-            const int row = row0 + qg * 16 + n16;
-            const uint8_t* src = a.q8 + (q_head * a.S_pad + row) * D + g * 32;
-            u32x4 lo = {0u, 0u, 0u, 0u}, hi = {0u, 0u, 0u, 0u};
-            if (g * 32 < D) {
-                lo = *reinterpret_cast<const u32x4*>(src);
-                hi = *reinterpret_cast<const u32x4*>(src + 16);
-            }
-            qf[qg] = v8i{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
-                         (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
-            m_run[qg] = -__builtin_inff();
-        }
         c8 = (float)((double)a.q_scale[q_head] * (double)a.k_scale[kv_head] * a.l_d);
         a2 = acc_threshold(a.t2, c8);
+        inv_c8 = 1.0f / c8;
         if (a.mask && half == 0) {
             uint8_t* mrow = a.mask + (q_head * a.nT + r) * a.nT;
             for (int t = lane; t < a.nT; t += 64)
@@ -222,82 +314,36 @@ __global__ __launch_bounds__(kThreads, 1) void lamp_attn_kernel(AttnArgs a) {
         for (int db = 0; db < C::kDB; ++db) acc_o[qg][db] = v4f{0.f, 0.f, 0.f, 0.f};
     }
 
-    // ---- staging of one KV tile (all threads) ------------------------------------
-    // Loads are unconditional (addresses clamped into the tensors) so that they
-    // stay in flight together; rows past the end are zeroed when stored to LDS.
-    u32x4 stage[C::kStage];
-    uint32_t k16_valid = 0;    // bit it: chunk it of K16 lies inside the sequence
-    auto stage_load = [&](int t) {
-        const uint8_t* k8src = a.k8 + (kv_head * a.S_pad + (size_t)t * kTileKeys) * D;
-#pragma unroll
-        for (int it = 0; it < C::kK8It; ++it) {
-            const int c = min(tid + it * kThreads, C::kK8Chunks - 1);
-            stage[it] = *reinterpret_cast<const u32x4*>(k8src + (size_t)c * 16);
-        }
-        k16_valid = 0;
-#pragma unroll
-        for (int it = 0; it < C::kK16It; ++it) {
-            const int c = min(tid + it * kThreads, C::kK16Chunks - 1);
-            const int row = c / (D / 8), col = c % (D / 8);
-            const int key = t * kTileKeys + row;
-            k16_valid |= (key < a.S ? 1u : 0u) << it;
-            const int kc = min(key, a.S - 1);
-            stage[C::kK8It + it] = *reinterpret_cast<const u32x4*>(a.k16 + (kv_head * a.S + kc) * D + col * 8);
-        }
-        const uint16_t* vsrc = a.vt + (kv_head * a.nT + t) * (size_t)D * kTileKeys;
-#pragma unroll
-        for (int it = 0; it < C::kVtIt; ++it) {
-            const int c = min(tid + it * kThreads, C::kVtChunks - 1);
-            stage[C::kK8It + C::kK16It + it] = *reinterpret_cast<const u32x4*>(vsrc + (size_t)c * 8);
-        }
-    };
-    auto stage_store = [&](int buf) {
-        uint8_t* base = lds + buf * C::kBufBytes;
-#pragma unroll
-        for (int it = 0; it < C::kK8It; ++it) {
-            const int c = tid + it * kThreads;
-            const int row = c / (D / 16), col = c % (D / 16);
-            if (c < C::kK8Chunks) *reinterpret_cast<u32x4*>(base + row * C::kK8Stride + col * 16) = stage[it];
-        }
-#pragma unroll
-        for (int it = 0; it < C::kK16It; ++it) {
-            const int c = tid + it * kThreads;
-            const int row = c / (D / 8), col = c % (D / 8);
-            u32x4 w = stage[C::kK8It + it];
-            if (!((k16_valid >> it) & 1u)) w = u32x4{0u, 0u, 0u, 0u};
-            if (c < C::kK16Chunks)
-                *reinterpret_cast<u32x4*>(base + C::kK8Bytes + row * C::kK16Stride + col * 16) = w;
-        }
-#pragma unroll
-        for (int it = 0; it < C::kVtIt; ++it) {
-            const int c = tid + it * kThreads;
-            const int row = c / 8, col = c % 8;
-            if (c < C::kVtChunks)
-                *reinterpret_cast<u32x4*>(base + C::kK8Bytes + C::kK16Bytes + row * C::kVtStride + col * 16) =
-                    stage[C::kK8It + C::kK16It + it];
-        }
+    auto work = [&](int t) __attribute__((always_inline)) {
+        return active && t >= t_begin && t <= t_end && tile_visited(r, t, a.S, a.causal, a.window);
     };
 
-    // ---- per-tile state carried across the flag exchange ----------------------------
-    u32x2 P[kQG][4];          // bf16 weights: keys 16kb + 4g + {0..3}, query 16qg + n16
-    float alpha[kQG], m_use[kQG];
-    uint32_t vis[kQG];        // masked tiles: bit kb*4+i = entry visible
-
-    // (1)-(4): 8-bit logits, running max, 8-bit exponentials, two-stage test.
-    // Returns this wave's 4-bit flag set (wave-uniform).
-    auto first_pass = [&](int t, int buf, auto masked_tag) -> uint32_t {
-        constexpr bool kMasked = decltype(masked_tag)::value;
-        const uint8_t* k8l = lds + buf * C::kBufBytes;
-
-        // (1) s[qg][kb][i] = 8-bit accumulator of key 16kb + 4g + i, query 16qg + n16
-        v4f s[kQG][4];
+    // ---- matrix-core phases ---------------------------------------------------------
+    // Q.K^T of tile t: s[qg][kb][i] = 8-bit accumulator of key 16kb + 4g + i, query 16qg + n16
+    auto qk = [&](v4f (&s)[kQG][4], int t) __attribute__((always_inline)) {
+        const uint8_t* k8l = lds + C::kK8Off + (t & 1) * C::kK8Bytes;
+        v8i qf[kQG];
+#pragma unroll
+        for (int qg = 0; qg < kQG; ++qg) {
+            qf[qg] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
+            const int row = qg * 16 + n16;
+            if (D >= 128 || g * 32 < D) {
+                const int gg = D >= 128 ? g : (g & 1);
+                const u32x4 lo = *reinterpret_cast<const u32x4*>(q8_lds + lds_off<C::kK8Row>(row, 2 * gg));
+                const u32x4 hi = *reinterpret_cast<const u32x4*>(q8_lds + lds_off<C::kK8Row>(row, 2 * gg + 1));
+                qf[qg] = v8i{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                             (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+            }
+        }
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) {
+            // lane group g holds depth 32g .. 32g+31; for D = 64 groups 2, 3 hold zeros
             v8i ka = {0, 0, 0, 0, 0, 0, 0, 0};
-            if (g * 32 < D) {
-                const uint8_t* p = k8l + (kb * 16 + n16) * C::kK8Stride + g * 32;
-                const u32x4 lo = *reinterpret_cast<const u32x4*>(p);
-                const u32x4 hi = *reinterpret_cast<const u32x4*>(p + 16);
+            const int row = kb * 16 + n16;
+            if (D >= 128 || g * 32 < D) {
+                const int gg = D >= 128 ? g : (g & 1);
+                const u32x4 lo = *reinterpret_cast<const u32x4*>(k8l + lds_off<C::kK8Row>(row, 2 * gg));
+                const u32x4 hi = *reinterpret_cast<const u32x4*>(k8l + lds_off<C::kK8Row>(row, 2 * gg + 1));
                 ka = v8i{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
                          (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
             }
@@ -306,7 +352,101 @@ __global__ __launch_bounds__(kThreads, 1) void lamp_attn_kernel(AttnArgs a) {
                 s[qg][kb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
                     ka, qf[qg], v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
         }
+    };
+    // P.V of tile t (and the row sums, with an all-ones operand)
+    const v8bf ones = {(__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f,
+                       (__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f};
+    auto pv = [&](const u32x2 (&P)[kQG][4], int t) __attribute__((always_inline)) {
+        (void)t;
+        const uint8_t* vtl = lds + C::kVtOff;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            v8bf pb[kQG];
+#pragma unroll
+            for (int qg = 0; qg < kQG; ++qg) {
+                const u32x4 w = {P[qg][2 * h][0], P[qg][2 * h][1], P[qg][2 * h + 1][0], P[qg][2 * h + 1][1]};
+                pb[qg] = __builtin_bit_cast(v8bf, w);
+            }
+#pragma unroll
+            for (int db = 0; db < C::kDB; ++db) {
+                const v8bf va = *reinterpret_cast<const v8bf*>(vtl + lds_off<C::kVtRow>(db * 16 + n16, h * 4 + g));
+#pragma unroll
+                for (int qg = 0; qg < kQG; ++qg)
+                    acc_o[qg][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb[qg], acc_o[qg][db], 0, 0, 0);
+            }
+#pragma unroll
+            for (int qg = 0; qg < kQG; ++qg)
+                acc_l[qg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pb[qg], acc_l[qg], 0, 0, 0);
+        }
+    };
 
+    // ---- per-tile vector state ---------------------------------------------------------
+    float alpha[kQG], m_use[kQG];
+    float smax[kQG][4];                 // per (lane, sub-block) maxima of the 8-bit accumulators
+    float smin[kMode == 2 ? kQG : 1][4];    // and minima, when the first stage is off
+    uint32_t vis[kQG];                  // masked tiles: bit kb*4+i = entry visible
+
+    // (2)-(3): running max and 8-bit exponentials of tile t, straight-line code.
+    auto softmax = [&](const v4f (&s)[kQG][4], u32x2 (&P)[kQG][4], int t, auto masked_tag) __attribute__((always_inline)) {
+        constexpr bool kMasked = decltype(masked_tag)::value;
+        constexpr float kNegInf = -__builtin_inff();
+        if constexpr (kMasked) {
+#pragma unroll
+            for (int qg = 0; qg < kQG; ++qg) {
+                vis[qg] = 0u;
+                const int qi = row0 + qg * 16 + n16;
+#pragma unroll
+                for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int kj = t * kTileKeys + kb * 16 + g * 4 + i;
+                        vis[qg] |= (pair_visible(qi, kj, a.S, a.causal, a.window) ? 1u : 0u) << (kb * 4 + i);
+                    }
+            }
+        }
+        // running max in the log2 domain: rounding is monotone, so the max of
+        // the fp32 logits is c8 times the max accumulator, rounded
+#pragma unroll
+        for (int qg = 0; qg < kQG; ++qg) {
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb) {
+                float v[4], w[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    v[i] = w[i] = s[qg][kb][i];
+                    if constexpr (kMasked) {
+                        const bool vv = (vis[qg] >> (kb * 4 + i)) & 1u;
+                        v[i] = vv ? v[i] : kNegInf;
+                        w[i] = vv ? w[i] : -kNegInf;
+                    }
+                }
+                smax[qg][kb] = __builtin_fmaxf(__builtin_fmaxf(v[0], v[1]), __builtin_fmaxf(v[2], v[3]));
+                if constexpr (kMode == 2)
+                    smin[qg][kb] = __builtin_fminf(__builtin_fminf(w[0], w[1]), __builtin_fminf(w[2], w[3]));
+            }
+            float mx = __builtin_fmaxf(__builtin_fmaxf(smax[qg][0], smax[qg][1]),
+                                       __builtin_fmaxf(smax[qg][2], smax[qg][3]));
+            mx = max_over_lane_groups(mx);
+            const float mt = mx == kNegInf ? mx : mx * c8;
+            const float mn = __builtin_fmaxf(m_run[qg], mt);
+            alpha[qg] = mn == m_run[qg] ? 1.0f : fast_exp2(m_run[qg] - mn);
+            m_use[qg] = mn == kNegInf ? 0.0f : mn;
+            m_run[qg] = mn;
+        }
+        // 8-bit exponentials against the running max
+#pragma unroll
+        for (int qg = 0; qg < kQG; ++qg)
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb) {
+                float e[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    e[i] = fast_exp2(__builtin_fmaf(s[qg][kb][i], c8, -m_use[qg]));
+                    if constexpr (kMasked) e[i] = ((vis[qg] >> (kb * 4 + i)) & 1u) ? e[i] : 0.0f;
+                }
+                const uint32_t w = cvt_pk_e4m3_unit<true>(e[2], e[3], cvt_pk_e4m3_unit<false>(e[0], e[1], 0u));
+                P[qg][kb] = u32x2{e4m3x2_to_bf16x2<false>(w), e4m3x2_to_bf16x2<true>(w)};
+            }
         if constexpr (kDump) {
 #pragma unroll
             for (int qg = 0; qg < kQG; ++qg) {
@@ -320,188 +460,180 @@ __global__ __launch_bounds__(kThreads, 1) void lamp_attn_kernel(AttnArgs a) {
                     }
             }
         }
+    };
 
-        if constexpr (kMasked) {
+    // (4): the look-ahead test on the accumulators of tile t; returns the wave's
+    // 4-bit flag set (wave-uniform).  First stage: the 8-bit exponential is at
+    // least delta, i.e. its argument x = acc c8 - m is at least x_delta, i.e.
+    // acc >= a1 = (x_delta + m) / c8.  Second stage: |acc| >= a2.  When
+    // a1 > -a2 both hold iff acc >= max(a1, a2), so a sub-block holds a
+    // sensitive entry of this row iff its maximum does: one compare per (lane,
+    // sub-block).  Rows with a1 <= -a2 (a very negative running max) fall back
+    // to a per-entry test for the wave.
+    auto test = [&](const v4f (&s)[kQG][4], bool masked) __attribute__((always_inline)) -> uint32_t {
+        uint64_t hit[4] = {0, 0, 0, 0};
+        if constexpr (kMode == 1) {
+            bool slow = false;
 #pragma unroll
             for (int qg = 0; qg < kQG; ++qg) {
-                vis[qg] = 0u;
-                const int qi = row0 + qg * 16 + n16;
+                const float a1 = (a.x_delta + m_use[qg]) * inv_c8;
+                const float thr = __builtin_fmaxf(a1, a2);
+                slow |= a1 <= -a2;
+#pragma unroll
+                for (int kb = 0; kb < 4; ++kb) hit[kb] |= wave_ballot(smax[qg][kb] >= thr);
+            }
+            if (wave_ballot(slow) != 0) {
+#pragma unroll
+                for (int kb = 0; kb < 4; ++kb) hit[kb] = 0;
+#pragma unroll
+                for (int qg = 0; qg < kQG; ++qg)
+#pragma unroll
+                    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            const float v = s[qg][kb][i];
+                            bool sens = __builtin_fmaf(v, c8, -m_use[qg]) >= a.x_delta;
+                            sens = sens && __builtin_fabsf(v) >= a2;
+                            if (masked) sens = sens && ((vis[qg] >> (kb * 4 + i)) & 1u);
+                            hit[kb] |= wave_ballot(sens);
+                        }
+            }
+        } else if constexpr (kMode == 2) {
+            // first stage off: every visible entry is active; |acc| >= a2 holds
+            // for some entry iff the sub-block maximum or minus its minimum does
+#pragma unroll
+            for (int qg = 0; qg < kQG; ++qg)
 #pragma unroll
                 for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const int kj = t * kTileKeys + kb * 16 + g * 4 + i;
-                        if (pair_visible(qi, kj, a.S, a.causal, a.window)) vis[qg] |= 1u << (kb * 4 + i);
-                    }
-            }
+                    hit[kb] |= wave_ballot(smax[qg][kb] >= a2) | wave_ballot(smin[qg][kb] <= -a2);
         }
-
-        // (2) running max in the log2 domain: rounding is monotone, so the max
-        //     of the fp32 logits is c8 times the max accumulator, rounded
-#pragma unroll
-        for (int qg = 0; qg < kQG; ++qg) {
-            float mx = -__builtin_inff();
-#pragma unroll
-            for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    float v = s[qg][kb][i];
-                    if constexpr (kMasked) v = ((vis[qg] >> (kb * 4 + i)) & 1u) ? v : -__builtin_inff();
-                    mx = __builtin_fmaxf(mx, v);
-                }
-            mx = max_over_lane_groups(mx);
-            const float mt = mx == -__builtin_inff() ? mx : mx * c8;
-            const float mn = __builtin_fmaxf(m_run[qg], mt);
-            alpha[qg] = mn == m_run[qg] ? 1.0f : fast_exp2(m_run[qg] - mn);
-            m_use[qg] = mn == -__builtin_inff() ? 0.0f : mn;
-            m_run[qg] = mn;
-        }
-
-        // (3) 8-bit exponentials, (4) first and second stage of the test.  Each
-        //     stage is one compare whose lane mask stays in scalar registers.
-        uint64_t hit[4] = {0, 0, 0, 0};
-#pragma unroll
-        for (int qg = 0; qg < kQG; ++qg)
-#pragma unroll
-            for (int kb = 0; kb < 4; ++kb) {
-                float e[4];
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    e[i] = fast_exp2(__builtin_fmaf(s[qg][kb][i], c8, -m_use[qg]));
-                    if constexpr (kMasked) {
-                        const bool vv = (vis[qg] >> (kb * 4 + i)) & 1u;
-                        e[i] = vv ? e[i] : 0.0f;
-                        hit[kb] |= wave_ballot(e[i] >= a.e_delta) & wave_ballot(__builtin_fabsf(s[qg][kb][i]) >= a2) &
-                                   wave_ballot(vv);
-                    } else {
-                        hit[kb] |= wave_ballot(e[i] >= a.e_delta) & wave_ballot(__builtin_fabsf(s[qg][kb][i]) >= a2);
-                    }
-                }
-                const uint32_t w = cvt_pk_e4m3_unit<true>(e[2], e[3], cvt_pk_e4m3_unit<false>(e[0], e[1], 0u));
-                P[qg][kb] = u32x2{e4m3x2_to_bf16x2<false>(w), e4m3x2_to_bf16x2<true>(w)};
-            }
         uint32_t flags = 0;
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) flags |= (hit[kb] != 0 ? 1u : 0u) << kb;
         return flags;
     };
 
-    // (5)-(7): 16-bit recompute of the flagged sub-blocks, rescale, P.V, mask byte.
-    auto second_pass = [&](int t, int buf, uint32_t flags, auto masked_tag) {
-        constexpr bool kMasked = decltype(masked_tag)::value;
-        const uint8_t* k16l = lds + buf * C::kBufBytes + C::kK8Bytes;
-        const uint8_t* vtl = k16l + C::kK16Bytes;
-
-        // (5) flagged sub-blocks.  The flag set is wave-uniform (scalar), so each
-        //     sub-block is either skipped or recomputed by the whole wave with a
-        //     scalar branch: no lane diverges, and the register tile P is
-        //     addressed with compile-time indices.
+    // (5): 16-bit recompute of tile t.  The flag set is wave-uniform (scalar):
+    // the wave walks its set bits behind scalar branches, running the bf16
+    // logits of each flagged sub-block on the matrix cores and rounding its
+    // exponentials to bf16 into the compile-time-indexed register tile P.
+    auto recompute = [&](u32x2 (&P)[kQG][4], uint32_t flags, bool masked) __attribute__((always_inline)) {
+        const uint8_t* k16l = lds + C::kK16Off;
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
             if (!((flags >> c) & 1u)) continue;
-            v8bf ka[C::kDC];
+            v4f acc16[kQG];
 #pragma unroll
-            for (int ch = 0; ch < C::kDC; ++ch)
-                ka[ch] = *reinterpret_cast<const v8bf*>(k16l + (c * 16 + n16) * C::kK16Stride + (ch * 32 + g * 8) * 2);
+            for (int ch = 0; ch < C::kDC; ++ch) {
+                const v8bf ka = *reinterpret_cast<const v8bf*>(k16l + lds_off<C::kK16Row>(c * 16 + n16, ch * 4 + g));
+#pragma unroll
+                for (int qg = 0; qg < kQG; ++qg) {
+                    const v8bf qb = *reinterpret_cast<const v8bf*>(q16_lds + lds_off<C::kK16Row>(qg * 16 + n16, ch * 4 + g));
+                    acc16[qg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                        ka, qb, ch == 0 ? v4f{0.f, 0.f, 0.f, 0.f} : acc16[qg], 0, 0, 0);
+                }
+            }
 #pragma unroll
             for (int qg = 0; qg < kQG; ++qg) {
-                v4f acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int ch = 0; ch < C::kDC; ++ch) {
-                    const v8bf qb = *reinterpret_cast<const v8bf*>(q16_lds + (qg * 16 + n16) * C::kK16Stride + (ch * 32 + g * 8) * 2);
-                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[ch], qb, acc, 0, 0, 0);
-                }
                 float e[4];
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    e[i] = fast_exp2(__builtin_fmaf(acc[i], c16, -m_use[qg]));
-                    if constexpr (kMasked) e[i] = ((vis[qg] >> (c * 4 + i)) & 1u) ? e[i] : 0.0f;
+                    e[i] = fast_exp2(__builtin_fmaf(acc16[qg][i], c16, -m_use[qg]));
+                    if (masked) e[i] = ((vis[qg] >> (c * 4 + i)) & 1u) ? e[i] : 0.0f;
                 }
                 P[qg][c] = u32x2{f32x2_to_bf16x2(e[0], e[1]), f32x2_to_bf16x2(e[2], e[3])};
             }
         }
-
-        if constexpr (kDump) {
-#pragma unroll
-            for (int qg = 0; qg < kQG; ++qg) {
-                const int qi = row0 + qg * 16 + n16;
-#pragma unroll
-                for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const int kj = t * kTileKeys + kb * 16 + g * 4 + i;
-                        const uint32_t w = P[qg][kb][i / 2];
-                        if (qi < a.S && kj < a.S)
-                            a.dump_p[(q_head * a.S + qi) * a.S + kj] = (uint16_t)((i & 1) ? (w >> 16) : (w & 0xFFFFu));
-                    }
-            }
-        }
-
-        // (6) online-softmax rescale, then P.V and the row sums
-        bool rescale = false;
-#pragma unroll
-        for (int qg = 0; qg < kQG; ++qg) rescale |= alpha[qg] != 1.0f;
-        if (wave_ballot(rescale) != 0) {
-#pragma unroll
-            for (int qg = 0; qg < kQG; ++qg) {
-                acc_l[qg] *= alpha[qg];
-#pragma unroll
-                for (int db = 0; db < C::kDB; ++db) acc_o[qg][db] *= alpha[qg];
-            }
-        }
-        const v8bf ones = {(__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f,
-                           (__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f};
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            v8bf pb[kQG];
-#pragma unroll
-            for (int qg = 0; qg < kQG; ++qg) {
-                const u32x4 w = {P[qg][2 * h][0], P[qg][2 * h][1], P[qg][2 * h + 1][0], P[qg][2 * h + 1][1]};
-                pb[qg] = __builtin_bit_cast(v8bf, w);
-            }
-#pragma unroll
-            for (int db = 0; db < C::kDB; ++db) {
-                const v8bf va = *reinterpret_cast<const v8bf*>(vtl + (db * 16 + n16) * C::kVtStride + h * 64 + g * 16);
-#pragma unroll
-                for (int qg = 0; qg < kQG; ++qg)
-                    acc_o[qg][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb[qg], acc_o[qg][db], 0, 0, 0);
-            }
-#pragma unroll
-            for (int qg = 0; qg < kQG; ++qg)
-                acc_l[qg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pb[qg], acc_l[qg], 0, 0, 0);
-        }
-
-        // (7) mask byte
-        if (a.mask && half == 0 && lane == 0)
-            a.mask[(q_head * a.nT + r) * a.nT + t] = (uint8_t)(0x80u | flags);
     };
 
-    // ---- main loop over the workgroup's KV tiles (double-buffered staging) -----
-    stage_load(t_begin);
-    stage_store(0);
-    __syncthreads();
+    // ---- prologue staging and the first tile's Q.K^T ------------------------------
+    v4f S[kQG][4];
+    u32x2 P[kQG][4];
+    load_k8(t_begin);
+    load_k16(t_begin);
+    store_k8(t_begin);
+    store_k16();
+    if (t_begin + 1 <= t_end) {
+        load_k8(t_begin + 1);
+        store_k8(t_begin + 1);
+    }
+    lds_barrier();
+    if (work(t_begin)) qk(S, t_begin);
+    lds_barrier();   // every wave has read K8(t_begin) before its slot is refilled
+
+    // ---- the pipelined loop ---------------------------------------------------------
     for (int t = t_begin; t <= t_end; ++t) {
-        const int buf = (t - t_begin) & 1;
-        const bool has_next = t < t_end;
-        if (has_next) stage_load(t + 1);
-        const bool work = active && tile_visited(r, t, a.S, a.causal, a.window);
+        const bool ld_k8 = t + 2 <= t_end, ld_k16 = t + 1 <= t_end;
+        // K16 of tile t (loaded in the previous iteration) into its single slot:
+        // every wave has finished the recompute of tile t-1, and the flag
+        // barrier below orders these stores before the recompute of tile t
+        if (t > t_begin) store_k16();
+        const bool w_prev = work(t - 1), w_cur = work(t), w_next = work(t + 1);
         const bool full = tile_full(r, t, a.S, a.causal, a.window);
-        uint32_t flags = 0;
-        if (work) {
-            if (full) flags = first_pass(t, buf, std::integral_constant<bool, false>{});
-            else flags = first_pass(t, buf, std::integral_constant<bool, true>{});
+        // P.V of tile t-1 (reads P before the exponentials of tile t overwrite
+        // it) interleaved with the vector work of tile t, in one block
+        if (w_prev && w_cur && full) {
+            pv(P, t - 1);
+            softmax(S, P, t, std::integral_constant<bool, false>{});
+        } else {
+            if (w_prev) pv(P, t - 1);
+            if (w_cur) {
+                if (full) softmax(S, P, t, std::integral_constant<bool, false>{});
+                else softmax(S, P, t, std::integral_constant<bool, true>{});
+            }
         }
+        // loads for later tiles, stored to LDS before the barrier that ends this
+        // iteration
+        if (ld_k8) load_k8(t + 2);
+        if (ld_k16) load_k16(t + 1);
+        load_vt(t);
+        uint32_t flags = w_cur ? test(S, !full) : 0u;
         // the two waves of a 64-row block OR their flags
         if (lane == 0) flag_lds[wave] = flags;
         lds_barrier();
         flags |= flag_lds[wave ^ 1];
-        if (work) {
-            if (full) second_pass(t, buf, flags, std::integral_constant<bool, false>{});
-            else second_pass(t, buf, flags, std::integral_constant<bool, true>{});
+        if (w_cur && flags != 0) recompute(P, flags, !full);
+        // Q.K^T of tile t+1 runs on the matrix cores under what follows
+        if (w_next) qk(S, t + 1);
+        if (w_cur) {
+            if constexpr (kDump) {
+#pragma unroll
+                for (int qg = 0; qg < kQG; ++qg) {
+                    const int qi = row0 + qg * 16 + n16;
+#pragma unroll
+                    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            const int kj = t * kTileKeys + kb * 16 + g * 4 + i;
+                            const uint32_t w = P[qg][kb][i / 2];
+                            if (qi < a.S && kj < a.S)
+                                a.dump_p[(q_head * a.S + qi) * a.S + kj] = (uint16_t)((i & 1) ? (w >> 16) : (w & 0xFFFFu));
+                        }
+                }
+            }
+            // (6) online-softmax rescale of everything accumulated so far (the
+            //     P.V of tile t-1 included), before the P.V of tile t
+#pragma unroll
+            for (int qg = 0; qg < kQG; ++qg) {
+                if (wave_ballot(alpha[qg] != 1.0f) != 0) {
+                    acc_l[qg] *= alpha[qg];
+#pragma unroll
+                    for (int db = 0; db < C::kDB; ++db) acc_o[qg][db] *= alpha[qg];
+                }
+            }
+            // (7) mask byte
+            if (a.mask && half == 0 && lane == 0)
+                a.mask[(q_head * a.nT + r) * a.nT + t] = (uint8_t)(0x80u | flags);
         }
-        if (has_next) stage_store(buf ^ 1);
+        // K8 of tile t+2 into the slot Q.K^T of tile t used; V^T of tile t into
+        // its single slot (every wave passed the flag barrier, so the P.V of
+        // tile t-1 has read it)
+        if (ld_k8) store_k8(t + 2);
+        store_vt();
         lds_barrier();
     }
+    // P.V of the last tile
+    if (work(t_end)) pv(P, t_end);
 
     // ---- epilogue: out = O / l ------------------------------------------------------
     if (active) {
@@ -525,7 +657,9 @@ hipError_t launch_d(const Shape& sh, const AttnParams& p, hipStream_t st) {
     a.q8 = p.q8; a.k8 = p.k8; a.q16 = p.q16; a.k16 = p.k16; a.vt = p.vt;
     a.q_scale = p.q_scale; a.k_scale = p.k_scale; a.out = p.out; a.mask = p.mask;
     a.dump_s = p.dump_s; a.dump_p = p.dump_p;
-    a.l_d = p.log2e_over_sqrt_d; a.e_delta = p.e_delta; a.t2 = p.t2;
+    a.l_d = p.log2e_over_sqrt_d; a.t2 = p.t2;
+    a.x_delta = p.e_delta > 0.0f ? (float)std::log2((double)p.e_delta) : -__builtin_inff();
+    a.test_mode = !(p.t2 < __builtin_inff()) || !(p.e_delta < __builtin_inff()) ? 0 : (p.e_delta > 0.0f ? 1 : 2);
     a.B = sh.B; a.Hq = sh.Hq; a.Hkv = sh.Hkv; a.S = sh.S; a.nT = sh.nT; a.S_pad = sh.S_pad;
     a.causal = p.causal; a.window = p.window;
     a.G = sh.Hq / sh.Hkv;
@@ -536,13 +670,14 @@ hipError_t launch_d(const Shape& sh, const AttnParams& p, hipStream_t st) {
     a.xcd_remap = (a.n_wg % 8 == 0) ? 1 : 0;
     const size_t lds = Cfg<D>::kLdsBytes;
     const bool dump = p.dump_s != nullptr && p.dump_p != nullptr;
-    const void* fn = dump ? (const void*)lamp_attn_kernel<D, true> : (const void*)lamp_attn_kernel<D, false>;
-    hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    using Fn = void (*)(AttnArgs);
+    static const Fn table[2][3] = {
+        {lamp_attn_kernel<D, false, 0>, lamp_attn_kernel<D, false, 1>, lamp_attn_kernel<D, false, 2>},
+        {lamp_attn_kernel<D, true, 0>, lamp_attn_kernel<D, true, 1>, lamp_attn_kernel<D, true, 2>}};
+    const Fn fn = table[dump ? 1 : 0][a.test_mode];
+    hipError_t e = hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
-    if (dump)
-        hipLaunchKernelGGL((lamp_attn_kernel<D, true>), dim3(a.n_wg), dim3(kThreads), lds, st, a);
-    else
-        hipLaunchKernelGGL((lamp_attn_kernel<D, false>), dim3(a.n_wg), dim3(kThreads), lds, st, a);
+    hipLaunchKernelGGL(fn, dim3(a.n_wg), dim3(kThreads), lds, st, a);
     return hipGetLastError();
 }
 

@@ -74,7 +74,7 @@ int get_workspace(size_t bytes, void** out) {
         if (ws.ptr) {
             e = hipDeviceSynchronize();
             if (e != hipSuccess) return hip_fail(e, "hipDeviceSynchronize");
-            hipFree(ws.ptr);
+            (void)hipFree(ws.ptr);
             ws.ptr = nullptr;
             ws.bytes = 0;
         }
