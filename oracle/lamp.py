@@ -59,8 +59,11 @@ def head_scales(bits):
     a = max |x| over the head's slab (exact).  If a == 0 the scale and its
     inverse are 1, otherwise scale = fl32(a / 448) and inv = fl32(448 / a).
     """
-    x = bf16_bits_to_f64(bits)
-    a = np.abs(x).max(axis=(2, 3))
+    B, H = bits.shape[:2]
+    a = np.zeros((B, H))
+    for b in range(B):          # one slab at a time keeps the temporaries small
+        for h in range(H):
+            a[b, h] = np.abs(bf16_bits_to_f64(bits[b, h])).max()
     safe = np.where(a > 0, a, 1.0)
     scale = np.where(a > 0, fl32(safe / 448.0), 1.0)
     inv = np.where(a > 0, fl32(448.0 / safe), 1.0)
@@ -253,19 +256,45 @@ def run_unit(ctx, b, hq, r, flag_override=None, trace=None):
 # --------------------------------------------------------------------------
 # Whole forward pass
 # --------------------------------------------------------------------------
+class PerHead:
+    """Values of a [B, H, S, D] tensor, computed one (batch, head) slab at a
+    time on first use and kept.  Indexed like the full array with a leading
+    (b, h): ``x[b, h, rows]``.  Nothing but evaluation order differs from
+    computing the whole tensor up front: every step here is per head."""
+
+    def __init__(self, slab):
+        self._slab = slab
+        self._cache = {}
+
+    def __getitem__(self, idx):
+        key = (int(idx[0]), int(idx[1]))
+        if key not in self._cache:
+            self._cache[key] = self._slab(*key)
+        return self._cache[key][tuple(idx[2:])]
+
+
 def prepare(q_bits, k_bits, v_bits, causal, window, delta, tau):
-    """Quantise Q and K and collect everything the units read."""
+    """Scales of Q and K, and per-head access to everything the units read
+    (the e4m3 values of Q and K, and the bf16 values of Q, K and V)."""
     B, Hq, S, D = q_bits.shape
     Hkv = k_bits.shape[1]
     assert Hq % Hkv == 0 and k_bits.shape == v_bits.shape == (B, Hkv, S, D)
-    q8, _, sq, _ = quantize(q_bits)
-    k8, _, sk, _ = quantize(k_bits)
+    sq, iq = head_scales(q_bits)
+    sk, ik = head_scales(k_bits)
+
+    def e4m3_slab(bits, inv):
+        # the quantisation of step 2 on one head: E4M3(fl32(x * inv))
+        return lambda b, h: round_e4m3(fl32(bf16_bits_to_f64(bits[b, h]) * inv[b, h]))
+
+    def bf16_slab(bits):
+        return lambda b, h: bf16_bits_to_f64(bits[b, h])
+
     return dict(B=B, Hq=Hq, Hkv=Hkv, S=S, D=D, G=Hq // Hkv,
                 causal=bool(causal), window=int(window),
                 delta=float(delta), T2=tau_threshold(tau),
-                q8=q8, k8=k8, sq=sq, sk=sk,
-                q16=bf16_bits_to_f64(q_bits), k16=bf16_bits_to_f64(k_bits),
-                v=bf16_bits_to_f64(v_bits))
+                q8=PerHead(e4m3_slab(q_bits, iq)), k8=PerHead(e4m3_slab(k_bits, ik)), sq=sq, sk=sk,
+                q16=PerHead(bf16_slab(q_bits)), k16=PerHead(bf16_slab(k_bits)),
+                v=PerHead(bf16_slab(v_bits)))
 
 
 def all_units(B, Hq, S):
