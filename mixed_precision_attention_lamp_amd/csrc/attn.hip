@@ -1,4 +1,5 @@
-// Fused LampAttention forward kernel for gfx950 (MI355X).
+// Fused LampAttention forward kernel for gfx950 (MI355X), head dimensions 64
+// and 128 (D = 256: attn_deferred.hip).
 //
 // Method: "LampAttention: Look-Ahead Mixed-Precision FlashAttention for
 // Dedicated Accelerators" (abstract).  Per 64x64 tile of (query rows, keys):
@@ -18,11 +19,11 @@
 //      tables 1-6).
 //
 // Schedule: the loop over KV tiles is software-pipelined.  In the iteration of
-// tile t a wave issues the P.V products of tile t-1 on the matrix cores in the
-// same straight-line block as the vector work of tile t (max, exponentials,
-// 8-bit rounding), so that the two overlap; after the sub-block test and the
-// 16-bit recompute of tile t it issues the Q.K^T products of tile t+1, which
-// run under the rescale, the LDS stores and the barrier.  Tiles are staged through registers into unpadded LDS
+// tile t a wave first issues the P.V products of tile t-1, which run on the
+// matrix cores under the vector work of tile t (max, exponentials, 8-bit
+// rounding); after the sub-block test and the 16-bit recompute of tile t it
+// issues the Q.K^T products of tile t+1, which run under the rescale, the LDS
+// stores and the barrier.  Tiles are staged through registers into unpadded LDS
 // layouts whose 16-byte chunks are XOR-swizzled by row (conflict-free operand
 // reads); K8 runs two tiles ahead of the vector work (two LDS slots), K16 one
 // and V^T zero (one slot each).  Q8 and Q16 rows stay in each wave's LDS.
@@ -43,6 +44,7 @@
 
 #include "common.hpp"
 #include "kernels.hpp"
+#include "tiles.hpp"
 
 namespace lamp {
 
@@ -98,71 +100,6 @@ struct Cfg {
     static constexpr int kDB = D / 16;        // 16-wide output column blocks
     static constexpr int kDC = D / 32;        // 32-deep bf16 matrix-core steps
 };
-
-// XOR swizzle of the 16-byte chunks of a staged row (NC chunks per row): the
-// 16 lanes of a lane group read 16 consecutive rows at one logical chunk and
-// hit distinct LDS banks.
-template <int NC>
-__device__ __forceinline__ int swz(int row) {
-    if constexpr (NC >= 16) return row & 15;
-    else if constexpr (NC == 8) return (row ^ (row >> 3)) & 7;
-    else return ((row >> 1) ^ (row >> 2)) & 3;
-}
-
-// Byte offset of logical chunk `chunk` of row `row` in a staged tile.
-template <int RowBytes>
-__device__ __forceinline__ int lds_off(int row, int chunk) {
-    return row * RowBytes + ((chunk ^ swz<RowBytes / 16>(row)) << 4);
-}
-
-__device__ __forceinline__ int tile_lo(int r, int window) {
-    if (window <= 0) return 0;
-    const int j = r * kTileRows - window + 1;
-    return j <= 0 ? 0 : j / kTileKeys;
-}
-
-__device__ __forceinline__ int tile_hi(int r, int nT, int causal) {
-    return causal ? min(r, nT - 1) : nT - 1;
-}
-
-__device__ __forceinline__ bool tile_visited(int r, int t, int S, int causal, int window) {
-    const int i0 = r * kTileRows, i1 = min(i0 + kTileRows - 1, S - 1);
-    const int j0 = t * kTileKeys, j1 = min(j0 + kTileKeys - 1, S - 1);
-    if (causal && i1 < j0) return false;
-    if (window > 0 && i0 - j1 > window - 1) return false;
-    return true;
-}
-
-// Every (query, key) pair of the tile exists and is visible.
-__device__ __forceinline__ bool tile_full(int r, int t, int S, int causal, int window) {
-    const int i0 = r * kTileRows, i1 = i0 + kTileRows - 1;
-    const int j0 = t * kTileKeys, j1 = j0 + kTileKeys - 1;
-    if (i1 >= S || j1 >= S) return false;
-    if (causal && j1 > i0) return false;
-    if (window > 0 && i1 - j0 > window - 1) return false;
-    return true;
-}
-
-__device__ __forceinline__ bool pair_visible(int i, int j, int S, int causal, int window) {
-    return i < S && j < S && (!causal || j <= i) && (window <= 0 || i - j < window);
-}
-
-// Smallest fp32 a >= 0 with fl32(a * c8) >= t2: then |s| >= t2 for the
-// log2-domain logit s = fl32(acc * c8) exactly when |acc| >= a (rounding is
-// monotone).  0 when every logit passes, +inf when none can.
-__device__ float acc_threshold(float t2, float c8) {
-    if (!(t2 > 0.0f)) return 0.0f;
-    if (t2 == __builtin_inff()) return __builtin_inff();
-    float a = t2 / c8;
-    if (!(a < __builtin_inff())) return __builtin_inff();
-    // positive finite floats step by one ulp with their bit pattern
-    for (int it = 0; it < 8 && a > 0.0f; ++it) {
-        const float p = __uint_as_float(__float_as_uint(a) - 1u);
-        if (p * c8 >= t2) a = p; else break;
-    }
-    for (int it = 0; it < 8 && !(a * c8 >= t2); ++it) a = __uint_as_float(__float_as_uint(a) + 1u);
-    return a;
-}
 
 // kMode: 0 = no test (second stage off), 1 = both stages, 2 = second stage only.
 template <int D, bool kDump, int kMode>
@@ -570,17 +507,13 @@ __global__ __launch_bounds__(kThreads, 1) void lamp_attn_kernel(AttnArgs a) {
         if (t > t_begin) store_k16();
         const bool w_prev = work(t - 1), w_cur = work(t), w_next = work(t + 1);
         const bool full = tile_full(r, t, a.S, a.causal, a.window);
-        // P.V of tile t-1 (reads P before the exponentials of tile t overwrite
-        // it) interleaved with the vector work of tile t, in one block
-        if (w_prev && w_cur && full) {
-            pv(P, t - 1);
-            softmax(S, P, t, std::integral_constant<bool, false>{});
-        } else {
-            if (w_prev) pv(P, t - 1);
-            if (w_cur) {
-                if (full) softmax(S, P, t, std::integral_constant<bool, false>{});
-                else softmax(S, P, t, std::integral_constant<bool, true>{});
-            }
+        // P.V of tile t-1 is issued first (it reads P before the exponentials
+        // of tile t overwrite it) and runs on the matrix cores under the
+        // vector work of tile t
+        if (w_prev) pv(P, t - 1);
+        if (w_cur) {
+            if (full) softmax(S, P, t, std::integral_constant<bool, false>{});
+            else softmax(S, P, t, std::integral_constant<bool, true>{});
         }
         // loads for later tiles, stored to LDS before the barrier that ends this
         // iteration
@@ -686,6 +619,7 @@ hipError_t launch_d(const Shape& sh, const AttnParams& p, hipStream_t st) {
 hipError_t launch_attention(const Shape& sh, const AttnParams& p, hipStream_t st) {
     if (sh.D == 64) return launch_d<64>(sh, p, st);
     if (sh.D == 128) return launch_d<128>(sh, p, st);
+    if (sh.D == 256) return launch_attention_deferred(sh, p, st);
     return hipErrorInvalidValue;
 }
 

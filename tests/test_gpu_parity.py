@@ -131,6 +131,10 @@ SMALL = [
     (1, 2, 1, 65, 128, 1, 0, 2 ** -8, 2 ** -1, "sinks", 46),        # one full + one 1-row block
     (1, 1, 1, 1, 64, 1, 0, 2 ** -8, 2 ** -1, "plain", 47),          # S = 1
     (1, 4, 1, 500, 128, 1, 0, 2 ** -8, 2 ** -5, "channels+drift", 48),
+    (1, 2, 1, 200, 256, 1, 0, 2 ** -8, 2 ** -1, "channels", 51),    # D = 256, G = 2
+    (1, 3, 3, 290, 256, 1, 100, 2 ** -4, 2 ** -2, "channels", 52),  # D = 256, window, G = 1
+    (1, 2, 2, 70, 256, 0, 0, 0.0, 0.0, "channels", 53),             # D = 256, all 16-bit
+    (1, 4, 4, 129, 256, 1, 0, 0.0, 2 ** -3, "sinks", 54),           # D = 256, first stage off
 ]
 
 
@@ -160,7 +164,7 @@ def test_forward_parity_endpoints(ends):
 # per-entry dumps: 8-bit accumulators and the weights that enter P.V
 # --------------------------------------------------------------------------
 DUMP = [SMALL[0], SMALL[1], SMALL[5], (1, 3, 3, 130, 64, 0, 0, 0.0, 2 ** -2, "channels", 49),
-        (1, 2, 1, 260, 128, 1, 0, 0.0, 0.0, "channels", 50)]
+        (1, 2, 1, 260, 128, 1, 0, 0.0, 0.0, "channels", 50), SMALL[11]]
 
 
 @pytest.mark.parametrize("case", DUMP)
@@ -226,11 +230,27 @@ def _sample_units(B, Hq, S, n, seed):
     return sorted(units)
 
 
-def test_forward_parity_qwen3_8b_full_size():
-    q, k, v, cfg = make_config_inputs("qwen3-8b")
-    units = _sample_units(cfg["B"], cfg["Hq"], cfg["S"], 12, 7)
-    rep = compare(q, k, v, cfg["causal"], cfg["window"], 2 ** -8, 2 ** -1, units=units,
-                  label="qwen3-8b sampled")
+FULL = [
+    # workload, delta, tau, sampled units
+    ("qwen3-8b", 2 ** -8, 2 ** -1, 12),
+    ("qwen3-32b", 2 ** -8, 2 ** -5, 8),
+    ("gemma3-12b", 2 ** -4, 2 ** -1, 8),
+    ("gemma3-12b-w1024", 2 ** -8, 2 ** -1, 8),
+    ("qwen3-30b-a3b", 2 ** -8, 2 ** -1, 6),
+]
+
+
+@pytest.mark.parametrize("full", FULL, ids=[f[0] for f in FULL])
+def test_forward_parity_full_size(full):
+    """Each full-size workload in the launch configuration the bench times
+    (one call over every head and row block); the oracle checks sampled
+    (batch, head, 64-row block) units, always including the first and last
+    row blocks."""
+    name, delta, tau, n = full
+    q, k, v, cfg = make_config_inputs(name)
+    units = _sample_units(cfg["B"], cfg["Hq"], cfg["S"], n, 7)
+    rep = compare(q, k, v, cfg["causal"], cfg["window"], delta, tau, units=units,
+                  label=f"{name} sampled")
     assert_parity(rep)
 
 
