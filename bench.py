@@ -2,6 +2,7 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload qwen3-8b]
                     [--delta D] [--tau T] [--no-cpu-baseline]
+    python bench.py --copy-calibrate      # plain 1 GiB device copy (counter calibration)
 
 A step is one lamp_attn_fwd call (quantisation pass, V transpose and the fused
 attention kernel) over one batch of seeded synthetic input already resident
@@ -11,6 +12,7 @@ stream it is launched on), the recompute statistics and the CPU oracle timed
 on a bounded sample of the same workload.
 """
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -25,6 +27,38 @@ METRIC = "attn fwd TFLOP/s + % blended FP8/bf16 roofline; 16-bit sub-block fract
 PEAK_FP8 = 5.0e15          # MI355X dense FP8 matrix FLOP/s
 PEAK_BF16 = 2.5e15         # MI355X dense bf16 matrix FLOP/s
 PEAK_HBM = 8.0e12          # MI355X HBM3E bytes/s
+COPY_BYTES = 1 << 30       # size of the calibration copy
+
+# HBM traffic of the attention kernel on the qwen3-8b workload from two
+# rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE; KiB per dispatch), each scaled
+# by the same counter's reading for a plain copy of COPY_BYTES (see
+# profiles/attn_qwen3_8b_hbm_traffic.md).  Valid only for the kernel source
+# whose hash is recorded; any change to it makes the figure null.
+TRAFFIC = {"kernel_hash": "ddfa76df4c69c5e3", "workload": "qwen3-8b", "delta": 2.0 ** -8, "tau": 2.0 ** -1,
+           "bytes_per_launch": 147463219.0}
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "mixed_precision_attention_lamp_amd", "csrc")
+    for name in ("attn.hip", "tiles.hpp", "common.hpp"):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def copy_calibrate():
+    """A plain device-to-device copy of COPY_BYTES, five times (for counter
+    calibration: the copy reads and writes exactly COPY_BYTES each time)."""
+    import torch
+    a = torch.empty(COPY_BYTES, dtype=torch.uint8, device="cuda:0")
+    b = torch.empty_like(a)
+    a.fill_(1)
+    torch.cuda.synchronize()
+    for _ in range(5):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": COPY_BYTES, "copies": 5}), flush=True)
 
 
 def visible_pairs_per_head(S, causal, window):
@@ -98,11 +132,15 @@ def main():
     ap.add_argument("--tau", type=float, default=2.0 ** -1)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--copy-calibrate", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
               "the path is single-GPU by design", file=sys.stderr)
         sys.exit(2)
+    if args.copy_calibrate:
+        copy_calibrate()
+        return
 
     from inputs import make_config_inputs
 
@@ -167,6 +205,11 @@ def main():
     quant_bytes = 3.0 * (nq + nk)
     t_roof = t_mfma + quant_bytes / PEAK_HBM
     achieved = f_alg / (attn_ms_avg * 1e-3)
+    traffic = None
+    if (TRAFFIC is not None and TRAFFIC["kernel_hash"] == kernel_source_hash()
+            and TRAFFIC["workload"] == args.workload and TRAFFIC["delta"] == args.delta
+            and TRAFFIC["tau"] == args.tau):
+        traffic = TRAFFIC["bytes_per_launch"]
     res = {
         "metric": METRIC,
         "value": f_nom / (ms_per_step * 1e-3) / 1e12,
@@ -184,7 +227,7 @@ def main():
                    "S": S, "D": D, "causal": causal, "window": window,
                    "delta": args.delta, "tau": args.tau},
         "roofline": {"bound": "mfma", "achieved": achieved / 1e12, "peak": blended_peak / 1e12,
-                     "unit": "TFLOP/s", "frac": achieved / blended_peak, "traffic": None},
+                     "unit": "TFLOP/s", "frac": achieved / blended_peak, "traffic": traffic},
         "blended_roofline_frac": t_roof / (ms_per_step * 1e-3),
         "kernel_ms": {"attention": attn_ms_avg, "quantise_and_transpose": prep_ms_avg},
         "recompute": {"r_sb": stats["r_sb"], "r_e": stats["r_e"], "hist_0_to_4": stats["hist"],
