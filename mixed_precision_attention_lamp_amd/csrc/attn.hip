@@ -94,8 +94,7 @@ struct Cfg {
     static constexpr int kK8Off = 0;                            // two slots
     static constexpr int kK16Off = 2 * kK8Bytes;                // one slot
     static constexpr int kVtOff = kK16Off + kK16Bytes;          // one slot
-    static constexpr int kQ16Off = kVtOff + kVtBytes;
-    static constexpr int kQ8Off = kQ16Off + kWaves * kQ16Bytes;
+    static constexpr int kQ8Off = kVtOff + kVtBytes;
     static constexpr int kLdsBytes = kQ8Off + kWaves * kQ8Bytes;
     static constexpr int kDB = D / 16;        // 16-wide output column blocks
     static constexpr int kDC = D / 32;        // 32-deep bf16 matrix-core steps
@@ -138,7 +137,6 @@ __global__ __launch_bounds__(kThreads, 1) void lamp_attn_kernel(AttnArgs a) {
     const size_t kv_head = (size_t)b * a.Hkv + hk;
     const size_t q_head = (size_t)b * a.Hq + hq;
 
-    uint8_t* q16_lds = lds + C::kQ16Off + wave * C::kQ16Bytes;
     uint8_t* q8_lds = lds + C::kQ8Off + wave * C::kQ8Bytes;
 
     // ---- staging: register loads at the start of an iteration, LDS stores at its end
@@ -202,20 +200,16 @@ __global__ __launch_bounds__(kThreads, 1) void lamp_attn_kernel(AttnArgs a) {
         for (int i = 0; i < kVtCh; ++i) *reinterpret_cast<u32x4*>(base + (tid + i * kThreads) * 16) = st_vt[i];
     };
 
-    // ---- prologue: this wave's Q16 and Q8 rows into its LDS -----------------------
+    // ---- prologue: this wave's Q16 operand into registers, Q8 rows into its LDS ----
     float m_run[kQG], c8 = 0.0f, inv_c8 = 0.0f, a2 = 0.0f;
     const float c16 = (float)a.l_d;
-    {
-        constexpr int kNC = C::kK16Row / 16;
-        const int qmax = a.S - 1;
+    v8bf qb[C::kDC][kQG];     // bf16 operand of 16-query group qg, 32-deep step ch
 #pragma unroll
-        for (int i = 0; i < C::kQ16Bytes / 1024; ++i) {
-            const int p = i * 1024 + lane * 16;
-            const int row = p / C::kK16Row, slot = (p % C::kK16Row) >> 4;
-            const int gq = min(row0 + row, qmax);    // rows past the end are never written out
-            *reinterpret_cast<u32x4*>(q16_lds + p) = *reinterpret_cast<const u32x4*>(
-                reinterpret_cast<const uint8_t*>(a.q16 + (q_head * a.S + gq) * D) + ((slot ^ swz<kNC>(row)) << 4));
-        }
+    for (int qg = 0; qg < kQG; ++qg) {
+        // rows past the end are never written out
+        const uint16_t* qrow = a.q16 + (q_head * a.S + min(row0 + qg * 16 + n16, a.S - 1)) * D;
+#pragma unroll
+        for (int ch = 0; ch < C::kDC; ++ch) qb[ch][qg] = *reinterpret_cast<const v8bf*>(qrow + ch * 32 + g * 8);
     }
     {
         constexpr int kNC = C::kK8Row / 16;
@@ -465,9 +459,8 @@ __global__ __launch_bounds__(kThreads, 1) void lamp_attn_kernel(AttnArgs a) {
                 const v8bf ka = *reinterpret_cast<const v8bf*>(k16l + lds_off<C::kK16Row>(c * 16 + n16, ch * 4 + g));
 #pragma unroll
                 for (int qg = 0; qg < kQG; ++qg) {
-                    const v8bf qb = *reinterpret_cast<const v8bf*>(q16_lds + lds_off<C::kK16Row>(qg * 16 + n16, ch * 4 + g));
                     acc16[qg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                        ka, qb, ch == 0 ? v4f{0.f, 0.f, 0.f, 0.f} : acc16[qg], 0, 0, 0);
+                        ka, qb[ch][qg], ch == 0 ? v4f{0.f, 0.f, 0.f, 0.f} : acc16[qg], 0, 0, 0);
                 }
             }
 #pragma unroll

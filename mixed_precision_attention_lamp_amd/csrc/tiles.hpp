@@ -10,12 +10,14 @@
 namespace lamp {
 
 // XOR swizzle of the 16-byte chunks of a staged row (NC chunks per row): the
-// 16 lanes of a lane group read 16 consecutive rows at one logical chunk and
-// hit distinct LDS banks.
+// lanes of a lane group read consecutive rows at one logical chunk, and every
+// 8 (NC = 8, 16) or 4 (NC = 4) consecutive rows of that read hit distinct LDS
+// banks.  The swizzle depends on the row modulo 16 only, so operand rows
+// 16 apart share one address register plus an immediate offset.
 template <int NC>
 __device__ __forceinline__ int swz(int row) {
     if constexpr (NC >= 16) return row & 15;
-    else if constexpr (NC == 8) return (row ^ (row >> 3)) & 7;
+    else if constexpr (NC == 8) return row & 7;
     else return ((row >> 1) ^ (row >> 2)) & 3;
 }
 
