@@ -62,6 +62,7 @@ struct AttnArgs {
     const uint16_t* k16;
     const uint16_t* vt;
     const float* q_scale;
+    const float* q_inv;
     const float* k_scale;
     float* out;
     uint8_t* mask;
@@ -212,15 +213,32 @@ __global__ __launch_bounds__(kThreads, 1) void lamp_attn_kernel(AttnArgs a) {
         for (int ch = 0; ch < C::kDC; ++ch) qb[ch][qg] = *reinterpret_cast<const v8bf*>(qrow + ch * 32 + g * 8);
     }
     {
+        // Q8 = E4M3(fl32(q * inv)) for this wave's rows, the arithmetic of the
+        // quantisation pass; rows past the end are zero
         constexpr int kNC = C::kK8Row / 16;
-        const int qmax = a.S_pad - 1;
+        const float inv = active ? a.q_inv[q_head] : 1.0f;
 #pragma unroll
         for (int i = 0; i < C::kQ8Bytes / 1024; ++i) {
             const int p = i * 1024 + lane * 16;
             const int row = p / C::kK8Row, slot = (p % C::kK8Row) >> 4;
-            const int gq = min(row0 + row, qmax);
-            *reinterpret_cast<u32x4*>(q8_lds + p) = *reinterpret_cast<const u32x4*>(
-                a.q8 + (q_head * a.S_pad + gq) * D + ((slot ^ swz<kNC>(row)) << 4));
+            const int gq = row0 + row;
+            u32x4 o = {0u, 0u, 0u, 0u};
+            if (gq < a.S) {
+                const uint16_t* src = a.q16 + (q_head * a.S + gq) * D + ((slot ^ swz<kNC>(row)) << 4);
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const u32x4 w = *reinterpret_cast<const u32x4*>(src + 8 * h);
+                    float x[8];
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        x[2 * j] = bf16_bits_to_float(w[j] & 0xFFFFu) * inv;
+                        x[2 * j + 1] = bf16_bits_to_float(w[j] >> 16) * inv;
+                    }
+                    o[2 * h] = cvt_pk_e4m3<true>(x[2], x[3], cvt_pk_e4m3<false>(x[0], x[1], 0u));
+                    o[2 * h + 1] = cvt_pk_e4m3<true>(x[6], x[7], cvt_pk_e4m3<false>(x[4], x[5], 0u));
+                }
+            }
+            *reinterpret_cast<u32x4*>(q8_lds + p) = o;
         }
     }
 #pragma unroll
@@ -581,7 +599,7 @@ template <int D>
 hipError_t launch_d(const Shape& sh, const AttnParams& p, hipStream_t st) {
     AttnArgs a;
     a.q8 = p.q8; a.k8 = p.k8; a.q16 = p.q16; a.k16 = p.k16; a.vt = p.vt;
-    a.q_scale = p.q_scale; a.k_scale = p.k_scale; a.out = p.out; a.mask = p.mask;
+    a.q_scale = p.q_scale; a.q_inv = p.q_inv; a.k_scale = p.k_scale; a.out = p.out; a.mask = p.mask;
     a.dump_s = p.dump_s; a.dump_p = p.dump_p;
     a.l_d = p.log2e_over_sqrt_d; a.t2 = p.t2;
     a.x_delta = p.e_delta > 0.0f ? (float)std::log2((double)p.e_delta) : -__builtin_inff();

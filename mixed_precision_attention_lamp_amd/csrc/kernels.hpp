@@ -19,10 +19,11 @@ int amax_chunks(int S, int D);
 
 // Quantisation pass (Q and K): per-(batch, head) amax partial maxima, then
 // scales and e4m3 codes.  q8 / k8 are written with `rows_out` rows per head
-// (rows >= S are zero).  partial must hold (B*Hq + B*Hkv) * amax_chunks(S, D)
-// uint32 values.
+// (rows >= S are zero).  With q8 null, Q gets only its scales and inverse
+// scales (q_inv, nullable otherwise).  partial must hold
+// (B*Hq + B*Hkv) * amax_chunks(S, D) uint32 values.
 hipError_t launch_quantize(const Shape& sh, const uint16_t* q, const uint16_t* k,
-                           uint32_t* partial, float* q_scale, float* k_scale,
+                           uint32_t* partial, float* q_scale, float* k_scale, float* q_inv,
                            uint8_t* q8, uint8_t* k8, int rows_out, hipStream_t st);
 
 // V [B, Hkv, S, D] -> vt [B, Hkv, nT, D, 64] (keys of each tile transposed and
@@ -33,13 +34,14 @@ hipError_t launch_transpose_v(const Shape& sh, const uint16_t* v, uint16_t* vt, 
                               hipStream_t st);
 
 struct AttnParams {
-    const uint8_t* q8;      // [B, Hq, S_pad, D] e4m3 codes
+    const uint8_t* q8;      // [B, Hq, S_pad, D] e4m3 codes (D = 256; the D <= 128 kernel quantises Q itself)
     const uint8_t* k8;      // [B, Hkv, S_pad, D]
     const uint16_t* q16;    // [B, Hq, S, D] bf16 (caller's Q)
     const uint16_t* k16;    // [B, Hkv, S, D] bf16 (caller's K)
     const uint16_t* vt;     // [B, Hkv, nT, D, 64] bf16
     const uint16_t* vsb;    // D = 256: [B, Hkv, nT, 4, D, 16] bf16
     const float* q_scale;   // [B * Hq]
+    const float* q_inv;     // [B * Hq] inverse scales, as the quantisation pass uses them
     const float* k_scale;   // [B * Hkv]
     float* out;             // [B, Hq, S, D]
     uint8_t* mask;          // [B, Hq, nT, nT] or null

@@ -136,7 +136,7 @@ float exponential_threshold(float delta) {
 }
 
 struct Layout {
-    size_t partial, q_scale, k_scale, q8, k8, vt, vsb, rec_m, total;
+    size_t partial, q_scale, k_scale, q_inv, q8, k8, vt, vsb, rec_m, total;
 };
 
 Layout workspace_layout(const lamp::Shape& sh, int causal, int window) {
@@ -146,6 +146,7 @@ Layout workspace_layout(const lamp::Shape& sh, int causal, int window) {
     const size_t nslab = (size_t)sh.B * (sh.Hq + sh.Hkv);
     L.partial = take(nslab * lamp::amax_chunks(sh.S, sh.D) * sizeof(uint32_t));
     L.q_scale = take((size_t)sh.B * sh.Hq * sizeof(float));
+    L.q_inv = take((size_t)sh.B * sh.Hq * sizeof(float));
     L.k_scale = take((size_t)sh.B * sh.Hkv * sizeof(float));
     L.q8 = take((size_t)sh.B * sh.Hq * sh.S_pad * sh.D);
     L.k8 = take((size_t)sh.B * sh.Hkv * sh.S_pad * sh.D);
@@ -202,7 +203,10 @@ static int attn_fwd_impl(const void* q, const void* k, const void* v, float* out
         if (ev) ++g_n_timed;
     }
     if (ev) (void)hipEventRecord(ev[0], g_stream);
-    hipError_t e = lamp::launch_quantize(sh, q16, k16, partial, q_scale, k_scale, q8, k8, sh.S_pad, g_stream);
+    auto* q_inv = reinterpret_cast<float*>(base + L.q_inv);
+    // the D <= 128 attention kernel quantises its Q rows itself
+    hipError_t e = lamp::launch_quantize(sh, q16, k16, partial, q_scale, k_scale, q_inv,
+                                         sh.D == 256 ? q8 : nullptr, k8, sh.S_pad, g_stream);
     if (e != hipSuccess) return hip_fail(e, "quantise launch");
     e = lamp::launch_transpose_v(sh, v16, vt, vsb, g_stream);
     if (e != hipSuccess) return hip_fail(e, "transpose launch");
@@ -210,7 +214,7 @@ static int attn_fwd_impl(const void* q, const void* k, const void* v, float* out
 
     lamp::AttnParams p;
     p.q8 = q8; p.k8 = k8; p.q16 = q16; p.k16 = k16; p.vt = vt; p.vsb = vsb;
-    p.q_scale = q_scale; p.k_scale = k_scale;
+    p.q_scale = q_scale; p.k_scale = k_scale; p.q_inv = q_inv;
     p.out = out; p.mask = subblock_mask_out;
     p.rec_m = rec_m;
     p.log2e_over_sqrt_d = kLog2e / std::sqrt((double)D);
@@ -297,7 +301,7 @@ int lamp_quantize_qk(const void* q, const void* k, int B, int Hq, int Hkv, int S
     if (rc != LAMP_OK) return rc;
     auto* partial = reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(ws) + L.partial);
     hipError_t e = lamp::launch_quantize(sh, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
-                                         partial, q_scale, k_scale, q8, k8, S, g_stream);
+                                         partial, q_scale, k_scale, nullptr, q8, k8, S, g_stream);
     if (e != hipSuccess) return hip_fail(e, "quantise launch");
     return LAMP_OK;
 }

@@ -62,15 +62,18 @@ __global__ __launch_bounds__(kThreads) void amax_kernel(const uint16_t* __restri
 }
 
 // blockIdx.y = slab, blockIdx.x = output chunk.  Output slabs have rows_out
-// rows of D codes; rows >= S are written as zero.
+// rows of D codes; rows >= S are written as zero.  With q8 null the Q slabs
+// only get their scale and inverse scale (the attention kernel quantises Q
+// rows itself, with the same arithmetic).
 __global__ __launch_bounds__(kThreads) void quantize_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint32_t* __restrict__ partial, float* __restrict__ q_scale, float* __restrict__ k_scale,
-    uint8_t* __restrict__ q8, uint8_t* __restrict__ k8, int n_q_slabs, int S, int D, int nch,
-    int rows_out) {
+    float* __restrict__ q_inv, uint8_t* __restrict__ q8, uint8_t* __restrict__ k8, int n_q_slabs,
+    int S, int D, int nch, int rows_out) {
     __shared__ uint32_t red[kThreads / 64];
     const int slab = blockIdx.y;
     const bool is_q = slab < n_q_slabs;
+    if (is_q && q8 == nullptr && blockIdx.x != 0) return;
     const int hs = is_q ? slab : slab - n_q_slabs;
     const uint16_t* src = (is_q ? q : k) + (size_t)hs * S * D;
     uint8_t* dst = (is_q ? q8 : k8) + (size_t)hs * rows_out * D;
@@ -85,7 +88,11 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(
         scale = (float)((double)amax / 448.0);
         inv = (float)(448.0 / (double)amax);
     }
-    if (blockIdx.x == 0 && threadIdx.x == 0) (is_q ? q_scale : k_scale)[hs] = scale;
+    if (blockIdx.x == 0 && threadIdx.x == 0) {
+        (is_q ? q_scale : k_scale)[hs] = scale;
+        if (is_q && q_inv) q_inv[hs] = inv;
+    }
+    if (is_q && q8 == nullptr) return;
 
     const int in_len = S * D;
     const int out_len = rows_out * D;
@@ -187,8 +194,8 @@ __global__ void debug_convert_kernel(const float* __restrict__ x, int64_t n, uin
 int amax_chunks(int S, int D) { return (S * D + kChunk - 1) / kChunk; }
 
 hipError_t launch_quantize(const Shape& sh, const uint16_t* q, const uint16_t* k,
-                           uint32_t* partial, float* q_scale, float* k_scale, uint8_t* q8,
-                           uint8_t* k8, int rows_out, hipStream_t st) {
+                           uint32_t* partial, float* q_scale, float* k_scale, float* q_inv,
+                           uint8_t* q8, uint8_t* k8, int rows_out, hipStream_t st) {
     const int nq = sh.B * sh.Hq, nk = sh.B * sh.Hkv;
     const int nch = amax_chunks(sh.S, sh.D);
     hipLaunchKernelGGL(amax_kernel, dim3(nch, nq + nk), dim3(kThreads), 0, st, q, k, partial, nq,
@@ -197,7 +204,7 @@ hipError_t launch_quantize(const Shape& sh, const uint16_t* q, const uint16_t* k
     if (e != hipSuccess) return e;
     const int nch_out = (rows_out * sh.D + kChunk - 1) / kChunk;
     hipLaunchKernelGGL(quantize_kernel, dim3(nch_out, nq + nk), dim3(kThreads), 0, st, q, k,
-                       partial, q_scale, k_scale, q8, k8, nq, sh.S, sh.D, nch, rows_out);
+                       partial, q_scale, k_scale, q_inv, q8, k8, nq, sh.S, sh.D, nch, rows_out);
     return hipGetLastError();
 }
 
