@@ -28,10 +28,8 @@
  *   - Arguments are validated before any HIP call; on a validation error
  *     nothing is launched and nothing is written.  The return value is LAMP_OK
  *     or a negative error code; lamp_last_error() gives a message.
- *   - The library owns one device workspace per device (Q8, K8, a transposed
- *     copy of V, scales; for D = 256 also a per-sub-block copy of V and the row
- *     maxima of flagged tiles, up to B*Hq*S*ceil(S/64)*4 bytes); it only grows,
- *     and lamp_release_workspace() frees it.
+ *   - The library owns one device workspace per device (K8, a transposed copy
+ *     of V, scales); it only grows, and lamp_release_workspace() frees it.
  *   - Inputs must be finite.  Not thread-safe for concurrent calls sharing a
  *     device; the stream and the last error are per host thread.
  */
@@ -65,8 +63,7 @@ enum {
  *             Byte (b, hq, r, t): bit 7 = tile (query rows 64r.., keys 64t..) visited,
  *             bit c (0..3) = sub-block c (keys 64t+16c .. 64t+16c+15) recomputed in
  *             16-bit; 0 for tiles that hold no visible entry.
- * Sizes: B, Hq, Hkv, S >= 1; Hq % Hkv == 0; D in {64, 128, 256};
- * S <= 262144 (4096 tiles); B*Hq*S*D < 2^31. */
+ * Sizes: B, Hq, Hkv, S >= 1; Hq % Hkv == 0; D in {64, 128, 256}; B*Hq*S*D < 2^31. */
 int lamp_attn_fwd(const void* q, const void* k, const void* v, float* out,
                   int B, int Hq, int Hkv, int S, int D,
                   int causal, int window, float delta, float tau,

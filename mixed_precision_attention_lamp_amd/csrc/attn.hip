@@ -1,5 +1,5 @@
-// Fused LampAttention forward kernel for gfx950 (MI355X), head dimensions 64
-// and 128 (D = 256: attn_deferred.hip).
+// Fused LampAttention forward kernel for gfx950 (MI355X), head dimensions 64,
+// 128 and 256.
 //
 // Method: "LampAttention: Look-Ahead Mixed-Precision FlashAttention for
 // Dedicated Accelerators" (abstract).  Per 64x64 tile of (query rows, keys):
@@ -26,18 +26,21 @@
 // stores and the barrier.  Tiles are staged through registers into unpadded LDS
 // layouts whose 16-byte chunks are XOR-swizzled by row (conflict-free operand
 // reads); K8 runs two tiles ahead of the vector work (two LDS slots), K16 one
-// and V^T zero (one slot each).  Q8 and Q16 rows stay in each wave's LDS.
+// and V^T zero (one slot each, ordered by the two barriers of a tile).  Each
+// wave quantises its Q rows into LDS in the prologue (the arithmetic of the
+// quantisation pass) and keeps its Q16 operand in registers.
 //
 // Work decomposition: a workgroup of eight waves shares staged K/V tiles.  A
-// pair of waves owns one 64-row query block of one query head (32 rows each,
-// so that the fp32 output accumulator stays in architectural registers, where
-// the per-row rescale is one multiply); the pair ORs its 4-bit sub-block flags
-// through LDS.  The four pairs are four query heads of one GQA group (or fewer
-// heads and consecutive row blocks when the group is smaller), so one staged
-// K/V tile serves all of them.  Logits are held transposed (keys in rows,
-// queries in columns): lane l keeps query l % 16 of each 16-query group, which
-// makes the row max a register reduction plus two cross-lane steps and lets
-// the exponentials feed the P.V operand in place.
+// wave owns 32 query rows (16 for D = 256), so that the fp32 output
+// accumulator stays in architectural registers, where the per-row rescale is
+// one multiply; the 2 (4) waves of one 64-row query block of one query head
+// OR their 4-bit sub-block flags through LDS.  The 4 (2) blocks of a workgroup
+// are query heads of one GQA group (or fewer heads and consecutive row blocks
+// when the group is smaller), so one staged K/V tile serves all of them.
+// Logits are held transposed (keys in rows, queries in columns): lane l keeps
+// query l % 16 of each 16-query group, which makes the row max a register
+// reduction plus two cross-lane steps and lets the exponentials feed the P.V
+// operand in place.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -52,11 +55,8 @@ namespace {
 
 constexpr int kWaves = 8;
 constexpr int kThreads = kWaves * 64;
-constexpr int kWaveRows = 32;            // query rows per wave
-constexpr int kQG = kWaveRows / 16;      // 16-query groups per wave
 
 struct AttnArgs {
-    const uint8_t* q8;
     const uint8_t* k8;
     const uint16_t* q16;
     const uint16_t* k16;
@@ -75,8 +75,8 @@ struct AttnArgs {
     int B, Hq, Hkv, S, nT, S_pad;
     int causal, window;
     int G;               // Hq / Hkv
-    int heads_per_wg;    // 4, 2 or 1
-    int rows_per_wg;     // 4 / heads_per_wg
+    int heads_per_wg;    // kBlocks, ..., 1
+    int rows_per_wg;     // kBlocks / heads_per_wg
     int n_rg;            // row-block groups
     int xcd_remap;       // number of workgroups is a multiple of 8
     int n_wg;
@@ -84,6 +84,13 @@ struct AttnArgs {
 
 template <int D>
 struct Cfg {
+    // a wave owns 32 query rows (16 for D = 256, whose output accumulator is
+    // twice as wide); 2 (or 4) waves form one 64-row block
+    static constexpr int kQG = D == 256 ? 1 : 2;        // 16-query groups per wave
+    static constexpr int kWaveRows = 16 * kQG;
+    static constexpr int kWavesPerBlock = kTileRows / kWaveRows;
+    static constexpr int kBlocks = kWaves / kWavesPerBlock;   // 64-row blocks per workgroup
+    static constexpr int kKS = D >= 128 ? D / 128 : 1;       // 128-deep FP8 matrix-core steps
     static constexpr int kK8Row = D;                   // bytes per staged row
     static constexpr int kK16Row = 2 * D;
     static constexpr int kVtRow = 2 * kTileKeys;
@@ -105,16 +112,18 @@ struct Cfg {
 template <int D, bool kDump, int kMode>
 __global__ __launch_bounds__(kThreads, 1) void lamp_attn_kernel(AttnArgs a) {
     using C = Cfg<D>;
+    constexpr int kQG = C::kQG;
+    constexpr int kWaveRows = C::kWaveRows;
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-    __shared__ uint32_t flag_lds[kWaves];    // 4-bit flag sets exchanged by wave pairs
+    __shared__ uint32_t flag_lds[kWaves];    // 4-bit flag sets exchanged by the waves of a block
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6;
     const int lane = tid & 63;
     const int n16 = lane & 15;     // query column within a 16-query group
     const int g = lane >> 4;       // lane group: which 4 keys / which k-slice
-    const int pair = wave >> 1;    // which (head, 64-row block) of the workgroup
-    const int half = wave & 1;     // rows 32*half .. 32*half+31 of that block
+    const int blk = wave / C::kWavesPerBlock;   // which (head, 64-row block) of the workgroup
+    const int wib = wave % C::kWavesPerBlock;   // rows wib*kWaveRows .. of that block
 
     // ---- workgroup -> (batch, kv head, head group, row-block group) ----------
     int wg = blockIdx.x;
@@ -126,14 +135,14 @@ __global__ __launch_bounds__(kThreads, 1) void lamp_attn_kernel(AttnArgs a) {
     u /= n_hg;
     const int hk = u % a.Hkv;
     const int b = u / a.Hkv;
-    const int hq = hk * a.G + hg * a.heads_per_wg + (pair % a.heads_per_wg);
-    const int r = rg * a.rows_per_wg + pair / a.heads_per_wg;
+    const int hq = hk * a.G + hg * a.heads_per_wg + (blk % a.heads_per_wg);
+    const int r = rg * a.rows_per_wg + blk / a.heads_per_wg;
     const bool active = r < a.nT;
     const int r_first = rg * a.rows_per_wg;
     const int r_last = min(r_first + a.rows_per_wg - 1, a.nT - 1);
     const int t_begin = tile_lo(r_first, a.window);
     const int t_end = tile_hi(r_last, a.nT, a.causal);
-    const int row0 = r * kTileRows + half * kWaveRows;   // first query row of this wave
+    const int row0 = r * kTileRows + wib * kWaveRows;   // first query row of this wave
 
     const size_t kv_head = (size_t)b * a.Hkv + hk;
     const size_t q_head = (size_t)b * a.Hq + hq;
@@ -247,7 +256,7 @@ __global__ __launch_bounds__(kThreads, 1) void lamp_attn_kernel(AttnArgs a) {
         c8 = (float)((double)a.q_scale[q_head] * (double)a.k_scale[kv_head] * a.l_d);
         a2 = acc_threshold(a.t2, c8);
         inv_c8 = 1.0f / c8;
-        if (a.mask && half == 0) {
+        if (a.mask && wib == 0) {
             uint8_t* mrow = a.mask + (q_head * a.nT + r) * a.nT;
             for (int t = lane; t < a.nT; t += 64)
                 if (!tile_visited(r, t, a.S, a.causal, a.window)) mrow[t] = 0;
@@ -271,35 +280,19 @@ __global__ __launch_bounds__(kThreads, 1) void lamp_attn_kernel(AttnArgs a) {
     // Q.K^T of tile t: s[qg][kb][i] = 8-bit accumulator of key 16kb + 4g + i, query 16qg + n16
     auto qk = [&](v4f (&s)[kQG][4], int t) __attribute__((always_inline)) {
         const uint8_t* k8l = lds + C::kK8Off + (t & 1) * C::kK8Bytes;
-        v8i qf[kQG];
 #pragma unroll
-        for (int qg = 0; qg < kQG; ++qg) {
-            qf[qg] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
-            const int row = qg * 16 + n16;
-            if (D >= 128 || g * 32 < D) {
-                const int gg = D >= 128 ? g : (g & 1);
-                const u32x4 lo = *reinterpret_cast<const u32x4*>(q8_lds + lds_off<C::kK8Row>(row, 2 * gg));
-                const u32x4 hi = *reinterpret_cast<const u32x4*>(q8_lds + lds_off<C::kK8Row>(row, 2 * gg + 1));
-                qf[qg] = v8i{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
-                             (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+        for (int st = 0; st < C::kKS; ++st) {
+            v8i qf[kQG];
+#pragma unroll
+            for (int qg = 0; qg < kQG; ++qg) qf[qg] = fp8_operand<D>(q8_lds, qg * 16 + n16, st, g);
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb) {
+                const v8i ka = fp8_operand<D>(k8l, kb * 16 + n16, st, g);
+#pragma unroll
+                for (int qg = 0; qg < kQG; ++qg)
+                    s[qg][kb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                        ka, qf[qg], st == 0 ? v4f{0.f, 0.f, 0.f, 0.f} : s[qg][kb], 0, 0, 0, 0, 0, 0);
             }
-        }
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb) {
-            // lane group g holds depth 32g .. 32g+31; for D = 64 groups 2, 3 hold zeros
-            v8i ka = {0, 0, 0, 0, 0, 0, 0, 0};
-            const int row = kb * 16 + n16;
-            if (D >= 128 || g * 32 < D) {
-                const int gg = D >= 128 ? g : (g & 1);
-                const u32x4 lo = *reinterpret_cast<const u32x4*>(k8l + lds_off<C::kK8Row>(row, 2 * gg));
-                const u32x4 hi = *reinterpret_cast<const u32x4*>(k8l + lds_off<C::kK8Row>(row, 2 * gg + 1));
-                ka = v8i{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
-                         (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
-            }
-#pragma unroll
-            for (int qg = 0; qg < kQG; ++qg)
-                s[qg][kb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                    ka, qf[qg], v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
         }
     };
     // P.V of tile t (and the row sums, with an all-ones operand)
@@ -532,10 +525,12 @@ __global__ __launch_bounds__(kThreads, 1) void lamp_attn_kernel(AttnArgs a) {
         if (ld_k16) load_k16(t + 1);
         load_vt(t);
         uint32_t flags = w_cur ? test(S, !full) : 0u;
-        // the two waves of a 64-row block OR their flags
+        // the waves of a 64-row block OR their flags
         if (lane == 0) flag_lds[wave] = flags;
         lds_barrier();
-        flags |= flag_lds[wave ^ 1];
+        flags = 0;
+#pragma unroll
+        for (int w = 0; w < C::kWavesPerBlock; ++w) flags |= flag_lds[blk * C::kWavesPerBlock + w];
         if (w_cur && flags != 0) recompute(P, flags, !full);
         // Q.K^T of tile t+1 runs on the matrix cores under what follows
         if (w_next) qk(S, t + 1);
@@ -566,7 +561,7 @@ __global__ __launch_bounds__(kThreads, 1) void lamp_attn_kernel(AttnArgs a) {
                 }
             }
             // (7) mask byte
-            if (a.mask && half == 0 && lane == 0)
+            if (a.mask && wib == 0 && lane == 0)
                 a.mask[(q_head * a.nT + r) * a.nT + t] = (uint8_t)(0x80u | flags);
         }
         // K8 of tile t+2 into the slot Q.K^T of tile t used; V^T of tile t into
@@ -598,7 +593,7 @@ __global__ __launch_bounds__(kThreads, 1) void lamp_attn_kernel(AttnArgs a) {
 template <int D>
 hipError_t launch_d(const Shape& sh, const AttnParams& p, hipStream_t st) {
     AttnArgs a;
-    a.q8 = p.q8; a.k8 = p.k8; a.q16 = p.q16; a.k16 = p.k16; a.vt = p.vt;
+    a.k8 = p.k8; a.q16 = p.q16; a.k16 = p.k16; a.vt = p.vt;
     a.q_scale = p.q_scale; a.q_inv = p.q_inv; a.k_scale = p.k_scale; a.out = p.out; a.mask = p.mask;
     a.dump_s = p.dump_s; a.dump_p = p.dump_p;
     a.l_d = p.log2e_over_sqrt_d; a.t2 = p.t2;
@@ -607,8 +602,10 @@ hipError_t launch_d(const Shape& sh, const AttnParams& p, hipStream_t st) {
     a.B = sh.B; a.Hq = sh.Hq; a.Hkv = sh.Hkv; a.S = sh.S; a.nT = sh.nT; a.S_pad = sh.S_pad;
     a.causal = p.causal; a.window = p.window;
     a.G = sh.Hq / sh.Hkv;
-    a.heads_per_wg = (a.G % 4 == 0) ? 4 : (a.G % 2 == 0) ? 2 : 1;
-    a.rows_per_wg = 4 / a.heads_per_wg;
+    a.heads_per_wg = 1;
+    for (int h = Cfg<D>::kBlocks; h >= 1; h /= 2)
+        if (a.G % h == 0) { a.heads_per_wg = h; break; }
+    a.rows_per_wg = Cfg<D>::kBlocks / a.heads_per_wg;
     a.n_rg = (sh.nT + a.rows_per_wg - 1) / a.rows_per_wg;
     a.n_wg = sh.B * sh.Hkv * (a.G / a.heads_per_wg) * a.n_rg;
     a.xcd_remap = (a.n_wg % 8 == 0) ? 1 : 0;
@@ -630,7 +627,7 @@ hipError_t launch_d(const Shape& sh, const AttnParams& p, hipStream_t st) {
 hipError_t launch_attention(const Shape& sh, const AttnParams& p, hipStream_t st) {
     if (sh.D == 64) return launch_d<64>(sh, p, st);
     if (sh.D == 128) return launch_d<128>(sh, p, st);
-    if (sh.D == 256) return launch_attention_deferred(sh, p, st);
+    if (sh.D == 256) return launch_d<256>(sh, p, st);
     return hipErrorInvalidValue;
 }
 

@@ -27,25 +27,19 @@ hipError_t launch_quantize(const Shape& sh, const uint16_t* q, const uint16_t* k
                            uint8_t* q8, uint8_t* k8, int rows_out, hipStream_t st);
 
 // V [B, Hkv, S, D] -> vt [B, Hkv, nT, D, 64] (keys of each tile transposed and
-// permuted into the order the P.V matrix-core operand reads; padding keys 0)
-// and, when vsb is non-null, vsb [B, Hkv, nT, 4, D, 16] (per 16-key sub-block,
-// transposed, keys in order).
-hipError_t launch_transpose_v(const Shape& sh, const uint16_t* v, uint16_t* vt, uint16_t* vsb,
-                              hipStream_t st);
+// permuted into the order the P.V matrix-core operand reads; padding keys 0).
+hipError_t launch_transpose_v(const Shape& sh, const uint16_t* v, uint16_t* vt, hipStream_t st);
 
 struct AttnParams {
-    const uint8_t* q8;      // [B, Hq, S_pad, D] e4m3 codes (D = 256; the D <= 128 kernel quantises Q itself)
     const uint8_t* k8;      // [B, Hkv, S_pad, D]
     const uint16_t* q16;    // [B, Hq, S, D] bf16 (caller's Q)
     const uint16_t* k16;    // [B, Hkv, S, D] bf16 (caller's K)
     const uint16_t* vt;     // [B, Hkv, nT, D, 64] bf16
-    const uint16_t* vsb;    // D = 256: [B, Hkv, nT, 4, D, 16] bf16
     const float* q_scale;   // [B * Hq]
     const float* q_inv;     // [B * Hq] inverse scales, as the quantisation pass uses them
     const float* k_scale;   // [B * Hkv]
     float* out;             // [B, Hq, S, D]
     uint8_t* mask;          // [B, Hq, nT, nT] or null
-    float* rec_m;           // D = 256: [B * Hq * rec_slot_base(nT, ...), 64] row maxima of flagged tiles
     float* dump_s = nullptr;     // debug dump of 8-bit accumulators [B, Hq, S, S]
     uint16_t* dump_p = nullptr;  // debug dump of final bf16 weights [B, Hq, S, S]
     double log2e_over_sqrt_d;
@@ -54,24 +48,8 @@ struct AttnParams {
     int causal, window;
 };
 
-// Record slots of the attention kernel: row block r of a (batch, query head)
-// owns slots [rec_slot_base(r), rec_slot_base(r + 1)), one per KV tile it can
-// visit (all nT without a causal mask; r + 1 with one; at most
-// ceil(window / 64) + 1 with a window as well).  Each slot holds the 64 row
-// maxima of one flagged tile.
-__host__ __device__ inline int64_t rec_slot_base(int r, int nT, int causal, int window) {
-    if (!causal) return (int64_t)r * nT;
-    if (window <= 0) return (int64_t)r * (r + 1) / 2;
-    const int64_t w = (window + 63) / 64 + 1;
-    if (r <= w) return (int64_t)r * (r + 1) / 2;
-    return w * (w + 1) / 2 + (int64_t)(r - w) * w;
-}
-
-// The forward attention kernel for D = 64, 128 (16-bit recompute inside the
-// tile loop) and, through launch_attention_deferred, D = 256 (16-bit work as a
-// correction after the loop; needs vsb and rec_m).
+// The forward attention kernel (16-bit recompute inside the tile loop).
 hipError_t launch_attention(const Shape& sh, const AttnParams& p, hipStream_t st);
-hipError_t launch_attention_deferred(const Shape& sh, const AttnParams& p, hipStream_t st);
 
 // Sub-block statistics of a mask (see lamp_subblock_stats).
 hipError_t launch_subblock_stats(const uint8_t* mask, int B, int Hq, int S, int causal,

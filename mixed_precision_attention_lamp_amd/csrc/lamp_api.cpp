@@ -17,7 +17,6 @@ namespace {
 
 constexpr double kLog2e = 1.4426950408889634;   // fp64 nearest to log2(e)
 constexpr int kMaxDevices = 64;
-constexpr int kMaxTiles = 4096;   // KV tiles per sequence (12-bit tile index in the record lists)
 
 thread_local hipStream_t g_stream = nullptr;
 thread_local std::string g_error;
@@ -99,9 +98,6 @@ int check_sizes(int B, int Hq, int Hkv, int S, int D) {
     if (D != 64 && D != 128 && D != 256)
         return fail(LAMP_ERR_UNSUPPORTED, "head dimension D=%d (supported: 64, 128, 256)", D);
     const int64_t nT = (S + 63) / 64;
-    if (nT > kMaxTiles)
-        return fail(LAMP_ERR_UNSUPPORTED, "S=%d exceeds %d (the record lists index tiles in 12 bits)", S,
-                    kMaxTiles * 64);
     const int64_t elems = (int64_t)B * Hq * nT * 64 * D;
     if (elems >= ((int64_t)1 << 31))
         return fail(LAMP_ERR_UNSUPPORTED, "B*Hq*S*D = %lld exceeds 2^31", (long long)elems);
@@ -136,10 +132,10 @@ float exponential_threshold(float delta) {
 }
 
 struct Layout {
-    size_t partial, q_scale, k_scale, q_inv, q8, k8, vt, vsb, rec_m, total;
+    size_t partial, q_scale, k_scale, q_inv, k8, vt, total;
 };
 
-Layout workspace_layout(const lamp::Shape& sh, int causal, int window) {
+Layout workspace_layout(const lamp::Shape& sh) {
     Layout L;
     size_t off = 0;
     auto take = [&](size_t bytes) { size_t o = off; off = round_up(off + bytes, 256); return o; };
@@ -148,15 +144,8 @@ Layout workspace_layout(const lamp::Shape& sh, int causal, int window) {
     L.q_scale = take((size_t)sh.B * sh.Hq * sizeof(float));
     L.q_inv = take((size_t)sh.B * sh.Hq * sizeof(float));
     L.k_scale = take((size_t)sh.B * sh.Hkv * sizeof(float));
-    L.q8 = take((size_t)sh.B * sh.Hq * sh.S_pad * sh.D);
     L.k8 = take((size_t)sh.B * sh.Hkv * sh.S_pad * sh.D);
     L.vt = take((size_t)sh.B * sh.Hkv * sh.nT * sh.D * 64 * sizeof(uint16_t));
-    // the D = 256 kernel's correction layouts
-    const bool deferred = sh.D == 256;
-    L.vsb = take(deferred ? (size_t)sh.B * sh.Hkv * sh.nT * sh.D * 64 * sizeof(uint16_t) : 0);
-    L.rec_m = take(deferred ? (size_t)sh.B * sh.Hq * (size_t)lamp::rec_slot_base(sh.nT, sh.nT, causal, window) *
-                                  64 * sizeof(float)
-                            : 0);
     L.total = off;
     return L;
 }
@@ -177,7 +166,7 @@ static int attn_fwd_impl(const void* q, const void* k, const void* v, float* out
     if (std::isnan(delta) || std::isnan(tau)) return fail(LAMP_ERR_INVALID, "delta and tau must not be NaN");
 
     const lamp::Shape sh = make_shape(B, Hq, Hkv, S, D);
-    const Layout L = workspace_layout(sh, causal, window);
+    const Layout L = workspace_layout(sh);
     void* ws = nullptr;
     rc = get_workspace(L.total, &ws);
     if (rc != LAMP_OK) return rc;
@@ -189,11 +178,8 @@ static int attn_fwd_impl(const void* q, const void* k, const void* v, float* out
     auto* partial = reinterpret_cast<uint32_t*>(base + L.partial);
     auto* q_scale = reinterpret_cast<float*>(base + L.q_scale);
     auto* k_scale = reinterpret_cast<float*>(base + L.k_scale);
-    auto* q8 = base + L.q8;
     auto* k8 = base + L.k8;
     auto* vt = reinterpret_cast<uint16_t*>(base + L.vt);
-    auto* vsb = sh.D == 256 ? reinterpret_cast<uint16_t*>(base + L.vsb) : nullptr;
-    auto* rec_m = sh.D == 256 ? reinterpret_cast<float*>(base + L.rec_m) : nullptr;
 
     hipEvent_t* ev = nullptr;
     if (g_timing && g_n_timed < kMaxTimed) {
@@ -204,19 +190,18 @@ static int attn_fwd_impl(const void* q, const void* k, const void* v, float* out
     }
     if (ev) (void)hipEventRecord(ev[0], g_stream);
     auto* q_inv = reinterpret_cast<float*>(base + L.q_inv);
-    // the D <= 128 attention kernel quantises its Q rows itself
-    hipError_t e = lamp::launch_quantize(sh, q16, k16, partial, q_scale, k_scale, q_inv,
-                                         sh.D == 256 ? q8 : nullptr, k8, sh.S_pad, g_stream);
+    // the attention kernel quantises its Q rows itself
+    hipError_t e = lamp::launch_quantize(sh, q16, k16, partial, q_scale, k_scale, q_inv, nullptr, k8,
+                                         sh.S_pad, g_stream);
     if (e != hipSuccess) return hip_fail(e, "quantise launch");
-    e = lamp::launch_transpose_v(sh, v16, vt, vsb, g_stream);
+    e = lamp::launch_transpose_v(sh, v16, vt, g_stream);
     if (e != hipSuccess) return hip_fail(e, "transpose launch");
     if (ev) (void)hipEventRecord(ev[1], g_stream);
 
     lamp::AttnParams p;
-    p.q8 = q8; p.k8 = k8; p.q16 = q16; p.k16 = k16; p.vt = vt; p.vsb = vsb;
+    p.k8 = k8; p.q16 = q16; p.k16 = k16; p.vt = vt;
     p.q_scale = q_scale; p.k_scale = k_scale; p.q_inv = q_inv;
     p.out = out; p.mask = subblock_mask_out;
-    p.rec_m = rec_m;
     p.log2e_over_sqrt_d = kLog2e / std::sqrt((double)D);
     p.e_delta = exponential_threshold(delta);
     p.t2 = (float)(16.0 * (double)tau * kLog2e);
@@ -295,9 +280,9 @@ int lamp_quantize_qk(const void* q, const void* k, int B, int Hq, int Hkv, int S
     int rc = check_sizes(B, Hq, Hkv, S, D);
     if (rc != LAMP_OK) return rc;
     const lamp::Shape sh = make_shape(B, Hq, Hkv, S, D);
-    const Layout L = workspace_layout(sh, 0, 0);
+    const Layout L = workspace_layout(sh);
     void* ws = nullptr;
-    rc = get_workspace(L.rec_m, &ws);   // the record slots are not needed here
+    rc = get_workspace(L.total, &ws);
     if (rc != LAMP_OK) return rc;
     auto* partial = reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(ws) + L.partial);
     hipError_t e = lamp::launch_quantize(sh, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),

@@ -117,14 +117,10 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(
 
 // One block per (tile, batch*kv head): V[64 keys][D] -> vt[D][64 positions].
 // Within each 32-key half, key 16*hi + 4*g + i goes to position 8*g + 4*hi + i:
-// lane group g of the P.V operand then reads 8 consecutive positions.  Also
-// vsb[4 sub-blocks][D][16 keys] (keys in order): one sub-block's transposed
-// values in 4 contiguous rows-of-32-bytes per 16 columns, for the 16-bit
-// correction of single sub-blocks.
+// lane group g of the P.V operand then reads 8 consecutive positions.
 template <int D>
 __global__ __launch_bounds__(kThreads) void transpose_v_kernel(const uint16_t* __restrict__ v,
-                                                               uint16_t* __restrict__ vt,
-                                                               uint16_t* __restrict__ vsb, int S,
+                                                               uint16_t* __restrict__ vt, int S,
                                                                int nT) {
     constexpr int kStride = D + 8;   // bf16 per LDS row
     __shared__ uint16_t tile[kTileKeys * kStride];
@@ -157,21 +153,6 @@ __global__ __launch_bounds__(kThreads) void transpose_v_kernel(const uint16_t* _
             packed[j] = (uint32_t)tile[k0 * kStride + d] | ((uint32_t)tile[k1 * kStride + d] << 16);
         }
         *reinterpret_cast<u32x4*>(out + d * kTileKeys + pb * 8) =
-            u32x4{packed[0], packed[1], packed[2], packed[3]};
-    }
-    if (vsb == nullptr) return;
-    uint16_t* out_sb = vsb + ((size_t)bh * nT + t) * D * kTileKeys;
-#pragma unroll
-    for (int it = 0; it < kSubBlocks * D * 2 / kThreads; ++it) {
-        const int w = threadIdx.x + it * kThreads;
-        const int c = w / (2 * D), d = (w / 2) % D, half = w % 2;   // keys 16c + 8 half .. +7
-        uint32_t packed[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int k0 = 16 * c + 8 * half + 2 * j;
-            packed[j] = (uint32_t)tile[k0 * kStride + d] | ((uint32_t)tile[(k0 + 1) * kStride + d] << 16);
-        }
-        *reinterpret_cast<u32x4*>(out_sb + (c * D + d) * kSubKeys + half * 8) =
             u32x4{packed[0], packed[1], packed[2], packed[3]};
     }
 }
@@ -208,15 +189,14 @@ hipError_t launch_quantize(const Shape& sh, const uint16_t* q, const uint16_t* k
     return hipGetLastError();
 }
 
-hipError_t launch_transpose_v(const Shape& sh, const uint16_t* v, uint16_t* vt, uint16_t* vsb,
-                              hipStream_t st) {
+hipError_t launch_transpose_v(const Shape& sh, const uint16_t* v, uint16_t* vt, hipStream_t st) {
     const dim3 grid(sh.nT, sh.B * sh.Hkv);
     if (sh.D == 64)
-        hipLaunchKernelGGL(transpose_v_kernel<64>, grid, dim3(kThreads), 0, st, v, vt, vsb, sh.S, sh.nT);
+        hipLaunchKernelGGL(transpose_v_kernel<64>, grid, dim3(kThreads), 0, st, v, vt, sh.S, sh.nT);
     else if (sh.D == 128)
-        hipLaunchKernelGGL(transpose_v_kernel<128>, grid, dim3(kThreads), 0, st, v, vt, vsb, sh.S, sh.nT);
+        hipLaunchKernelGGL(transpose_v_kernel<128>, grid, dim3(kThreads), 0, st, v, vt, sh.S, sh.nT);
     else
-        hipLaunchKernelGGL(transpose_v_kernel<256>, grid, dim3(kThreads), 0, st, v, vt, vsb, sh.S, sh.nT);
+        hipLaunchKernelGGL(transpose_v_kernel<256>, grid, dim3(kThreads), 0, st, v, vt, sh.S, sh.nT);
     return hipGetLastError();
 }
 

@@ -54,7 +54,6 @@ def _fwd(lib, **kw):
     (dict(Hq=3, Hkv=2), -1, "multiple"),
     (dict(D=96), -2, "D=96"),
     (dict(D=512), -2, "D=512"),
-    (dict(S=4096 * 64 + 1), -2, "exceeds"),
     (dict(causal=2), -1, "causal"),
     (dict(window=-1), -1, "window"),
     (dict(window=16, causal=0), -1, "window"),
