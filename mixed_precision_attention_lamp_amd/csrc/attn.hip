@@ -99,10 +99,13 @@ struct Cfg {
     static constexpr int kVtBytes = D * kVtRow;
     static constexpr int kQ16Bytes = kWaveRows * kK16Row;      // per wave
     static constexpr int kQ8Bytes = kWaveRows * kK8Row;        // per wave
+    // ping-pong schedule (two K16 and V^T slots) where the slots fit in LDS
+    static constexpr bool kPP = D <= 128;
+    static constexpr int kSlots16 = kPP ? 2 : 1;
     static constexpr int kK8Off = 0;                            // two slots
-    static constexpr int kK16Off = 2 * kK8Bytes;                // one slot
-    static constexpr int kVtOff = kK16Off + kK16Bytes;          // one slot
-    static constexpr int kQ8Off = kVtOff + kVtBytes;
+    static constexpr int kK16Off = 2 * kK8Bytes;
+    static constexpr int kVtOff = kK16Off + kSlots16 * kK16Bytes;
+    static constexpr int kQ8Off = kVtOff + kSlots16 * kVtBytes;
     static constexpr int kLdsBytes = kQ8Off + kWaves * kQ8Bytes;
     static constexpr int kDB = D / 16;        // 16-wide output column blocks
     static constexpr int kDC = D / 32;        // 32-deep bf16 matrix-core steps
@@ -152,21 +155,26 @@ __global__ __launch_bounds__(kThreads, 1) void lamp_attn_kernel(AttnArgs a) {
     // ---- staging: register loads at the start of an iteration, LDS stores at its end
     // Thread tid owns the 16-byte chunks tid + kThreads*i of a tile, i.e. LDS
     // bytes [16 c, 16 c + 16) of the swizzled layout, and loads the global chunk
-    // that belongs there.
+    // that belongs there.  Loads and stores run every iteration: a tile past
+    // the last one reloads the last one (its stores fill slots that no later
+    // phase reads), which keeps every load consumed by a store on every path
+    // and so keeps the compiler from waiting on loads at the loop head.
     constexpr int kK8Ch = C::kK8Bytes / 16 / kThreads;     // chunks per thread and tile
     constexpr int kK16Ch = C::kK16Bytes / 16 / kThreads;
     constexpr int kVtCh = C::kVtBytes / 16 / kThreads;
     static_assert(kK16Ch >= 1 && kVtCh >= 1, "tile smaller than one chunk per thread");
     constexpr int kK8ChMin = kK8Ch > 0 ? kK8Ch : 1;
     u32x4 st_k8[kK8ChMin], st_k16[kK16Ch], st_vt[kVtCh];
+    // Global addresses are a wave-uniform tile base plus an unsigned 32-bit
+    // per-thread byte offset (scalar base + vector offset addressing).
     auto load_k8 = [&](int t) __attribute__((always_inline)) {
-        const uint8_t* src = a.k8 + (kv_head * a.S_pad + (size_t)t * kTileKeys) * D;
+        const uint8_t* src = a.k8 + (kv_head * a.S_pad + (size_t)min(t, t_end) * kTileKeys) * D;
         constexpr int kNC = C::kK8Row / 16;
 #pragma unroll
         for (int i = 0; i < kK8ChMin; ++i) {
-            const int p = min((tid + i * kThreads) * 16, C::kK8Bytes - 16);
-            const int row = p / C::kK8Row, slot = (p % C::kK8Row) >> 4;
-            st_k8[i] = *reinterpret_cast<const u32x4*>(src + row * C::kK8Row + ((slot ^ swz<kNC>(row)) << 4));
+            const unsigned p = min((tid + i * kThreads) * 16, C::kK8Bytes - 16);
+            const unsigned row = p / C::kK8Row, slot = (p % C::kK8Row) >> 4;
+            st_k8[i] = *reinterpret_cast<const u32x4*>(src + (row * C::kK8Row + ((slot ^ swz<kNC>(row)) << 4)));
         }
     };
     auto store_k8 = [&](int t) __attribute__((always_inline)) {
@@ -177,35 +185,35 @@ __global__ __launch_bounds__(kThreads, 1) void lamp_attn_kernel(AttnArgs a) {
             if (p < C::kK8Bytes) *reinterpret_cast<u32x4*>(base + p) = st_k8[i];
         }
     };
+    const uint8_t* k16_head = reinterpret_cast<const uint8_t*>(a.k16 + kv_head * a.S * D);
     auto load_k16 = [&](int t) __attribute__((always_inline)) {
         constexpr int kNC = C::kK16Row / 16;
 #pragma unroll
         for (int i = 0; i < kK16Ch; ++i) {
-            const int p = (tid + i * kThreads) * 16;
-            const int row = p / C::kK16Row, slot = (p % C::kK16Row) >> 4;
+            const unsigned p = (tid + i * kThreads) * 16;
+            const unsigned row = p / C::kK16Row, slot = (p % C::kK16Row) >> 4;
             // keys past the end reload the last key: they are masked out
-            const int key = min(t * kTileKeys + row, a.S - 1);
-            st_k16[i] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint8_t*>(a.k16 + (kv_head * a.S + key) * D) +
-                                                        ((slot ^ swz<kNC>(row)) << 4));
+            const unsigned key = min(t * kTileKeys + (int)row, a.S - 1);
+            st_k16[i] = *reinterpret_cast<const u32x4*>(k16_head + (key * C::kK16Row + ((slot ^ swz<kNC>(row)) << 4)));
         }
     };
-    auto store_k16 = [&]() __attribute__((always_inline)) {
-        uint8_t* base = lds + C::kK16Off;
+    auto store_k16 = [&](int slot) __attribute__((always_inline)) {
+        uint8_t* base = lds + C::kK16Off + slot * C::kK16Bytes;
 #pragma unroll
         for (int i = 0; i < kK16Ch; ++i) *reinterpret_cast<u32x4*>(base + (tid + i * kThreads) * 16) = st_k16[i];
     };
     auto load_vt = [&](int t) __attribute__((always_inline)) {
-        const uint8_t* src = reinterpret_cast<const uint8_t*>(a.vt + (kv_head * a.nT + t) * (size_t)D * kTileKeys);
+        const uint8_t* src = reinterpret_cast<const uint8_t*>(a.vt + (kv_head * a.nT + min(t, t_end)) * (size_t)D * kTileKeys);
         constexpr int kNC = C::kVtRow / 16;
 #pragma unroll
         for (int i = 0; i < kVtCh; ++i) {
-            const int p = (tid + i * kThreads) * 16;
-            const int row = p / C::kVtRow, slot = (p % C::kVtRow) >> 4;
-            st_vt[i] = *reinterpret_cast<const u32x4*>(src + row * C::kVtRow + ((slot ^ swz<kNC>(row)) << 4));
+            const unsigned p = (tid + i * kThreads) * 16;
+            const unsigned row = p / C::kVtRow, slot = (p % C::kVtRow) >> 4;
+            st_vt[i] = *reinterpret_cast<const u32x4*>(src + (row * C::kVtRow + ((slot ^ swz<kNC>(row)) << 4)));
         }
     };
-    auto store_vt = [&]() __attribute__((always_inline)) {
-        uint8_t* base = lds + C::kVtOff;
+    auto store_vt = [&](int slot) __attribute__((always_inline)) {
+        uint8_t* base = lds + C::kVtOff + slot * C::kVtBytes;
 #pragma unroll
         for (int i = 0; i < kVtCh; ++i) *reinterpret_cast<u32x4*>(base + (tid + i * kThreads) * 16) = st_vt[i];
     };
@@ -299,8 +307,44 @@ __global__ __launch_bounds__(kThreads, 1) void lamp_attn_kernel(AttnArgs a) {
     const v8bf ones = {(__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f,
                        (__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f};
     auto pv = [&](const u32x2 (&P)[kQG][4], int t) __attribute__((always_inline)) {
-        (void)t;
-        const uint8_t* vtl = lds + C::kVtOff;
+        const uint8_t* vtl = lds + C::kVtOff + (C::kPP ? (t & 1) * C::kVtBytes : 0);
+        if constexpr (C::kPP) {
+            // software-pipelined operand reads: the first half's V^T operands
+            // are read up front, and each read of the second half reuses the
+            // registers of the first-half operand whose products were just
+            // issued; the schedule is pinned (the scheduler would sink every
+            // read next to its use)
+            v8bf va[C::kDB];
+#pragma unroll
+            for (int db = 0; db < C::kDB; ++db)
+                va[db] = *reinterpret_cast<const v8bf*>(vtl + lds_off<C::kVtRow>(db * 16 + n16, g));
+            __builtin_amdgcn_sched_group_barrier(0x100, C::kDB, 0);
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                v8bf pb[kQG];
+#pragma unroll
+                for (int qg = 0; qg < kQG; ++qg) {
+                    const u32x4 w = {P[qg][2 * h][0], P[qg][2 * h][1], P[qg][2 * h + 1][0], P[qg][2 * h + 1][1]};
+                    pb[qg] = __builtin_bit_cast(v8bf, w);
+                }
+#pragma unroll
+                for (int db = 0; db < C::kDB; ++db) {
+#pragma unroll
+                    for (int qg = 0; qg < kQG; ++qg)
+                        acc_o[qg][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[db], pb[qg], acc_o[qg][db], 0, 0, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x008, kQG, 0);
+                    if (h == 0) {
+                        va[db] = *reinterpret_cast<const v8bf*>(vtl + lds_off<C::kVtRow>(db * 16 + n16, 4 + g));
+                        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                    }
+                }
+#pragma unroll
+                for (int qg = 0; qg < kQG; ++qg)
+                    acc_l[qg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pb[qg], acc_l[qg], 0, 0, 0);
+                __builtin_amdgcn_sched_group_barrier(0x008, kQG, 0);
+            }
+            return;
+        }
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             v8bf pb[kQG];
@@ -459,8 +503,9 @@ __global__ __launch_bounds__(kThreads, 1) void lamp_attn_kernel(AttnArgs a) {
     // the wave walks its set bits behind scalar branches, running the bf16
     // logits of each flagged sub-block on the matrix cores and rounding its
     // exponentials to bf16 into the compile-time-indexed register tile P.
-    auto recompute = [&](u32x2 (&P)[kQG][4], uint32_t flags, bool masked) __attribute__((always_inline)) {
-        const uint8_t* k16l = lds + C::kK16Off;
+    auto recompute = [&](u32x2 (&P)[kQG][4], uint32_t flags, auto masked_tag, int t) __attribute__((always_inline)) {
+        constexpr bool kMasked = decltype(masked_tag)::value;
+        const uint8_t* k16l = lds + C::kK16Off + (C::kPP ? (t & 1) * C::kK16Bytes : 0);
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
             if (!((flags >> c) & 1u)) continue;
@@ -480,35 +525,132 @@ __global__ __launch_bounds__(kThreads, 1) void lamp_attn_kernel(AttnArgs a) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     e[i] = fast_exp2(__builtin_fmaf(acc16[qg][i], c16, -m_use[qg]));
-                    if (masked) e[i] = ((vis[qg] >> (c * 4 + i)) & 1u) ? e[i] : 0.0f;
+                    if constexpr (kMasked) e[i] = ((vis[qg] >> (c * 4 + i)) & 1u) ? e[i] : 0.0f;
                 }
                 P[qg][c] = u32x2{f32x2_to_bf16x2(e[0], e[1]), f32x2_to_bf16x2(e[2], e[3])};
             }
         }
     };
 
-    // ---- prologue staging and the first tile's Q.K^T ------------------------------
+    // debug: the final weights of tile t
+    auto dump_p = [&](const u32x2 (&P)[kQG][4], int t) __attribute__((always_inline)) {
+        if constexpr (kDump) {
+#pragma unroll
+            for (int qg = 0; qg < kQG; ++qg) {
+                const int qi = row0 + qg * 16 + n16;
+#pragma unroll
+                for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int kj = t * kTileKeys + kb * 16 + g * 4 + i;
+                        const uint32_t w = P[qg][kb][i / 2];
+                        if (qi < a.S && kj < a.S)
+                            a.dump_p[(q_head * a.S + qi) * a.S + kj] = (uint16_t)((i & 1) ? (w >> 16) : (w & 0xFFFFu));
+                    }
+            }
+        }
+    };
+    // (6) online-softmax rescale of everything accumulated so far, before the
+    //     P.V of tile t
+    auto rescale = [&]() __attribute__((always_inline)) {
+#pragma unroll
+        for (int qg = 0; qg < kQG; ++qg) {
+            if (wave_ballot(alpha[qg] != 1.0f) != 0) {
+                acc_l[qg] *= alpha[qg];
+#pragma unroll
+                for (int db = 0; db < C::kDB; ++db) acc_o[qg][db] *= alpha[qg];
+            }
+        }
+    };
+
     v4f S[kQG][4];
     u32x2 P[kQG][4];
+    if constexpr (C::kPP) {
+    // ---- ping-pong schedule ---------------------------------------------------------
+    // Waves 0-3 (one per SIMD) and waves 4-7 run the same sequence of phases,
+    // the second group one phase behind the first, so that on every SIMD one
+    // wave is in a vector phase while the other is in a matrix phase:
+    //   V(t): running max, exponentials and test of tile t, flags out;
+    //   M(t): rescale, 16-bit recompute and P.V of tile t, Q.K^T of tile t+1,
+    //         and the LDS stores of K8(t+2), K16(t+1) and V^T(t+1) (loaded in
+    //         V(t)).
+    // A workgroup barrier ends every phase.  The two groups read the K16 and
+    // V^T tiles of t and the K8 tile of t+1 in two consecutive phases, M(t) of
+    // each; two slots of each array then suffice, and the stores of a phase
+    // never touch a slot read in it.
+    const int grp = wave >> 2;
+    load_k8(t_begin);
+    store_k8(t_begin);
+    load_k8(t_begin + 1);
+    load_k16(t_begin);
+    load_vt(t_begin);
+    lds_barrier();
+    if (grp == 1) lds_barrier();
+    // M(t_begin - 1): the first Q.K^T and the stores for tile t_begin
+    if (work(t_begin)) qk(S, t_begin);
+    store_k8(t_begin + 1);
+    store_k16(t_begin & 1);
+    store_vt(t_begin & 1);
+    lds_barrier();
+    for (int t = t_begin; t <= t_end; ++t) {
+        const bool w_cur = work(t), w_next = work(t + 1);
+        const bool full = tile_full(r, t, a.S, a.causal, a.window);
+        // ---- V(t)
+        load_k8(t + 2);
+        load_k16(t + 1);
+        load_vt(t + 1);
+        uint32_t flags = 0;
+        if (w_cur) {
+            if (full) softmax(S, P, t, std::integral_constant<bool, false>{});
+            else softmax(S, P, t, std::integral_constant<bool, true>{});
+            flags = test(S, !full);
+        }
+        if (lane == 0) flag_lds[wave] = flags;
+        lds_barrier();
+        // ---- M(t), at raised issue priority: the matrix-core work of this wave
+        // goes first and the vector work of the other wave fills around it
+        __builtin_amdgcn_s_setprio(1);
+        flags = 0;
+#pragma unroll
+        for (int w = 0; w < C::kWavesPerBlock; ++w) flags |= flag_lds[blk * C::kWavesPerBlock + w];
+        // the loads of V(t) have arrived; storing them first frees their registers
+        store_k8(t + 2);
+        store_k16((t + 1) & 1);
+        store_vt((t + 1) & 1);
+        if (w_cur) {
+            rescale();
+            if (flags != 0) {
+                if (full) recompute(P, flags, std::integral_constant<bool, false>{}, t);
+                else recompute(P, flags, std::integral_constant<bool, true>{}, t);
+            }
+            dump_p(P, t);
+            pv(P, t);
+            if (a.mask && wib == 0 && lane == 0)
+                a.mask[(q_head * a.nT + r) * a.nT + t] = (uint8_t)(0x80u | flags);
+        }
+        if (w_next) qk(S, t + 1);
+        __builtin_amdgcn_s_setprio(0);
+        lds_barrier();
+    }
+    if (grp == 0) lds_barrier();
+    } else {
+    // ---- prologue staging and the first tile's Q.K^T ------------------------------
     load_k8(t_begin);
     load_k16(t_begin);
     store_k8(t_begin);
-    store_k16();
-    if (t_begin + 1 <= t_end) {
-        load_k8(t_begin + 1);
-        store_k8(t_begin + 1);
-    }
+    store_k16(0);
+    load_k8(t_begin + 1);
+    store_k8(t_begin + 1);
     lds_barrier();
     if (work(t_begin)) qk(S, t_begin);
     lds_barrier();   // every wave has read K8(t_begin) before its slot is refilled
 
     // ---- the pipelined loop ---------------------------------------------------------
     for (int t = t_begin; t <= t_end; ++t) {
-        const bool ld_k8 = t + 2 <= t_end, ld_k16 = t + 1 <= t_end;
         // K16 of tile t (loaded in the previous iteration) into its single slot:
         // every wave has finished the recompute of tile t-1, and the flag
         // barrier below orders these stores before the recompute of tile t
-        if (t > t_begin) store_k16();
+        if (t > t_begin) store_k16(0);
         const bool w_prev = work(t - 1), w_cur = work(t), w_next = work(t + 1);
         const bool full = tile_full(r, t, a.S, a.causal, a.window);
         // P.V of tile t-1 is issued first (it reads P before the exponentials
@@ -521,8 +663,8 @@ __global__ __launch_bounds__(kThreads, 1) void lamp_attn_kernel(AttnArgs a) {
         }
         // loads for later tiles, stored to LDS before the barrier that ends this
         // iteration
-        if (ld_k8) load_k8(t + 2);
-        if (ld_k16) load_k16(t + 1);
+        load_k8(t + 2);
+        load_k16(t + 1);
         load_vt(t);
         uint32_t flags = w_cur ? test(S, !full) : 0u;
         // the waves of a 64-row block OR their flags
@@ -531,35 +673,15 @@ __global__ __launch_bounds__(kThreads, 1) void lamp_attn_kernel(AttnArgs a) {
         flags = 0;
 #pragma unroll
         for (int w = 0; w < C::kWavesPerBlock; ++w) flags |= flag_lds[blk * C::kWavesPerBlock + w];
-        if (w_cur && flags != 0) recompute(P, flags, !full);
+        if (w_cur && flags != 0) {
+            if (full) recompute(P, flags, std::integral_constant<bool, false>{}, t);
+            else recompute(P, flags, std::integral_constant<bool, true>{}, t);
+        }
         // Q.K^T of tile t+1 runs on the matrix cores under what follows
         if (w_next) qk(S, t + 1);
         if (w_cur) {
-            if constexpr (kDump) {
-#pragma unroll
-                for (int qg = 0; qg < kQG; ++qg) {
-                    const int qi = row0 + qg * 16 + n16;
-#pragma unroll
-                    for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) {
-                            const int kj = t * kTileKeys + kb * 16 + g * 4 + i;
-                            const uint32_t w = P[qg][kb][i / 2];
-                            if (qi < a.S && kj < a.S)
-                                a.dump_p[(q_head * a.S + qi) * a.S + kj] = (uint16_t)((i & 1) ? (w >> 16) : (w & 0xFFFFu));
-                        }
-                }
-            }
-            // (6) online-softmax rescale of everything accumulated so far (the
-            //     P.V of tile t-1 included), before the P.V of tile t
-#pragma unroll
-            for (int qg = 0; qg < kQG; ++qg) {
-                if (wave_ballot(alpha[qg] != 1.0f) != 0) {
-                    acc_l[qg] *= alpha[qg];
-#pragma unroll
-                    for (int db = 0; db < C::kDB; ++db) acc_o[qg][db] *= alpha[qg];
-                }
-            }
+            dump_p(P, t);
+            rescale();
             // (7) mask byte
             if (a.mask && wib == 0 && lane == 0)
                 a.mask[(q_head * a.nT + r) * a.nT + t] = (uint8_t)(0x80u | flags);
@@ -567,12 +689,13 @@ __global__ __launch_bounds__(kThreads, 1) void lamp_attn_kernel(AttnArgs a) {
         // K8 of tile t+2 into the slot Q.K^T of tile t used; V^T of tile t into
         // its single slot (every wave passed the flag barrier, so the P.V of
         // tile t-1 has read it)
-        if (ld_k8) store_k8(t + 2);
-        store_vt();
+        store_k8(t + 2);
+        store_vt(0);
         lds_barrier();
     }
     // P.V of the last tile
     if (work(t_end)) pv(P, t_end);
+    }
 
     // ---- epilogue: out = O / l ------------------------------------------------------
     if (active) {

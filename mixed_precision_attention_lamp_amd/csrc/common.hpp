@@ -70,11 +70,17 @@ __device__ __forceinline__ void lds_barrier() {
 // Lane mask of a predicate, kept in scalar registers.
 __device__ __forceinline__ uint64_t wave_ballot(bool p) { return __builtin_amdgcn_ballot_w64(p); }
 
-// Cross-lane max over the four 16-lane groups of a wave (lanes l, l^16, l^32, l^48).
+// Cross-lane max over the four 16-lane groups of a wave (lanes l, l^16, l^32,
+// l^48).  A permlane swap of a value with itself leaves each lane holding its
+// own value in one result and its partner's (l^32, resp. l^16) in the other,
+// in registers and without LDS.
 __device__ __forceinline__ float max_over_lane_groups(float x) {
-    x = __builtin_fmaxf(x, __shfl_xor(x, 16, 64));
-    x = __builtin_fmaxf(x, __shfl_xor(x, 32, 64));
-    return x;
+    const uint32_t b = __float_as_uint(x);
+    const auto s32 = __builtin_amdgcn_permlane32_swap(b, b, false, false);
+    x = __builtin_fmaxf(__uint_as_float(s32[0]), __uint_as_float(s32[1]));
+    const uint32_t c = __float_as_uint(x);
+    const auto s16 = __builtin_amdgcn_permlane16_swap(c, c, false, false);
+    return __builtin_fmaxf(__uint_as_float(s16[0]), __uint_as_float(s16[1]));
 }
 
 }  // namespace lamp
