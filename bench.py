@@ -34,8 +34,8 @@ COPY_BYTES = 1 << 30       # size of the calibration copy
 # by the same counter's reading for a plain copy of COPY_BYTES (see
 # profiles/attn_qwen3_8b_hbm_traffic.md).  Valid only for the kernel source
 # whose hash is recorded; any change to it makes the figure null.
-TRAFFIC = {"kernel_hash": "fe65578f2ff5ece9", "workload": "qwen3-8b", "delta": 2.0 ** -8, "tau": 2.0 ** -1,
-           "bytes_per_launch": 130017907.0}
+TRAFFIC = {"kernel_hash": "80c20d555b8ce0b2", "workload": "qwen3-8b", "delta": 2.0 ** -8, "tau": 2.0 ** -1,
+           "bytes_per_launch": 130267744.2}
 
 
 def kernel_source_hash():
@@ -125,8 +125,8 @@ def cpu_baseline(q, k, v, cfg, delta, tau, budget_s, cores):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--workload", default="qwen3-8b")
     ap.add_argument("--delta", type=float, default=2.0 ** -8)
     ap.add_argument("--tau", type=float, default=2.0 ** -1)

@@ -306,14 +306,14 @@ __global__ __launch_bounds__(kThreads, 1) void lamp_attn_kernel(AttnArgs a) {
     // P.V of tile t (and the row sums, with an all-ones operand)
     const v8bf ones = {(__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f,
                        (__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f};
+    // Ping-pong schedule: software-pipelined V^T operand reads.  The first
+    // half's operands are read up front, and each read of the second half
+    // reuses the registers of the first-half operand whose products were just
+    // issued; the schedule is pinned (the scheduler would sink every read next
+    // to its use).
     auto pv = [&](const u32x2 (&P)[kQG][4], int t) __attribute__((always_inline)) {
         const uint8_t* vtl = lds + C::kVtOff + (C::kPP ? (t & 1) * C::kVtBytes : 0);
         if constexpr (C::kPP) {
-            // software-pipelined operand reads: the first half's V^T operands
-            // are read up front, and each read of the second half reuses the
-            // registers of the first-half operand whose products were just
-            // issued; the schedule is pinned (the scheduler would sink every
-            // read next to its use)
             v8bf va[C::kDB];
 #pragma unroll
             for (int db = 0; db < C::kDB; ++db)
@@ -430,7 +430,11 @@ __global__ __launch_bounds__(kThreads, 1) void lamp_attn_kernel(AttnArgs a) {
                     e[i] = fast_exp2(__builtin_fmaf(s[qg][kb][i], c8, -m_use[qg]));
                     if constexpr (kMasked) e[i] = ((vis[qg] >> (kb * 4 + i)) & 1u) ? e[i] : 0.0f;
                 }
-                const uint32_t w = cvt_pk_e4m3_unit<true>(e[2], e[3], cvt_pk_e4m3_unit<false>(e[0], e[1], 0u));
+                // the high half of the first conversion's destination is
+                // overwritten by the second: any dead register serves as its
+                // initial value (a zero would cost a move per conversion)
+                const uint32_t w = cvt_pk_e4m3_unit<true>(
+                    e[2], e[3], cvt_pk_e4m3_unit<false>(e[0], e[1], __float_as_uint(e[0])));
                 P[qg][kb] = u32x2{e4m3x2_to_bf16x2<false>(w), e4m3x2_to_bf16x2<true>(w)};
             }
         if constexpr (kDump) {
@@ -570,8 +574,9 @@ __global__ __launch_bounds__(kThreads, 1) void lamp_attn_kernel(AttnArgs a) {
     // Waves 0-3 (one per SIMD) and waves 4-7 run the same sequence of phases,
     // the second group one phase behind the first, so that on every SIMD one
     // wave is in a vector phase while the other is in a matrix phase:
-    //   V(t): running max, exponentials and test of tile t, flags out;
-    //   M(t): rescale, 16-bit recompute and P.V of tile t, Q.K^T of tile t+1,
+    //   V(t): running max, exponentials, rescale and test of tile t, flags
+    //         out;
+    //   M(t): 16-bit recompute and P.V of tile t, Q.K^T of tile t+1,
     //         and the LDS stores of K8(t+2), K16(t+1) and V^T(t+1) (loaded in
     //         V(t)).
     // A workgroup barrier ends every phase.  The two groups read the K16 and
@@ -603,6 +608,7 @@ __global__ __launch_bounds__(kThreads, 1) void lamp_attn_kernel(AttnArgs a) {
         if (w_cur) {
             if (full) softmax(S, P, t, std::integral_constant<bool, false>{});
             else softmax(S, P, t, std::integral_constant<bool, true>{});
+            rescale();
             flags = test(S, !full);
         }
         if (lane == 0) flag_lds[wave] = flags;
@@ -613,12 +619,12 @@ __global__ __launch_bounds__(kThreads, 1) void lamp_attn_kernel(AttnArgs a) {
         flags = 0;
 #pragma unroll
         for (int w = 0; w < C::kWavesPerBlock; ++w) flags |= flag_lds[blk * C::kWavesPerBlock + w];
+        flags = __builtin_amdgcn_readfirstlane(flags);
         // the loads of V(t) have arrived; storing them first frees their registers
         store_k8(t + 2);
         store_k16((t + 1) & 1);
         store_vt((t + 1) & 1);
         if (w_cur) {
-            rescale();
             if (flags != 0) {
                 if (full) recompute(P, flags, std::integral_constant<bool, false>{}, t);
                 else recompute(P, flags, std::integral_constant<bool, true>{}, t);
@@ -673,6 +679,7 @@ __global__ __launch_bounds__(kThreads, 1) void lamp_attn_kernel(AttnArgs a) {
         flags = 0;
 #pragma unroll
         for (int w = 0; w < C::kWavesPerBlock; ++w) flags |= flag_lds[blk * C::kWavesPerBlock + w];
+        flags = __builtin_amdgcn_readfirstlane(flags);
         if (w_cur && flags != 0) {
             if (full) recompute(P, flags, std::integral_constant<bool, false>{}, t);
             else recompute(P, flags, std::integral_constant<bool, true>{}, t);
