@@ -78,7 +78,6 @@ struct AttnArgs {
     int heads_per_wg;    // kBlocks, ..., 1
     int rows_per_wg;     // kBlocks / heads_per_wg
     int n_rg;            // row-block groups
-    int xcd_remap;       // number of workgroups is a multiple of 8
     int n_wg;
 };
 
@@ -129,11 +128,18 @@ __global__ __launch_bounds__(kThreads, 1) void lamp_attn_kernel(AttnArgs a) {
     const int wib = wave % C::kWavesPerBlock;   // rows wib*kWaveRows .. of that block
 
     // ---- workgroup -> (batch, kv head, head group, row-block group) ----------
-    int wg = blockIdx.x;
-    if (a.xcd_remap) wg = (wg & 7) * (a.n_wg >> 3) + (wg >> 3);
+    // Workgroups are dispatched in index order, round-robin over the XCDs.
+    // Index order is longest (causal) rows first, so that the CUs that free
+    // first take the longest of the remaining rows; within a level of equal
+    // length the (batch, kv head, head group) units rotate by one per level,
+    // so that every XCD sees every unit (units differ in how much they
+    // recompute) rather than one unit per XCD.
+    const int wg = blockIdx.x;
     const int n_hg = a.G / a.heads_per_wg;
-    int u = wg / a.n_rg;
-    const int rg = a.n_rg - 1 - (wg % a.n_rg);   // longest (causal) rows first
+    const int n_u = a.n_wg / a.n_rg;
+    const int level = wg / n_u;
+    const int rg = a.n_rg - 1 - level;
+    int u = (wg % n_u + level) % n_u;
     const int hg = u % n_hg;
     u /= n_hg;
     const int hk = u % a.Hkv;
@@ -738,7 +744,6 @@ hipError_t launch_d(const Shape& sh, const AttnParams& p, hipStream_t st) {
     a.rows_per_wg = Cfg<D>::kBlocks / a.heads_per_wg;
     a.n_rg = (sh.nT + a.rows_per_wg - 1) / a.rows_per_wg;
     a.n_wg = sh.B * sh.Hkv * (a.G / a.heads_per_wg) * a.n_rg;
-    a.xcd_remap = (a.n_wg % 8 == 0) ? 1 : 0;
     const size_t lds = Cfg<D>::kLdsBytes;
     const bool dump = p.dump_s != nullptr && p.dump_p != nullptr;
     using Fn = void (*)(AttnArgs);
