@@ -14,7 +14,7 @@ struct Shape {
     int S_pad;   // nT * 64
 };
 
-// Bytes of amax partial maxima for a slab of S*D bf16 values.
+// Number of amax partial maxima (chunks) for a slab of S*D bf16 values.
 int amax_chunks(int S, int D);
 
 // Quantisation pass (Q and K): per-(batch, head) amax partial maxima, then
@@ -26,9 +26,16 @@ hipError_t launch_quantize(const Shape& sh, const uint16_t* q, const uint16_t* k
                            uint32_t* partial, float* q_scale, float* k_scale, float* q_inv,
                            uint8_t* q8, uint8_t* k8, int rows_out, hipStream_t st);
 
+// The amax partial maxima of launch_quantize, and in the same launch
 // V [B, Hkv, S, D] -> vt [B, Hkv, nT, D, 64] (keys of each tile transposed and
 // permuted into the order the P.V matrix-core operand reads; padding keys 0).
-hipError_t launch_transpose_v(const Shape& sh, const uint16_t* v, uint16_t* vt, hipStream_t st);
+hipError_t launch_amax_transpose(const Shape& sh, const uint16_t* q, const uint16_t* k,
+                                 uint32_t* partial, const uint16_t* v, uint16_t* vt, hipStream_t st);
+
+// The second half of launch_quantize: scales and codes from the partial maxima.
+hipError_t launch_quantize_codes(const Shape& sh, const uint16_t* q, const uint16_t* k,
+                                 const uint32_t* partial, float* q_scale, float* k_scale, float* q_inv,
+                                 uint8_t* q8, uint8_t* k8, int rows_out, hipStream_t st);
 
 struct AttnParams {
     const uint8_t* k8;      // [B, Hkv, S_pad, D]

@@ -190,12 +190,13 @@ static int attn_fwd_impl(const void* q, const void* k, const void* v, float* out
     }
     if (ev) (void)hipEventRecord(ev[0], g_stream);
     auto* q_inv = reinterpret_cast<float*>(base + L.q_inv);
-    // the attention kernel quantises its Q rows itself
-    hipError_t e = lamp::launch_quantize(sh, q16, k16, partial, q_scale, k_scale, q_inv, nullptr, k8,
-                                         sh.S_pad, g_stream);
+    // amax partial maxima and the V transpose, then scales and K8 (the
+    // attention kernel quantises its Q rows itself)
+    hipError_t e = lamp::launch_amax_transpose(sh, q16, k16, partial, v16, vt, g_stream);
+    if (e != hipSuccess) return hip_fail(e, "amax/transpose launch");
+    e = lamp::launch_quantize_codes(sh, q16, k16, partial, q_scale, k_scale, q_inv, nullptr, k8, sh.S_pad,
+                                    g_stream);
     if (e != hipSuccess) return hip_fail(e, "quantise launch");
-    e = lamp::launch_transpose_v(sh, v16, vt, g_stream);
-    if (e != hipSuccess) return hip_fail(e, "transpose launch");
     if (ev) (void)hipEventRecord(ev[1], g_stream);
 
     lamp::AttnParams p;

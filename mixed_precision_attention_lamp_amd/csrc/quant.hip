@@ -8,7 +8,8 @@
 // quantise; the second read is served mostly from the last-level cache) and
 // one byte is written.  V is transposed per 64-key tile here as well, so that
 // the attention kernel can stage it straight into the layout of the P.V
-// matrix-core operand.
+// matrix-core operand; that transpose runs in the same launch as the amax
+// reduction (both only read the inputs).
 #include <hip/hip_runtime.h>
 
 #include "common.hpp"
@@ -18,7 +19,7 @@ namespace lamp {
 
 namespace {
 
-constexpr int kChunk = 32768;      // bf16 values per amax / quantise block
+constexpr int kChunk = 8192;       // bf16 values per amax / quantise block (4 loads per thread)
 constexpr int kThreads = 256;
 
 __device__ __forceinline__ uint32_t max_bf16_mag(u32x4 w) {
@@ -43,37 +44,50 @@ __device__ __forceinline__ uint32_t block_max_u32(uint32_t v, uint32_t* red) {
     return v;
 }
 
+// Partial max |x| of chunk `chunk` of slab `slab` (Q heads first, then K
+// heads) into partial[slab * nch + chunk].
+__device__ __forceinline__ void amax_block(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+                                           uint32_t* __restrict__ partial, int n_q_slabs, int slab_len,
+                                           int nch, int slab, int chunk, uint32_t* red) {
+    const uint16_t* src = slab < n_q_slabs ? q + (size_t)slab * slab_len
+                                           : k + (size_t)(slab - n_q_slabs) * slab_len;
+    const int begin = chunk * kChunk;
+    const int end = min(begin + kChunk, slab_len);
+    uint32_t m = 0;
+#pragma unroll
+    for (int j = 0; j < kChunk / (kThreads * 8); ++j) {
+        const int i = begin + (j * kThreads + (int)threadIdx.x) * 8;
+        if (i < end) m = max(m, max_bf16_mag(*reinterpret_cast<const u32x4*>(src + i)));
+    }
+    m = block_max_u32(m, red);
+    if (threadIdx.x == 0) partial[(size_t)slab * nch + chunk] = m;
+}
+
 // blockIdx.y = slab (Q heads first, then K heads); blockIdx.x = chunk.
 __global__ __launch_bounds__(kThreads) void amax_kernel(const uint16_t* __restrict__ q,
                                                         const uint16_t* __restrict__ k,
                                                         uint32_t* __restrict__ partial,
                                                         int n_q_slabs, int slab_len, int nch) {
     __shared__ uint32_t red[kThreads / 64];
-    const int slab = blockIdx.y;
-    const uint16_t* src = slab < n_q_slabs ? q + (size_t)slab * slab_len
-                                           : k + (size_t)(slab - n_q_slabs) * slab_len;
-    const int begin = blockIdx.x * kChunk;
-    const int end = min(begin + kChunk, slab_len);
-    uint32_t m = 0;
-    for (int i = begin + threadIdx.x * 8; i < end; i += kThreads * 8)
-        m = max(m, max_bf16_mag(*reinterpret_cast<const u32x4*>(src + i)));
-    m = block_max_u32(m, red);
-    if (threadIdx.x == 0) partial[(size_t)slab * nch + blockIdx.x] = m;
+    amax_block(q, k, partial, n_q_slabs, slab_len, nch, blockIdx.y, blockIdx.x, red);
 }
 
-// blockIdx.y = slab, blockIdx.x = output chunk.  Output slabs have rows_out
-// rows of D codes; rows >= S are written as zero.  With q8 null the Q slabs
-// only get their scale and inverse scale (the attention kernel quantises Q
-// rows itself, with the same arithmetic).
+// One block per (slab, output chunk), slab-major: Q slabs first with
+// q_chunks blocks each, then K slabs with k_chunks each.  Output slabs have
+// rows_out rows of D codes; rows >= S are written as zero.  With q8 null
+// (q_chunks = 1) the Q slabs only get their scale and inverse scale (the
+// attention kernel quantises Q rows itself, with the same arithmetic).
 __global__ __launch_bounds__(kThreads) void quantize_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint32_t* __restrict__ partial, float* __restrict__ q_scale, float* __restrict__ k_scale,
     float* __restrict__ q_inv, uint8_t* __restrict__ q8, uint8_t* __restrict__ k8, int n_q_slabs,
-    int S, int D, int nch, int rows_out) {
+    int S, int D, int nch, int rows_out, int q_chunks, int k_chunks) {
     __shared__ uint32_t red[kThreads / 64];
-    const int slab = blockIdx.y;
-    const bool is_q = slab < n_q_slabs;
-    if (is_q && q8 == nullptr && blockIdx.x != 0) return;
+    const int n_qb = n_q_slabs * q_chunks;
+    const int bid = blockIdx.x;
+    const bool is_q = bid < n_qb;
+    const int slab = is_q ? bid / q_chunks : n_q_slabs + (bid - n_qb) / k_chunks;
+    const int chunk = is_q ? bid % q_chunks : (bid - n_qb) % k_chunks;
     const int hs = is_q ? slab : slab - n_q_slabs;
     const uint16_t* src = (is_q ? q : k) + (size_t)hs * S * D;
     uint8_t* dst = (is_q ? q8 : k8) + (size_t)hs * rows_out * D;
@@ -88,7 +102,7 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(
         scale = (float)((double)amax / 448.0);
         inv = (float)(448.0 / (double)amax);
     }
-    if (blockIdx.x == 0 && threadIdx.x == 0) {
+    if (chunk == 0 && threadIdx.x == 0) {
         (is_q ? q_scale : k_scale)[hs] = scale;
         if (is_q && q_inv) q_inv[hs] = inv;
     }
@@ -96,7 +110,7 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(
 
     const int in_len = S * D;
     const int out_len = rows_out * D;
-    const int begin = blockIdx.x * kChunk;
+    const int begin = chunk * kChunk;
     const int end = min(begin + kChunk, out_len);
     for (int i = begin + threadIdx.x * 8; i < end; i += kThreads * 8) {
         u32x2 o = {0u, 0u};
@@ -115,17 +129,16 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(
     }
 }
 
-// One block per (tile, batch*kv head): V[64 keys][D] -> vt[D][64 positions].
+template <int D>
+constexpr int kTrStride = D + 8;   // bf16 per LDS row of the transpose tile
+
+// One block per (tile t, batch*kv head bh): V[64 keys][D] -> vt[D][64 positions].
 // Within each 32-key half, key 16*hi + 4*g + i goes to position 8*g + 4*hi + i:
 // lane group g of the P.V operand then reads 8 consecutive positions.
 template <int D>
-__global__ __launch_bounds__(kThreads) void transpose_v_kernel(const uint16_t* __restrict__ v,
-                                                               uint16_t* __restrict__ vt, int S,
-                                                               int nT) {
-    constexpr int kStride = D + 8;   // bf16 per LDS row
-    __shared__ uint16_t tile[kTileKeys * kStride];
-    const int t = blockIdx.x;
-    const int bh = blockIdx.y;
+__device__ __forceinline__ void transpose_v_block(const uint16_t* __restrict__ v, uint16_t* __restrict__ vt,
+                                                  int S, int nT, int t, int bh, uint16_t* tile) {
+    constexpr int kStride = kTrStride<D>;
     constexpr int kChunksPerRow = D / 8;
 #pragma unroll
     for (int it = 0; it < kTileKeys * kChunksPerRow / kThreads; ++it) {
@@ -157,6 +170,25 @@ __global__ __launch_bounds__(kThreads) void transpose_v_kernel(const uint16_t* _
     }
 }
 
+// The amax partial maxima of Q and K and the V transpose in one launch: blocks
+// [0, n_amax) reduce chunk b % nch of slab b / nch, the rest transpose tile
+// (b - n_amax) % nT of head (b - n_amax) / nT.  The two roles share nothing.
+template <int D>
+__global__ __launch_bounds__(kThreads) void amax_transpose_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, uint32_t* __restrict__ partial,
+    int n_q_slabs, int slab_len, int nch, int n_amax, const uint16_t* __restrict__ v,
+    uint16_t* __restrict__ vt, int S, int nT) {
+    __shared__ uint32_t red[kThreads / 64];
+    __shared__ uint16_t tile[kTileKeys * kTrStride<D>];
+    const int bid = blockIdx.x;
+    if (bid < n_amax) {
+        amax_block(q, k, partial, n_q_slabs, slab_len, nch, bid / nch, bid % nch, red);
+        return;
+    }
+    const int tb = bid - n_amax;
+    transpose_v_block<D>(v, vt, S, nT, tb % nT, tb / nT, tile);
+}
+
 __global__ void debug_convert_kernel(const float* __restrict__ x, int64_t n, uint8_t* e4m3,
                                      uint16_t* e4m3_bf16, uint16_t* bf16, float* exp2) {
     for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n;
@@ -174,6 +206,19 @@ __global__ void debug_convert_kernel(const float* __restrict__ x, int64_t n, uin
 
 int amax_chunks(int S, int D) { return (S * D + kChunk - 1) / kChunk; }
 
+hipError_t launch_quantize_codes(const Shape& sh, const uint16_t* q, const uint16_t* k,
+                                 const uint32_t* partial, float* q_scale, float* k_scale, float* q_inv,
+                                 uint8_t* q8, uint8_t* k8, int rows_out, hipStream_t st) {
+    const int nq = sh.B * sh.Hq, nk = sh.B * sh.Hkv;
+    const int nch = amax_chunks(sh.S, sh.D);
+    const int nch_out = (rows_out * sh.D + kChunk - 1) / kChunk;
+    const int q_chunks = q8 ? nch_out : 1;
+    hipLaunchKernelGGL(quantize_kernel, dim3(nq * q_chunks + nk * nch_out), dim3(kThreads), 0, st, q, k,
+                       partial, q_scale, k_scale, q_inv, q8, k8, nq, sh.S, sh.D, nch, rows_out, q_chunks,
+                       nch_out);
+    return hipGetLastError();
+}
+
 hipError_t launch_quantize(const Shape& sh, const uint16_t* q, const uint16_t* k,
                            uint32_t* partial, float* q_scale, float* k_scale, float* q_inv,
                            uint8_t* q8, uint8_t* k8, int rows_out, hipStream_t st) {
@@ -183,20 +228,25 @@ hipError_t launch_quantize(const Shape& sh, const uint16_t* q, const uint16_t* k
                        sh.S * sh.D, nch);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const int nch_out = (rows_out * sh.D + kChunk - 1) / kChunk;
-    hipLaunchKernelGGL(quantize_kernel, dim3(nch_out, nq + nk), dim3(kThreads), 0, st, q, k,
-                       partial, q_scale, k_scale, q_inv, q8, k8, nq, sh.S, sh.D, nch, rows_out);
-    return hipGetLastError();
+    return launch_quantize_codes(sh, q, k, partial, q_scale, k_scale, q_inv, q8, k8, rows_out, st);
 }
 
-hipError_t launch_transpose_v(const Shape& sh, const uint16_t* v, uint16_t* vt, hipStream_t st) {
-    const dim3 grid(sh.nT, sh.B * sh.Hkv);
+hipError_t launch_amax_transpose(const Shape& sh, const uint16_t* q, const uint16_t* k,
+                                 uint32_t* partial, const uint16_t* v, uint16_t* vt, hipStream_t st) {
+    const int nq = sh.B * sh.Hq, nk = sh.B * sh.Hkv;
+    const int nch = amax_chunks(sh.S, sh.D);
+    const int n_amax = nch * (nq + nk);
+    const int n_blocks = n_amax + sh.nT * sh.B * sh.Hkv;
+    const int slab_len = sh.S * sh.D;
     if (sh.D == 64)
-        hipLaunchKernelGGL(transpose_v_kernel<64>, grid, dim3(kThreads), 0, st, v, vt, sh.S, sh.nT);
+        hipLaunchKernelGGL(amax_transpose_kernel<64>, dim3(n_blocks), dim3(kThreads), 0, st, q, k, partial,
+                           nq, slab_len, nch, n_amax, v, vt, sh.S, sh.nT);
     else if (sh.D == 128)
-        hipLaunchKernelGGL(transpose_v_kernel<128>, grid, dim3(kThreads), 0, st, v, vt, sh.S, sh.nT);
+        hipLaunchKernelGGL(amax_transpose_kernel<128>, dim3(n_blocks), dim3(kThreads), 0, st, q, k, partial,
+                           nq, slab_len, nch, n_amax, v, vt, sh.S, sh.nT);
     else
-        hipLaunchKernelGGL(transpose_v_kernel<256>, grid, dim3(kThreads), 0, st, v, vt, sh.S, sh.nT);
+        hipLaunchKernelGGL(amax_transpose_kernel<256>, dim3(n_blocks), dim3(kThreads), 0, st, q, k, partial,
+                           nq, slab_len, nch, n_amax, v, vt, sh.S, sh.nT);
     return hipGetLastError();
 }
 
