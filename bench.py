@@ -3,6 +3,7 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload qwen3-8b]
                     [--delta D] [--tau T] [--no-cpu-baseline]
     python bench.py --copy-calibrate      # plain 1 GiB device copy (counter calibration)
+    python bench.py --grid [--workload W] # speed/recompute curve over (delta, tau)
 
 A step is one lamp_attn_fwd call (quantisation pass, V transpose and the fused
 attention kernel) over one batch of seeded synthetic input already resident
@@ -122,6 +123,73 @@ def cpu_baseline(q, k, v, cfg, delta, tau, budget_s, cores):
                 wall_s=wall)
 
 
+# The (delta, tau) grid of the pages' tables and figures, plus the two
+# endpoints of the method: tau = +inf (no 16-bit recompute: the pure 8-bit
+# Q.K^T path) and delta = tau = 0 (every visible sub-block recomputed in 16 bit).
+GRID_DELTAS = (0.0, 2.0 ** -8, 2.0 ** -4)
+GRID_TAUS = tuple(2.0 ** -i for i in range(6))
+GRID_ENDPOINTS = ((2.0 ** -8, float("inf"), "8-bit Q.K^T only"), (0.0, 0.0, "all sub-blocks 16-bit"))
+
+
+def measure(lamp, torch, tensors, shape, causal, window, delta, tau, steps, warmup):
+    """Time `steps` calls of lamp_attn_fwd after `warmup` untimed ones; returns
+    the step time, the attention kernel time (HIP events on its stream), the
+    algorithmic FLOP counts and the sub-block statistics of the last call."""
+    qd, kd, vd, out, mask = tensors
+    B, Hq, Hkv, S, D = shape
+
+    def step():
+        lamp.lamp_attn_fwd(qd, kd, vd, out, causal, window, delta, tau, mask)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    lamp.lamp_set_timing(1)
+    lamp.lamp_read_timing()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for _ in range(steps):
+        step()
+    end.record()
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(end)
+    prep_ms, attn_ms, ncalls = lamp.lamp_read_timing()
+    lamp.lamp_set_timing(0)
+    stats = lamp.subblock_stats(mask, S, causal, window)
+    pairs = visible_pairs_per_head(S, causal, window) * B * Hq
+    assert pairs == stats["visible_entries"], (pairs, stats["visible_entries"])
+    f_qk8 = 2.0 * D * pairs
+    f_pv = 2.0 * D * pairs
+    f_qk16 = 2.0 * D * stats["flagged_entries"]
+    return dict(ms_per_step=total_ms / steps, attn_ms=attn_ms / max(ncalls, 1),
+                prep_ms=prep_ms / max(ncalls, 1), pairs=pairs, f_nom=4.0 * D * pairs,
+                f_qk8=f_qk8, f_pv=f_pv, f_qk16=f_qk16, stats=stats)
+
+
+def roofline_of(m):
+    """Blended matrix-core roofline of the attention kernel for one measurement."""
+    f_alg = m["f_qk8"] + m["f_pv"] + m["f_qk16"]
+    t_mfma = m["f_qk8"] / PEAK_FP8 + (m["f_pv"] + m["f_qk16"]) / PEAK_BF16
+    peak = f_alg / t_mfma
+    achieved = f_alg / (m["attn_ms"] * 1e-3)
+    return achieved, peak
+
+
+def run_grid(args, lamp, torch, tensors, shape, causal, window, cfg):
+    """One JSON line per (delta, tau) of the grid and per endpoint."""
+    runs = [(d, t, "") for d in GRID_DELTAS for t in GRID_TAUS] + list(GRID_ENDPOINTS)
+    for delta, tau, note in runs:
+        m = measure(lamp, torch, tensors, shape, causal, window, delta, tau, args.steps, args.warmup)
+        achieved, peak = roofline_of(m)
+        print(json.dumps({
+            "grid": args.workload, "delta": delta, "tau": tau if tau != float("inf") else "inf",
+            "note": note, "ms_per_step": m["ms_per_step"], "attention_ms": m["attn_ms"],
+            "nominal_tflops": m["f_nom"] / (m["ms_per_step"] * 1e-3) / 1e12,
+            "roofline_frac": achieved / peak, "r_sb": m["stats"]["r_sb"], "r_e": m["stats"]["r_e"],
+            "workload": cfg["desc"]}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -133,6 +201,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--copy-calibrate", action="store_true")
+    ap.add_argument("--grid", action="store_true",
+                    help="time the (delta, tau) grid and the two endpoints instead of one point")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
@@ -152,7 +222,7 @@ def main():
     # The CPU baseline runs first, in worker processes forked before this
     # process touches the GPU.
     cb = None
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and not args.grid:
         cores = max(1, min(len(os.sched_getaffinity(0)), 16))
         cb = cpu_baseline(q, k, v, cfg, args.delta, args.tau, args.cpu_budget, cores)
         cb.pop("wall_s", None)
@@ -169,42 +239,20 @@ def main():
     out = torch.empty((B, Hq, S, D), dtype=torch.float32, device=dev)
     mask = torch.empty((B, Hq, nT, nT), dtype=torch.uint8, device=dev)
 
-    def step():
-        lamp.lamp_attn_fwd(qd, kd, vd, out, causal, window, args.delta, args.tau, mask)
-
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    lamp.lamp_set_timing(1)
-    lamp.lamp_read_timing()
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    start.record()
-    for _ in range(args.steps):
-        step()
-    end.record()
-    torch.cuda.synchronize()
-    total_ms = start.elapsed_time(end)
-    prep_ms, attn_ms, ncalls = lamp.lamp_read_timing()
-    lamp.lamp_set_timing(0)
-    ms_per_step = total_ms / args.steps
-    attn_ms_avg = attn_ms / max(ncalls, 1)
-    prep_ms_avg = prep_ms / max(ncalls, 1)
-
-    stats = lamp.subblock_stats(mask, S, causal, window)
-    pairs = visible_pairs_per_head(S, causal, window) * B * Hq
-    assert pairs == stats["visible_entries"], (pairs, stats["visible_entries"])
-    f_nom = 4.0 * D * pairs
-    f_qk8 = 2.0 * D * pairs
-    f_pv = 2.0 * D * pairs
-    f_qk16 = 2.0 * D * stats["flagged_entries"]
-    f_alg = f_qk8 + f_pv + f_qk16
-    t_mfma = f_qk8 / PEAK_FP8 + (f_pv + f_qk16) / PEAK_BF16
-    blended_peak = f_alg / t_mfma
+    tensors = (qd, kd, vd, out, mask)
+    shape = (B, Hq, Hkv, S, D)
+    if args.grid:
+        run_grid(args, lamp, torch, tensors, shape, causal, window, cfg)
+        return
+    m = measure(lamp, torch, tensors, shape, causal, window, args.delta, args.tau, args.steps,
+                args.warmup)
+    ms_per_step, attn_ms_avg, prep_ms_avg = m["ms_per_step"], m["attn_ms"], m["prep_ms"]
+    stats, f_nom = m["stats"], m["f_nom"]
+    achieved, blended_peak = roofline_of(m)
     nq, nk = B * Hq * S * D, B * Hkv * S * D
     quant_bytes = 3.0 * (nq + nk)
+    t_mfma = m["f_qk8"] / PEAK_FP8 + (m["f_pv"] + m["f_qk16"]) / PEAK_BF16
     t_roof = t_mfma + quant_bytes / PEAK_HBM
-    achieved = f_alg / (attn_ms_avg * 1e-3)
     traffic = None
     if (TRAFFIC is not None and TRAFFIC["kernel_hash"] == kernel_source_hash()
             and TRAFFIC["workload"] == args.workload and TRAFFIC["delta"] == args.delta

@@ -466,7 +466,8 @@ __global__ __launch_bounds__(kThreads, 1) void lamp_attn_kernel(AttnArgs a) {
     // sensitive entry of this row iff its maximum does: one compare per (lane,
     // sub-block).  Rows with a1 <= -a2 (a very negative running max) fall back
     // to a per-entry test for the wave.
-    auto test = [&](const v4f (&s)[kQG][4], bool masked) __attribute__((always_inline)) -> uint32_t {
+    auto test = [&](const v4f (&s)[kQG][4], auto masked_tag) __attribute__((always_inline)) -> uint32_t {
+        constexpr bool kMasked = decltype(masked_tag)::value;
         uint64_t hit[4] = {0, 0, 0, 0};
         if constexpr (kMode == 1) {
             bool slow = false;
@@ -487,11 +488,13 @@ __global__ __launch_bounds__(kThreads, 1) void lamp_attn_kernel(AttnArgs a) {
                     for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
                         for (int i = 0; i < 4; ++i) {
+                            // each ballot of a compare is that compare's lane
+                            // mask; the masks combine in scalar registers
                             const float v = s[qg][kb][i];
-                            bool sens = __builtin_fmaf(v, c8, -m_use[qg]) >= a.x_delta;
-                            sens = sens && __builtin_fabsf(v) >= a2;
-                            if (masked) sens = sens && ((vis[qg] >> (kb * 4 + i)) & 1u);
-                            hit[kb] |= wave_ballot(sens);
+                            uint64_t h = wave_ballot(__builtin_fmaf(v, c8, -m_use[qg]) >= a.x_delta) &
+                                         wave_ballot(__builtin_fabsf(v) >= a2);
+                            if constexpr (kMasked) h &= wave_ballot((vis[qg] >> (kb * 4 + i)) & 1u);
+                            hit[kb] |= h;
                         }
             }
         } else if constexpr (kMode == 2) {
@@ -615,7 +618,8 @@ __global__ __launch_bounds__(kThreads, 1) void lamp_attn_kernel(AttnArgs a) {
             if (full) softmax(S, P, t, std::integral_constant<bool, false>{});
             else softmax(S, P, t, std::integral_constant<bool, true>{});
             rescale();
-            flags = test(S, !full);
+            flags = full ? test(S, std::integral_constant<bool, false>{})
+                         : test(S, std::integral_constant<bool, true>{});
         }
         if (lane == 0) flag_lds[wave] = flags;
         lds_barrier();
@@ -678,7 +682,10 @@ __global__ __launch_bounds__(kThreads, 1) void lamp_attn_kernel(AttnArgs a) {
         load_k8(t + 2);
         load_k16(t + 1);
         load_vt(t);
-        uint32_t flags = w_cur ? test(S, !full) : 0u;
+        uint32_t flags = 0u;
+        if (w_cur)
+            flags = full ? test(S, std::integral_constant<bool, false>{})
+                         : test(S, std::integral_constant<bool, true>{});
         // the waves of a 64-row block OR their flags
         if (lane == 0) flag_lds[wave] = flags;
         lds_barrier();
