@@ -129,17 +129,22 @@ def cpu_baseline(q, k, v, cfg, delta, tau, budget_s, cores):
 GRID_DELTAS = (0.0, 2.0 ** -8, 2.0 ** -4)
 GRID_TAUS = tuple(2.0 ** -i for i in range(6))
 GRID_ENDPOINTS = ((2.0 ** -8, float("inf"), "8-bit Q.K^T only"), (0.0, 0.0, "all sub-blocks 16-bit"))
+PLAIN_NOTE = "plain bf16 FlashAttention (no 8-bit pass)"
 
 
-def measure(lamp, torch, tensors, shape, causal, window, delta, tau, steps, warmup):
-    """Time `steps` calls of lamp_attn_fwd after `warmup` untimed ones; returns
-    the step time, the attention kernel time (HIP events on its stream), the
-    algorithmic FLOP counts and the sub-block statistics of the last call."""
+def measure(lamp, torch, tensors, shape, causal, window, delta, tau, steps, warmup, plain=False):
+    """Time `steps` calls of lamp_attn_fwd (lamp_attn_fwd_bf16 when plain)
+    after `warmup` untimed ones; returns the step time, the attention kernel
+    time (HIP events on its stream), the algorithmic FLOP counts and the
+    sub-block statistics of the last call."""
     qd, kd, vd, out, mask = tensors
     B, Hq, Hkv, S, D = shape
 
     def step():
-        lamp.lamp_attn_fwd(qd, kd, vd, out, causal, window, delta, tau, mask)
+        if plain:
+            lamp.lamp_attn_fwd_bf16(qd, kd, vd, out, causal, window, mask)
+        else:
+            lamp.lamp_attn_fwd(qd, kd, vd, out, causal, window, delta, tau, mask)
 
     for _ in range(warmup):
         step()
@@ -159,7 +164,7 @@ def measure(lamp, torch, tensors, shape, causal, window, delta, tau, steps, warm
     stats = lamp.subblock_stats(mask, S, causal, window)
     pairs = visible_pairs_per_head(S, causal, window) * B * Hq
     assert pairs == stats["visible_entries"], (pairs, stats["visible_entries"])
-    f_qk8 = 2.0 * D * pairs
+    f_qk8 = 0.0 if plain else 2.0 * D * pairs
     f_pv = 2.0 * D * pairs
     f_qk16 = 2.0 * D * stats["flagged_entries"]
     return dict(ms_per_step=total_ms / steps, attn_ms=attn_ms / max(ncalls, 1),
@@ -179,8 +184,11 @@ def roofline_of(m):
 def run_grid(args, lamp, torch, tensors, shape, causal, window, cfg):
     """One JSON line per (delta, tau) of the grid and per endpoint."""
     runs = [(d, t, "") for d in GRID_DELTAS for t in GRID_TAUS] + list(GRID_ENDPOINTS)
+    if shape[4] <= 128:
+        runs.append((0.0, 0.0, PLAIN_NOTE))
     for delta, tau, note in runs:
-        m = measure(lamp, torch, tensors, shape, causal, window, delta, tau, args.steps, args.warmup)
+        m = measure(lamp, torch, tensors, shape, causal, window, delta, tau, args.steps, args.warmup,
+                    plain=note == PLAIN_NOTE)
         achieved, peak = roofline_of(m)
         print(json.dumps({
             "grid": args.workload, "delta": delta, "tau": tau if tau != float("inf") else "inf",

@@ -69,6 +69,17 @@ int lamp_attn_fwd(const void* q, const void* k, const void* v, float* out,
                   int causal, int window, float delta, float tau,
                   uint8_t* subblock_mask_out);
 
+/* The 16-bit baseline: plain bf16 FlashAttention on the same tiles ("16-bit"
+ * column of tables 1-6 read as a kernel; no 8-bit pass).  Logits are the bf16
+ * products accumulated in fp32 on the matrix cores, the running row max comes
+ * from them, exponentials are rounded to bf16, and P.V runs in bf16 with fp32
+ * accumulation.  Arguments, layout and errors as lamp_attn_fwd without delta
+ * and tau; subblock_mask_out gets 0x8F for every visited tile (all four
+ * sub-blocks in 16-bit).  D in {64, 128} (LAMP_ERR_UNSUPPORTED otherwise). */
+int lamp_attn_fwd_bf16(const void* q, const void* k, const void* v, float* out,
+                       int B, int Hq, int Hkv, int S, int D,
+                       int causal, int window, uint8_t* subblock_mask_out);
+
 /* Per-tile count of 16-bit sub-blocks, reduced on the device ("16-bit sub-blocks
  * per tile", tables 1-6).  mask is the output of lamp_attn_fwd for the same
  * B, Hq, S, causal, window.  stats_out: int64 device array of LAMP_STATS_LEN:

@@ -9,9 +9,9 @@ package only marshals torch tensors into the C entry points (see _lib.py) and
 allocates outputs.
 """
 from ._lib import (LAMP_STATS_LEN, LampError, declared_symbols, lamp_attn_fwd,  # noqa: F401
-                   lamp_debug_attn_dump, lamp_debug_convert, lamp_last_error, lamp_quantize_qk,
-                   lamp_read_timing, lamp_release_workspace, lamp_set_stream, lamp_set_timing,
-                   lamp_subblock_stats, lamp_version, load)
+                   lamp_attn_fwd_bf16, lamp_debug_attn_dump, lamp_debug_convert, lamp_last_error,
+                   lamp_quantize_qk, lamp_read_timing, lamp_release_workspace, lamp_set_stream,
+                   lamp_set_timing, lamp_subblock_stats, lamp_version, load)
 
 TILE = 64
 
@@ -30,6 +30,19 @@ def attention(q, k, v, causal=True, window=0, delta=2.0 ** -8, tau=2.0 ** -1, wi
         nT = n_tiles(S)
         mask = torch.empty((B, Hq, nT, nT), dtype=torch.uint8, device=q.device)
     lamp_attn_fwd(q, k, v, out, int(causal), int(window), delta, tau, mask)
+    return out, mask
+
+
+def attention_bf16(q, k, v, causal=True, window=0, with_mask=True):
+    """Allocate the outputs and run the plain bf16 baseline (lamp_attn_fwd_bf16)."""
+    import torch
+    B, Hq, S, D = q.shape
+    out = torch.empty((B, Hq, S, D), dtype=torch.float32, device=q.device)
+    mask = None
+    if with_mask:
+        nT = n_tiles(S)
+        mask = torch.empty((B, Hq, nT, nT), dtype=torch.uint8, device=q.device)
+    lamp_attn_fwd_bf16(q, k, v, out, int(causal), int(window), mask)
     return out, mask
 
 

@@ -41,6 +41,8 @@ def load():
     vp, i32, f32, i64 = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_int64
     lib.lamp_attn_fwd.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, f32, f32, vp]
     lib.lamp_attn_fwd.restype = i32
+    lib.lamp_attn_fwd_bf16.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, vp]
+    lib.lamp_attn_fwd_bf16.restype = i32
     lib.lamp_debug_attn_dump.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, f32, f32,
                                          vp, vp, vp]
     lib.lamp_debug_attn_dump.restype = i32
@@ -125,6 +127,16 @@ def lamp_attn_fwd(q, k, v, out, causal=1, window=0, delta=2.0 ** -8, tau=2.0 ** 
     _check(lib.lamp_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, Hq, Hkv, S, D,
                              int(causal), int(window), float(delta), float(tau),
                              _ptr(subblock_mask_out)))
+
+
+def lamp_attn_fwd_bf16(q, k, v, out, causal=1, window=0, subblock_mask_out=None):
+    """The plain bf16 FlashAttention baseline; arguments as lamp_attn_fwd."""
+    lib = load()
+    B, Hq, S, D = q.shape
+    Hkv = k.shape[1]
+    _sync_stream(lib)
+    _check(lib.lamp_attn_fwd_bf16(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, Hq, Hkv, S, D,
+                                  int(causal), int(window), _ptr(subblock_mask_out)))
 
 
 def lamp_debug_attn_dump(q, k, v, out, causal, window, delta, tau, subblock_mask_out,

@@ -81,7 +81,7 @@ struct AttnArgs {
     int n_wg;
 };
 
-template <int D>
+template <int D, bool kPlain = false>
 struct Cfg {
     // a wave owns 32 query rows (16 for D = 256, whose output accumulator is
     // twice as wide); 2 (or 4) waves form one 64-row block
@@ -96,24 +96,32 @@ struct Cfg {
     static constexpr int kK8Bytes = kTileKeys * kK8Row;
     static constexpr int kK16Bytes = kTileKeys * kK16Row;
     static constexpr int kVtBytes = D * kVtRow;
-    static constexpr int kQ16Bytes = kWaveRows * kK16Row;      // per wave
     static constexpr int kQ8Bytes = kWaveRows * kK8Row;        // per wave
     // ping-pong schedule (two K16 and V^T slots) where the slots fit in LDS
     static constexpr bool kPP = D <= 128;
     static constexpr int kSlots16 = kPP ? 2 : 1;
+    // The tiles Q.K^T reads: K8, or K16 in the plain bf16 mode (which then
+    // needs no separate K16 slots and no Q8 rows).
+    static constexpr int kQKRow = kPlain ? kK16Row : kK8Row;
+    static constexpr int kQKBytes = kTileKeys * kQKRow;
     static constexpr int kK8Off = 0;                            // two slots
-    static constexpr int kK16Off = 2 * kK8Bytes;
-    static constexpr int kVtOff = kK16Off + kSlots16 * kK16Bytes;
+    static constexpr int kK16Off = 2 * kQKBytes;
+    static constexpr int kVtOff = kK16Off + (kPlain ? 0 : kSlots16 * kK16Bytes);
     static constexpr int kQ8Off = kVtOff + kSlots16 * kVtBytes;
-    static constexpr int kLdsBytes = kQ8Off + kWaves * kQ8Bytes;
+    static constexpr int kLdsBytes = kQ8Off + (kPlain ? 0 : kWaves * kQ8Bytes);
     static constexpr int kDB = D / 16;        // 16-wide output column blocks
     static constexpr int kDC = D / 32;        // 32-deep bf16 matrix-core steps
 };
 
-// kMode: 0 = no test (second stage off), 1 = both stages, 2 = second stage only.
+// kMode: 0 = no test (second stage off), 1 = both stages, 2 = second stage
+// only, 3 = plain bf16 FlashAttention (the 16-bit baseline: no 8-bit pass,
+// Q.K^T of every sub-block on the bf16 matrix cores, exponentials rounded to
+// bf16; ping-pong schedule only).
 template <int D, bool kDump, int kMode>
 __global__ __launch_bounds__(kThreads, 1) void lamp_attn_kernel(AttnArgs a) {
-    using C = Cfg<D>;
+    constexpr bool kPlain = kMode == 3;
+    using C = Cfg<D, kPlain>;
+    static_assert(!kPlain || C::kPP, "the plain bf16 mode runs on the ping-pong schedule");
     constexpr int kQG = C::kQG;
     constexpr int kWaveRows = C::kWaveRows;
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
@@ -165,7 +173,7 @@ __global__ __launch_bounds__(kThreads, 1) void lamp_attn_kernel(AttnArgs a) {
     // the last one reloads the last one (its stores fill slots that no later
     // phase reads), which keeps every load consumed by a store on every path
     // and so keeps the compiler from waiting on loads at the loop head.
-    constexpr int kK8Ch = C::kK8Bytes / 16 / kThreads;     // chunks per thread and tile
+    constexpr int kK8Ch = C::kQKBytes / 16 / kThreads;     // chunks per thread and tile
     constexpr int kK16Ch = C::kK16Bytes / 16 / kThreads;
     constexpr int kVtCh = C::kVtBytes / 16 / kThreads;
     static_assert(kK16Ch >= 1 && kVtCh >= 1, "tile smaller than one chunk per thread");
@@ -173,25 +181,36 @@ __global__ __launch_bounds__(kThreads, 1) void lamp_attn_kernel(AttnArgs a) {
     u32x4 st_k8[kK8ChMin], st_k16[kK16Ch], st_vt[kVtCh];
     // Global addresses are a wave-uniform tile base plus an unsigned 32-bit
     // per-thread byte offset (scalar base + vector offset addressing).
+    const uint8_t* k16_head = reinterpret_cast<const uint8_t*>(a.k16 + kv_head * a.S * D);
     auto load_k8 = [&](int t) __attribute__((always_inline)) {
-        const uint8_t* src = a.k8 + (kv_head * a.S_pad + (size_t)min(t, t_end) * kTileKeys) * D;
-        constexpr int kNC = C::kK8Row / 16;
+        constexpr int kNC = C::kQKRow / 16;
+        if constexpr (kPlain) {
+            // K16 rows; keys past the end reload the last key (masked out)
 #pragma unroll
-        for (int i = 0; i < kK8ChMin; ++i) {
-            const unsigned p = min((tid + i * kThreads) * 16, C::kK8Bytes - 16);
-            const unsigned row = p / C::kK8Row, slot = (p % C::kK8Row) >> 4;
-            st_k8[i] = *reinterpret_cast<const u32x4*>(src + (row * C::kK8Row + ((slot ^ swz<kNC>(row)) << 4)));
+            for (int i = 0; i < kK8ChMin; ++i) {
+                const unsigned p = (tid + i * kThreads) * 16;
+                const unsigned row = p / C::kQKRow, slot = (p % C::kQKRow) >> 4;
+                const unsigned key = min(min(t, t_end) * kTileKeys + (int)row, a.S - 1);
+                st_k8[i] = *reinterpret_cast<const u32x4*>(k16_head + (key * C::kQKRow + ((slot ^ swz<kNC>(row)) << 4)));
+            }
+        } else {
+            const uint8_t* src = a.k8 + (kv_head * a.S_pad + (size_t)min(t, t_end) * kTileKeys) * D;
+#pragma unroll
+            for (int i = 0; i < kK8ChMin; ++i) {
+                const unsigned p = min((tid + i * kThreads) * 16, C::kQKBytes - 16);
+                const unsigned row = p / C::kQKRow, slot = (p % C::kQKRow) >> 4;
+                st_k8[i] = *reinterpret_cast<const u32x4*>(src + (row * C::kQKRow + ((slot ^ swz<kNC>(row)) << 4)));
+            }
         }
     };
     auto store_k8 = [&](int t) __attribute__((always_inline)) {
-        uint8_t* base = lds + C::kK8Off + (t & 1) * C::kK8Bytes;
+        uint8_t* base = lds + C::kK8Off + (t & 1) * C::kQKBytes;
 #pragma unroll
         for (int i = 0; i < kK8ChMin; ++i) {
             const int p = (tid + i * kThreads) * 16;
-            if (p < C::kK8Bytes) *reinterpret_cast<u32x4*>(base + p) = st_k8[i];
+            if (p < C::kQKBytes) *reinterpret_cast<u32x4*>(base + p) = st_k8[i];
         }
     };
-    const uint8_t* k16_head = reinterpret_cast<const uint8_t*>(a.k16 + kv_head * a.S * D);
     auto load_k16 = [&](int t) __attribute__((always_inline)) {
         constexpr int kNC = C::kK16Row / 16;
 #pragma unroll
@@ -235,7 +254,7 @@ __global__ __launch_bounds__(kThreads, 1) void lamp_attn_kernel(AttnArgs a) {
 #pragma unroll
         for (int ch = 0; ch < C::kDC; ++ch) qb[ch][qg] = *reinterpret_cast<const v8bf*>(qrow + ch * 32 + g * 8);
     }
-    {
+    if constexpr (!kPlain) {
         // Q8 = E4M3(fl32(q * inv)) for this wave's rows, the arithmetic of the
         // quantisation pass; rows past the end are zero
         constexpr int kNC = C::kK8Row / 16;
@@ -267,9 +286,11 @@ __global__ __launch_bounds__(kThreads, 1) void lamp_attn_kernel(AttnArgs a) {
 #pragma unroll
     for (int qg = 0; qg < kQG; ++qg) m_run[qg] = -__builtin_inff();
     if (active) {
-        c8 = (float)((double)a.q_scale[q_head] * (double)a.k_scale[kv_head] * a.l_d);
-        a2 = acc_threshold(a.t2, c8);
-        inv_c8 = 1.0f / c8;
+        if constexpr (!kPlain) {
+            c8 = (float)((double)a.q_scale[q_head] * (double)a.k_scale[kv_head] * a.l_d);
+            a2 = acc_threshold(a.t2, c8);
+            inv_c8 = 1.0f / c8;
+        }
         if (a.mask && wib == 0) {
             uint8_t* mrow = a.mask + (q_head * a.nT + r) * a.nT;
             for (int t = lane; t < a.nT; t += 64)
@@ -293,7 +314,22 @@ __global__ __launch_bounds__(kThreads, 1) void lamp_attn_kernel(AttnArgs a) {
     // ---- matrix-core phases ---------------------------------------------------------
     // Q.K^T of tile t: s[qg][kb][i] = 8-bit accumulator of key 16kb + 4g + i, query 16qg + n16
     auto qk = [&](v4f (&s)[kQG][4], int t) __attribute__((always_inline)) {
-        const uint8_t* k8l = lds + C::kK8Off + (t & 1) * C::kK8Bytes;
+        if constexpr (kPlain) {
+            // bf16 logits of all four sub-blocks (the recompute's products)
+            const uint8_t* kl = lds + C::kK8Off + (t & 1) * C::kQKBytes;
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+#pragma unroll
+                for (int ch = 0; ch < C::kDC; ++ch) {
+                    const v8bf ka = *reinterpret_cast<const v8bf*>(kl + lds_off<C::kK16Row>(c * 16 + n16, ch * 4 + g));
+#pragma unroll
+                    for (int qg = 0; qg < kQG; ++qg)
+                        s[qg][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                            ka, qb[ch][qg], ch == 0 ? v4f{0.f, 0.f, 0.f, 0.f} : s[qg][c], 0, 0, 0);
+                }
+            return;
+        }
+        const uint8_t* k8l = lds + C::kK8Off + (t & 1) * C::kQKBytes;
 #pragma unroll
         for (int st = 0; st < C::kKS; ++st) {
             v8i qf[kQG];
@@ -419,7 +455,7 @@ __global__ __launch_bounds__(kThreads, 1) void lamp_attn_kernel(AttnArgs a) {
             float mx = __builtin_fmaxf(__builtin_fmaxf(smax[qg][0], smax[qg][1]),
                                        __builtin_fmaxf(smax[qg][2], smax[qg][3]));
             mx = max_over_lane_groups(mx);
-            const float mt = mx == kNegInf ? mx : mx * c8;
+            const float mt = mx == kNegInf ? mx : mx * (kPlain ? c16 : c8);
             const float mn = __builtin_fmaxf(m_run[qg], mt);
             alpha[qg] = mn == m_run[qg] ? 1.0f : fast_exp2(m_run[qg] - mn);
             m_use[qg] = mn == kNegInf ? 0.0f : mn;
@@ -433,15 +469,19 @@ __global__ __launch_bounds__(kThreads, 1) void lamp_attn_kernel(AttnArgs a) {
                 float e[4];
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    e[i] = fast_exp2(__builtin_fmaf(s[qg][kb][i], c8, -m_use[qg]));
+                    e[i] = fast_exp2(__builtin_fmaf(s[qg][kb][i], kPlain ? c16 : c8, -m_use[qg]));
                     if constexpr (kMasked) e[i] = ((vis[qg] >> (kb * 4 + i)) & 1u) ? e[i] : 0.0f;
                 }
-                // the high half of the first conversion's destination is
-                // overwritten by the second: any dead register serves as its
-                // initial value (a zero would cost a move per conversion)
-                const uint32_t w = cvt_pk_e4m3_unit<true>(
-                    e[2], e[3], cvt_pk_e4m3_unit<false>(e[0], e[1], __float_as_uint(e[0])));
-                P[qg][kb] = u32x2{e4m3x2_to_bf16x2<false>(w), e4m3x2_to_bf16x2<true>(w)};
+                if constexpr (kPlain) {
+                    P[qg][kb] = u32x2{f32x2_to_bf16x2(e[0], e[1]), f32x2_to_bf16x2(e[2], e[3])};
+                } else {
+                    // the high half of the first conversion's destination is
+                    // overwritten by the second: any dead register serves as
+                    // its initial value (a zero would cost a move per conversion)
+                    const uint32_t w = cvt_pk_e4m3_unit<true>(
+                        e[2], e[3], cvt_pk_e4m3_unit<false>(e[0], e[1], __float_as_uint(e[0])));
+                    P[qg][kb] = u32x2{e4m3x2_to_bf16x2<false>(w), e4m3x2_to_bf16x2<true>(w)};
+                }
             }
         if constexpr (kDump) {
 #pragma unroll
@@ -591,19 +631,20 @@ __global__ __launch_bounds__(kThreads, 1) void lamp_attn_kernel(AttnArgs a) {
     // A workgroup barrier ends every phase.  The two groups read the K16 and
     // V^T tiles of t and the K8 tile of t+1 in two consecutive phases, M(t) of
     // each; two slots of each array then suffice, and the stores of a phase
-    // never touch a slot read in it.
+    // never touch a slot read in it.  In the plain bf16 mode the Q.K^T tiles
+    // are K16 tiles, staged like K8, and there is no test or recompute.
     const int grp = wave >> 2;
     load_k8(t_begin);
     store_k8(t_begin);
     load_k8(t_begin + 1);
-    load_k16(t_begin);
+    if constexpr (!kPlain) load_k16(t_begin);
     load_vt(t_begin);
     lds_barrier();
     if (grp == 1) lds_barrier();
     // M(t_begin - 1): the first Q.K^T and the stores for tile t_begin
     if (work(t_begin)) qk(S, t_begin);
     store_k8(t_begin + 1);
-    store_k16(t_begin & 1);
+    if constexpr (!kPlain) store_k16(t_begin & 1);
     store_vt(t_begin & 1);
     lds_barrier();
     for (int t = t_begin; t <= t_end; ++t) {
@@ -611,15 +652,16 @@ __global__ __launch_bounds__(kThreads, 1) void lamp_attn_kernel(AttnArgs a) {
         const bool full = tile_full(r, t, a.S, a.causal, a.window);
         // ---- V(t)
         load_k8(t + 2);
-        load_k16(t + 1);
+        if constexpr (!kPlain) load_k16(t + 1);
         load_vt(t + 1);
         uint32_t flags = 0;
         if (w_cur) {
             if (full) softmax(S, P, t, std::integral_constant<bool, false>{});
             else softmax(S, P, t, std::integral_constant<bool, true>{});
             rescale();
-            flags = full ? test(S, std::integral_constant<bool, false>{})
-                         : test(S, std::integral_constant<bool, true>{});
+            if constexpr (!kPlain)
+                flags = full ? test(S, std::integral_constant<bool, false>{})
+                             : test(S, std::integral_constant<bool, true>{});
         }
         if (lane == 0) flag_lds[wave] = flags;
         lds_barrier();
@@ -632,10 +674,12 @@ __global__ __launch_bounds__(kThreads, 1) void lamp_attn_kernel(AttnArgs a) {
         flags = __builtin_amdgcn_readfirstlane(flags);
         // the loads of V(t) have arrived; storing them first frees their registers
         store_k8(t + 2);
-        store_k16((t + 1) & 1);
+        if constexpr (!kPlain) store_k16((t + 1) & 1);
         store_vt((t + 1) & 1);
         if (w_cur) {
-            if (flags != 0) {
+            if constexpr (kPlain) {
+                flags = 0xFu;   // every sub-block in 16-bit
+            } else if (flags != 0) {
                 if (full) recompute(P, flags, std::integral_constant<bool, false>{}, t);
                 else recompute(P, flags, std::integral_constant<bool, true>{}, t);
             }
@@ -751,13 +795,21 @@ hipError_t launch_d(const Shape& sh, const AttnParams& p, hipStream_t st) {
     a.rows_per_wg = Cfg<D>::kBlocks / a.heads_per_wg;
     a.n_rg = (sh.nT + a.rows_per_wg - 1) / a.rows_per_wg;
     a.n_wg = sh.B * sh.Hkv * (a.G / a.heads_per_wg) * a.n_rg;
-    const size_t lds = Cfg<D>::kLdsBytes;
+    size_t lds = Cfg<D>::kLdsBytes;
     const bool dump = p.dump_s != nullptr && p.dump_p != nullptr;
     using Fn = void (*)(AttnArgs);
     static const Fn table[2][3] = {
         {lamp_attn_kernel<D, false, 0>, lamp_attn_kernel<D, false, 1>, lamp_attn_kernel<D, false, 2>},
         {lamp_attn_kernel<D, true, 0>, lamp_attn_kernel<D, true, 1>, lamp_attn_kernel<D, true, 2>}};
-    const Fn fn = table[dump ? 1 : 0][a.test_mode];
+    Fn fn = table[dump ? 1 : 0][a.test_mode];
+    if (p.plain) {
+        if constexpr (Cfg<D>::kPP) {
+            fn = dump ? lamp_attn_kernel<D, true, 3> : lamp_attn_kernel<D, false, 3>;
+            lds = Cfg<D, true>::kLdsBytes;
+        } else {
+            return hipErrorInvalidValue;
+        }
+    }
     hipError_t e = hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(fn, dim3(a.n_wg), dim3(kThreads), lds, st, a);

@@ -26,11 +26,13 @@ hipError_t launch_quantize(const Shape& sh, const uint16_t* q, const uint16_t* k
                            uint32_t* partial, float* q_scale, float* k_scale, float* q_inv,
                            uint8_t* q8, uint8_t* k8, int rows_out, hipStream_t st);
 
-// The amax partial maxima of launch_quantize, and in the same launch
-// V [B, Hkv, S, D] -> vt [B, Hkv, nT, D, 64] (keys of each tile transposed and
-// permuted into the order the P.V matrix-core operand reads; padding keys 0).
+// The amax partial maxima of launch_quantize (when with_amax), and in the same
+// launch V [B, Hkv, S, D] -> vt [B, Hkv, nT, D, 64] (keys of each tile
+// transposed and permuted into the order the P.V matrix-core operand reads;
+// padding keys 0).
 hipError_t launch_amax_transpose(const Shape& sh, const uint16_t* q, const uint16_t* k,
-                                 uint32_t* partial, const uint16_t* v, uint16_t* vt, hipStream_t st);
+                                 uint32_t* partial, const uint16_t* v, uint16_t* vt, bool with_amax,
+                                 hipStream_t st);
 
 // The second half of launch_quantize: scales and codes from the partial maxima.
 hipError_t launch_quantize_codes(const Shape& sh, const uint16_t* q, const uint16_t* k,
@@ -53,6 +55,7 @@ struct AttnParams {
     float e_delta;          // smallest fp32 exponential that rounds to an e4m3 value >= delta
     float t2;               // second-stage threshold on |log2-domain logit|
     int causal, window;
+    int plain = 0;          // 1: plain bf16 FlashAttention (no 8-bit pass; D <= 128)
 };
 
 // The forward attention kernel (16-bit recompute inside the tile loop).

@@ -152,9 +152,10 @@ Layout workspace_layout(const lamp::Shape& sh) {
 
 }  // namespace
 
+// plain = 1: plain bf16 FlashAttention (delta and tau unused).
 static int attn_fwd_impl(const void* q, const void* k, const void* v, float* out, int B, int Hq, int Hkv,
                          int S, int D, int causal, int window, float delta, float tau,
-                         uint8_t* subblock_mask_out, float* dump_s, uint16_t* dump_p) {
+                         uint8_t* subblock_mask_out, float* dump_s, uint16_t* dump_p, int plain) {
     if (!q || !k || !v || !out) return fail(LAMP_ERR_INVALID, "q, k, v and out must be non-null");
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
         return fail(LAMP_ERR_INVALID, "q, k, v and out must be 16-byte aligned");
@@ -163,7 +164,9 @@ static int attn_fwd_impl(const void* q, const void* k, const void* v, float* out
     if (causal != 0 && causal != 1) return fail(LAMP_ERR_INVALID, "causal must be 0 or 1 (got %d)", causal);
     if (window < 0) return fail(LAMP_ERR_INVALID, "window must be >= 0 (got %d)", window);
     if (window > 0 && !causal) return fail(LAMP_ERR_INVALID, "a sliding window requires causal = 1");
-    if (std::isnan(delta) || std::isnan(tau)) return fail(LAMP_ERR_INVALID, "delta and tau must not be NaN");
+    if (!plain && (std::isnan(delta) || std::isnan(tau)))
+        return fail(LAMP_ERR_INVALID, "delta and tau must not be NaN");
+    if (plain && D > 128) return fail(LAMP_ERR_UNSUPPORTED, "the plain bf16 mode needs D <= 128 (got %d)", D);
 
     const lamp::Shape sh = make_shape(B, Hq, Hkv, S, D);
     const Layout L = workspace_layout(sh);
@@ -191,12 +194,15 @@ static int attn_fwd_impl(const void* q, const void* k, const void* v, float* out
     if (ev) (void)hipEventRecord(ev[0], g_stream);
     auto* q_inv = reinterpret_cast<float*>(base + L.q_inv);
     // amax partial maxima and the V transpose, then scales and K8 (the
-    // attention kernel quantises its Q rows itself)
-    hipError_t e = lamp::launch_amax_transpose(sh, q16, k16, partial, v16, vt, g_stream);
+    // attention kernel quantises its Q rows itself); the plain bf16 mode
+    // needs only the transpose
+    hipError_t e = lamp::launch_amax_transpose(sh, q16, k16, partial, v16, vt, !plain, g_stream);
     if (e != hipSuccess) return hip_fail(e, "amax/transpose launch");
-    e = lamp::launch_quantize_codes(sh, q16, k16, partial, q_scale, k_scale, q_inv, nullptr, k8, sh.S_pad,
-                                    g_stream);
-    if (e != hipSuccess) return hip_fail(e, "quantise launch");
+    if (!plain) {
+        e = lamp::launch_quantize_codes(sh, q16, k16, partial, q_scale, k_scale, q_inv, nullptr, k8, sh.S_pad,
+                                        g_stream);
+        if (e != hipSuccess) return hip_fail(e, "quantise launch");
+    }
     if (ev) (void)hipEventRecord(ev[1], g_stream);
 
     lamp::AttnParams p;
@@ -208,6 +214,7 @@ static int attn_fwd_impl(const void* q, const void* k, const void* v, float* out
     p.t2 = (float)(16.0 * (double)tau * kLog2e);
     p.causal = causal; p.window = window;
     p.dump_s = dump_s; p.dump_p = dump_p;
+    p.plain = plain;
     e = lamp::launch_attention(sh, p, g_stream);
     if (e != hipSuccess) return hip_fail(e, "attention launch");
     if (ev) (void)hipEventRecord(ev[2], g_stream);
@@ -220,7 +227,13 @@ int lamp_attn_fwd(const void* q, const void* k, const void* v, float* out, int B
                   int S, int D, int causal, int window, float delta, float tau,
                   uint8_t* subblock_mask_out) {
     return attn_fwd_impl(q, k, v, out, B, Hq, Hkv, S, D, causal, window, delta, tau, subblock_mask_out,
-                         nullptr, nullptr);
+                         nullptr, nullptr, 0);
+}
+
+int lamp_attn_fwd_bf16(const void* q, const void* k, const void* v, float* out, int B, int Hq, int Hkv,
+                       int S, int D, int causal, int window, uint8_t* subblock_mask_out) {
+    return attn_fwd_impl(q, k, v, out, B, Hq, Hkv, S, D, causal, window, 0.0f, 0.0f, subblock_mask_out,
+                         nullptr, nullptr, 1);
 }
 
 int lamp_debug_attn_dump(const void* q, const void* k, const void* v, float* out, int B, int Hq, int Hkv,
@@ -229,7 +242,7 @@ int lamp_debug_attn_dump(const void* q, const void* k, const void* v, float* out
     if (!acc8_out || !p_out) return fail(LAMP_ERR_INVALID, "acc8_out and p_out must be non-null");
     if (S > 2048) return fail(LAMP_ERR_UNSUPPORTED, "debug dump needs S <= 2048 (got %d)", S);
     return attn_fwd_impl(q, k, v, out, B, Hq, Hkv, S, D, causal, window, delta, tau, subblock_mask_out,
-                         acc8_out, p_out);
+                         acc8_out, p_out, 0);
 }
 
 int lamp_set_timing(int enable) {

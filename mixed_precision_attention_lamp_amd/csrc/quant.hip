@@ -232,10 +232,11 @@ hipError_t launch_quantize(const Shape& sh, const uint16_t* q, const uint16_t* k
 }
 
 hipError_t launch_amax_transpose(const Shape& sh, const uint16_t* q, const uint16_t* k,
-                                 uint32_t* partial, const uint16_t* v, uint16_t* vt, hipStream_t st) {
+                                 uint32_t* partial, const uint16_t* v, uint16_t* vt, bool with_amax,
+                                 hipStream_t st) {
     const int nq = sh.B * sh.Hq, nk = sh.B * sh.Hkv;
     const int nch = amax_chunks(sh.S, sh.D);
-    const int n_amax = nch * (nq + nk);
+    const int n_amax = with_amax ? nch * (nq + nk) : 0;
     const int n_blocks = n_amax + sh.nT * sh.B * sh.Hkv;
     const int slab_len = sh.S * sh.D;
     if (sh.D == 64)

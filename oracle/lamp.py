@@ -254,6 +254,74 @@ def run_unit(ctx, b, hq, r, flag_override=None, trace=None):
 
 
 # --------------------------------------------------------------------------
+# The 16-bit baseline: plain bf16 FlashAttention, no 8-bit pass
+# --------------------------------------------------------------------------
+def plain_unit(ctx, b, hq, r, trace=None):
+    """One 64-row query block of plain bf16 FlashAttention.
+
+    The "16-bit" baseline of tables 1-6 read as the same tiled kernel with
+    every sub-block in 16-bit and no 8-bit pass: logits are the bf16
+    products summed exactly and rounded once to fp32, s = fl32(acc * c16);
+    the running row max comes from these logits; exponentials
+    exp2(fma(acc, c16, -m)) are rounded to bf16; online-softmax rescale and
+    P.V as in ``run_unit``.  The mask byte of every visited tile is 0x8F
+    (all four sub-blocks in 16-bit).  Returns (out rows, {t: mask byte}).
+    """
+    S, D, G = ctx["S"], ctx["D"], ctx["G"]
+    hk = hq // G
+    rows = np.arange(r * BR, min(r * BR + BR, S))
+    nr = rows.size
+    c16 = float(fl32(log2_scale(D)))
+    q16 = ctx["q16"][b, hq, rows]
+    m = np.full(nr, -np.inf)
+    ell = np.zeros(nr)
+    O = np.zeros((nr, D))
+    mask = {}
+    for t in range(n_tiles(S)):
+        cols = np.arange(t * BC, min(t * BC + BC, S))
+        vis = visible(rows, cols, ctx["causal"], ctx["window"])
+        if not vis.any():
+            continue
+        acc16 = fl32(q16 @ ctx["k16"][b, hk, cols].T)
+        s16 = np.where(vis, fl32(acc16 * c16), -np.inf)
+        m_new = np.maximum(m, s16.max(axis=1))
+        live = m_new > -np.inf
+        safe_m = np.where(live, m_new, 0.0)
+        x = np.where(vis, fma32(acc16, c16, -safe_m[:, None]), -np.inf)
+        e = np.where(vis, exp2_f32(x), 0.0)
+        p = np.where(vis, round_bf16(e), 0.0)
+        alpha = np.where(np.isneginf(m), 0.0, np.exp2(m - safe_m))
+        alpha = np.where(live, alpha, 1.0)
+        ell = alpha * ell + p.sum(axis=1)
+        O = alpha[:, None] * O + p @ ctx["v"][b, hk, cols]
+        m = m_new
+        mask[t] = 0x80 | ((1 << NSB) - 1)
+        if trace is not None:
+            trace.append(dict(t=t, cols=cols, vis=vis, acc16=acc16, s16=s16, e=e, p=p,
+                              m_new=m_new.copy()))
+    out = fl32(O / ell[:, None])
+    if trace is not None:
+        trace.append(dict(final=True, m=m, ell=ell, O=O))
+    return out, mask
+
+
+def plain_forward(q_bits, k_bits, v_bits, causal=True, window=0, units=None):
+    """Plain bf16 FlashAttention over ``units`` (default: all); same return
+    convention as ``lamp_forward``."""
+    ctx = prepare(q_bits, k_bits, v_bits, causal, window, 0.0, 0.0)
+    B, Hq, S, D = ctx["B"], ctx["Hq"], ctx["S"], ctx["D"]
+    nT = n_tiles(S)
+    out = np.full((B, Hq, S, D), np.nan, dtype=np.float32)
+    mask = np.zeros((B, Hq, nT, nT), dtype=np.uint8)
+    for (b, hq, r) in (units if units is not None else all_units(B, Hq, S)):
+        o, mk = plain_unit(ctx, b, hq, r)
+        out[b, hq, r * BR:r * BR + o.shape[0]] = o.astype(np.float32)
+        for t, byte in mk.items():
+            mask[b, hq, r, t] = byte
+    return out, mask
+
+
+# --------------------------------------------------------------------------
 # Whole forward pass
 # --------------------------------------------------------------------------
 class PerHead:

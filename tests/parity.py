@@ -210,6 +210,90 @@ def compare(q, k, v, causal, window, delta, tau, units=None, gpu=None, label="")
     return rep
 
 
+# --------------------------------------------------------------------------
+# the plain bf16 baseline (lamp_attn_fwd_bf16 against oracle.lamp.plain_unit)
+# --------------------------------------------------------------------------
+def plain_flip_bound(ctx, b, h, r):
+    """Per (row, column) bound on |dO| of one unit of the plain bf16 baseline
+    from weights whose bf16 rounding can go the other way within the logit
+    window (bf16 matrix-core accumulation, one fp32 ulp, the running max) and
+    the exp2 window.  Returns (oracle rows, bound)."""
+    trace = []
+    out, _ = L.plain_unit(ctx, b, h, r, trace=trace)
+    fin = trace[-1]
+    G = ctx["G"]
+    vv = ctx["v"][b, h // G]
+    c16 = float(np.float32(L.log2_scale(ctx["D"])))
+    bound = np.zeros_like(out)
+    for rec in trace[:-1]:
+        rows = np.arange(r * 64, r * 64 + rec["vis"].shape[0])
+        vis = rec["vis"]
+        q16 = ctx["q16"][b, h, rows]
+        k16 = ctx["k16"][b, h // G, rec["cols"]]
+        maxp = np.max(np.abs(q16[:, None, :] * k16[None, :, :]), axis=2)
+        s16 = np.where(vis, rec["s16"], 0.0)
+        ds = c16 * EPS_ACC16 * maxp + np.spacing(np.abs(s16).astype(np.float32)).astype(np.float64)
+        dm = np.where(vis, ds, 0.0).max(axis=1, keepdims=True)
+        lo, hi = _e_bounds(rec["e"], ds + dm)
+        alt = np.zeros_like(rec["p"])
+        for ek in (lo, hi):
+            alt = np.maximum(alt, np.where(vis, np.abs(round_bf16(ek) - rec["p"]), 0.0))
+        scale = np.exp2(rec["m_new"] - fin["m"]) / fin["ell"]
+        vj = vv[rec["cols"]]
+        bound += np.einsum("ij,ijd->id", alt * scale[:, None], np.abs(vj[None, :, :] - out[:, None, :]))
+    return out, 1.1 * bound
+
+
+def compare_plain(q, k, v, causal, window, units=None, label=""):
+    """GPU plain bf16 baseline against the oracle: the mask bit-exact, the
+    outputs within MAX_ABS (plus the effect of weights near a bf16 rounding
+    midpoint) and MEAN_ABS.  Returns a report dict."""
+    import mixed_precision_attention_lamp_amd as lamp
+    B, Hq, S, D = q.shape
+    if units is None:
+        units = L.all_units(B, Hq, S)
+    say(f"[parity-bf16] {label} B={B} Hq={Hq} Hkv={k.shape[1]} S={S} D={D} causal={causal} "
+        f"window={window} units={len(units)}")
+    out_d, mask_d = lamp.attention_bf16(to_device(q), to_device(k), to_device(v), causal, window)
+    torch.cuda.synchronize()
+    out_g, mask_g = out_d.cpu().numpy(), mask_d.cpu().numpy()
+    ctx = L.prepare(q, k, v, causal, window, 0.0, 0.0)
+    diffs, mask_bad, unexplained, explained = [], 0, [], 0
+    for (b, h, r) in units:
+        o, mk = L.plain_unit(ctx, b, h, r)
+        nT = mask_g.shape[-1]
+        want = np.zeros(nT, dtype=np.uint8)
+        for t, byte in mk.items():
+            want[t] = byte
+        mask_bad += int((mask_g[b, h, r] != want).sum())
+        rows = slice(r * 64, r * 64 + o.shape[0])
+        d = np.abs(out_g[b, h, rows].astype(np.float64) - o.astype(np.float64))
+        diffs.append(d)
+        if (d > MAX_ABS).any():
+            _, bnd = plain_flip_bound(ctx, b, h, r)
+            for i in np.nonzero((d > MAX_ABS).any(axis=1))[0]:
+                if np.all(d[i] <= MAX_ABS + bnd[i]):
+                    explained += 1
+                else:
+                    j = int(np.argmax(d[i] - bnd[i]))
+                    unexplained.append((b, h, r * 64 + int(i), j, float(d[i, j]), float(bnd[i, j])))
+    d = np.concatenate([x.reshape(-1) for x in diffs])
+    rep = dict(max_abs=float(d.max()), mean_abs=float(d.mean()), mask_mismatches=mask_bad,
+               rows_explained=explained, rows_unexplained=unexplained,
+               finite=bool(np.isfinite(d).all()))
+    say(f"[parity-bf16] {label} max|dO|={rep['max_abs']:.3e} mean|dO|={rep['mean_abs']:.3e} "
+        f"mask mismatches {mask_bad}; rows above {MAX_ABS:g}: {explained + len(unexplained)} "
+        f"(explained by midpoint flips {explained}, unexplained {len(unexplained)})")
+    return rep
+
+
+def assert_parity_plain(rep):
+    assert rep["finite"], "non-finite outputs"
+    assert rep["mask_mismatches"] == 0
+    assert not rep["rows_unexplained"], f"rows above {MAX_ABS}: {rep['rows_unexplained'][:10]}"
+    assert rep["mean_abs"] <= MEAN_ABS, rep["mean_abs"]
+
+
 def assert_parity(rep):
     assert rep["finite"], "non-finite outputs"
     assert not rep["unexcused"], f"unexcused mask mismatches: {rep['unexcused'][:10]}"

@@ -23,7 +23,7 @@ def test_exports_every_declared_symbol(lib):
     assert {"lamp_attn_fwd", "lamp_subblock_stats", "lamp_quantize_qk", "lamp_set_stream",
             "lamp_last_error", "lamp_release_workspace", "lamp_version",
             "lamp_debug_convert", "lamp_set_timing", "lamp_read_timing",
-            "lamp_debug_attn_dump"} <= set(names)
+            "lamp_debug_attn_dump", "lamp_attn_fwd_bf16"} <= set(names)
     out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
     exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
@@ -91,3 +91,11 @@ def test_binding_raises_on_error():
         lamp.lamp_attn_fwd.__wrapped__ if hasattr(lamp.lamp_attn_fwd, "__wrapped__") else None
         _lib._check(_fwd(lamp.load(), D=96))
     assert ei.value.code == -2
+
+
+def test_bf16_baseline_rejects_before_hip(lib):
+    # D = 256 is not supported by the plain bf16 baseline; a bad size is
+    # rejected as for lamp_attn_fwd; neither touches the GPU
+    assert lib.lamp_attn_fwd_bf16(ALIGNED, ALIGNED, ALIGNED, ALIGNED, 1, 2, 1, 128, 256, 1, 0, None) == -2
+    assert "D <= 128" in lib.lamp_last_error().decode()
+    assert lib.lamp_attn_fwd_bf16(ALIGNED, ALIGNED, ALIGNED, ALIGNED, 1, 3, 2, 128, 128, 1, 0, None) == -1

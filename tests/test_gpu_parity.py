@@ -19,8 +19,8 @@ from oracle import lamp as L
 from oracle.formats import (bf16_bits_to_f64, e4m3_decode, e4m3_encode, exp2_f32, round_bf16,
                             round_e4m3)
 
-from parity import (EPS_ACC8, assert_parity, compare, fragile_alternatives, run_gpu, say,
-                    to_device)
+from parity import (EPS_ACC8, assert_parity, assert_parity_plain, compare, compare_plain,
+                    fragile_alternatives, run_gpu, say, to_device)
 
 pytestmark = pytest.mark.gpu
 
@@ -252,6 +252,41 @@ def test_forward_parity_full_size(full):
     rep = compare(q, k, v, cfg["causal"], cfg["window"], delta, tau, units=units,
                   label=f"{name} sampled")
     assert_parity(rep)
+
+
+# --------------------------------------------------------------------------
+# the plain bf16 baseline
+# --------------------------------------------------------------------------
+PLAIN = [
+    # B, Hq, Hkv, S, D, causal, window, structure, seed
+    (1, 1, 1, 256, 64, 1, 0, "sinks", 81),
+    (1, 4, 1, 300, 128, 1, 0, "channels", 82),     # G = 4, ragged tail
+    (2, 8, 2, 200, 128, 1, 0, "channels", 83),
+    (1, 3, 3, 130, 64, 0, 0, "channels", 84),      # non-causal
+    (1, 2, 2, 333, 128, 1, 100, "channels", 85),   # sliding window
+    (1, 1, 1, 1, 128, 1, 0, "plain", 86),          # S = 1
+]
+
+
+@pytest.mark.parametrize("case", PLAIN)
+def test_plain_bf16_parity_small(case):
+    B, Hq, Hkv, S, D, causal, window, st, seed = case
+    q, k, v = make_inputs(B, Hq, Hkv, S, D, seed, st)
+    assert_parity_plain(compare_plain(q, k, v, causal, window, label=str(case)))
+
+
+def test_plain_bf16_parity_full_size():
+    q, k, v, cfg = make_config_inputs("qwen3-8b")
+    units = _sample_units(cfg["B"], cfg["Hq"], cfg["S"], 10, 9)
+    assert_parity_plain(compare_plain(q, k, v, cfg["causal"], cfg["window"], units=units,
+                                      label="qwen3-8b sampled"))
+
+
+def test_plain_bf16_rejects_d256():
+    import mixed_precision_attention_lamp_amd as lamp
+    q, k, v = make_inputs(1, 1, 1, 64, 256, 87, "plain")
+    with pytest.raises(lamp.LampError):
+        lamp.attention_bf16(to_device(q), to_device(k), to_device(v), True, 0)
 
 
 # --------------------------------------------------------------------------

@@ -163,6 +163,42 @@ def test_all_sixteen_bit_is_bf16_attention(shape):
     assert np.abs(out - ex).max() <= bound
 
 
+@pytest.mark.parametrize("shape", ENDPOINT_SHAPES)
+def test_plain_bf16_is_bf16_attention(shape):
+    # the tiled 16-bit baseline against the untiled definitions: bf16 attention
+    # with the global row max, and exact attention, each within the bf16
+    # rounding of the weights
+    B, Hq, Hkv, S, D, causal, window, structure, seed = shape
+    q, k, v = make_inputs(B, Hq, Hkv, S, D, seed, structure)
+    out, mask = L.plain_forward(q, k, v, causal, window)
+    visited = mask != 0
+    assert np.all(mask[visited] == 0x8F)
+    st = L.subblock_stats(mask, S, causal, window)
+    assert st["flagged_subblocks"] == st["visited_subblocks"] > 0
+    u = 2.0 ** -8
+    bound = 4 * u / (1 - u) * _maxv(v)
+    assert np.abs(out - bf16_attention(q, k, v, causal, window)).max() <= bound
+    assert np.abs(out - exact_attention(q, k, v, causal, window)).max() <= bound
+
+
+def test_plain_bf16_special_cases():
+    # one key: the output is v0; equal keys: every weight is exactly 1 and the
+    # output is the mean of the visible values; zero queries: cumulative mean
+    q, k, v = make_inputs(1, 2, 1, 1, 64, 3, "plain")
+    out, _ = L.plain_forward(q, k, v, True, 0)
+    assert np.array_equal(out[0, :, 0], np.repeat(bf16_bits_to_f64(v)[0, :, 0], 2, axis=0))
+    S, D = 100, 64
+    q, k1, v = make_inputs(1, 1, 1, S, D, 5, "plain")
+    k = np.repeat(k1[:, :, :1], S, axis=2)
+    out, _ = L.plain_forward(q, k, v, False, 0)
+    vv = bf16_bits_to_f64(v)[0, 0]
+    np.testing.assert_allclose(out[0, 0], np.repeat(vv.mean(axis=0)[None], S, axis=0), atol=1e-6)
+    qz = np.zeros_like(q)
+    out, _ = L.plain_forward(qz, k1, v, True, 30)
+    for i in (0, 29, 30, 99):
+        np.testing.assert_allclose(out[0, 0, i], vv[max(0, i - 29):i + 1].mean(axis=0), atol=1e-6)
+
+
 def test_lamp_recovers_from_eight_bit_error():
     # the pages' claim: sending a minority of sub-blocks to 16-bit recovers
     # most of the 8-bit error (tables 1-6); on the sink workload
