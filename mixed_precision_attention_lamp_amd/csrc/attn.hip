@@ -138,16 +138,19 @@ __global__ __launch_bounds__(kThreads, 1) void lamp_attn_kernel(AttnArgs a) {
     // ---- workgroup -> (batch, kv head, head group, row-block group) ----------
     // Workgroups are dispatched in index order, round-robin over the XCDs.
     // Index order is longest (causal) rows first, so that the CUs that free
-    // first take the longest of the remaining rows; within a level of equal
-    // length the (batch, kv head, head group) units rotate by one per level,
-    // so that every XCD sees every unit (units differ in how much they
-    // recompute) rather than one unit per XCD.
+    // first take the longest of the remaining rows.  Within a level of equal
+    // length the (batch, kv head, head group) units are offset by the
+    // level's parity: an XCD then works on two units, alternately.  Units
+    // differ in how much they recompute, and one unit per XCD leaves the XCDs
+    // unevenly loaded; two share the load while the K/V tiles of a unit are
+    // fetched into two L2s only (spreading every unit over every XCD balances
+    // a little better but fetches each tile into every L2).
     const int wg = blockIdx.x;
     const int n_hg = a.G / a.heads_per_wg;
     const int n_u = a.n_wg / a.n_rg;
     const int level = wg / n_u;
     const int rg = a.n_rg - 1 - level;
-    int u = (wg % n_u + level) % n_u;
+    int u = (wg % n_u + (level & 1)) % n_u;
     const int hg = u % n_hg;
     u /= n_hg;
     const int hk = u % a.Hkv;
