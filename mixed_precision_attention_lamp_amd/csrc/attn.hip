@@ -622,146 +622,146 @@ __global__ __launch_bounds__(kThreads, 1) void lamp_attn_kernel(AttnArgs a) {
     v4f S[kQG][4];
     u32x2 P[kQG][4];
     if constexpr (C::kPP) {
-    // ---- ping-pong schedule ---------------------------------------------------------
-    // Waves 0-3 (one per SIMD) and waves 4-7 run the same sequence of phases,
-    // the second group one phase behind the first, so that on every SIMD one
-    // wave is in a vector phase while the other is in a matrix phase:
-    //   V(t): running max, exponentials, rescale and test of tile t, flags
-    //         out;
-    //   M(t): 16-bit recompute and P.V of tile t, Q.K^T of tile t+1,
-    //         and the LDS stores of K8(t+2), K16(t+1) and V^T(t+1) (loaded in
-    //         V(t)).
-    // A workgroup barrier ends every phase.  The two groups read the K16 and
-    // V^T tiles of t and the K8 tile of t+1 in two consecutive phases, M(t) of
-    // each; two slots of each array then suffice, and the stores of a phase
-    // never touch a slot read in it.  In the plain bf16 mode the Q.K^T tiles
-    // are K16 tiles, staged like K8, and there is no test or recompute.
-    const int grp = wave >> 2;
-    load_k8(t_begin);
-    store_k8(t_begin);
-    load_k8(t_begin + 1);
-    if constexpr (!kPlain) load_k16(t_begin);
-    load_vt(t_begin);
-    lds_barrier();
-    if (grp == 1) lds_barrier();
-    // M(t_begin - 1): the first Q.K^T and the stores for tile t_begin
-    if (work(t_begin)) qk(S, t_begin);
-    store_k8(t_begin + 1);
-    if constexpr (!kPlain) store_k16(t_begin & 1);
-    store_vt(t_begin & 1);
-    lds_barrier();
-    for (int t = t_begin; t <= t_end; ++t) {
-        const bool w_cur = work(t), w_next = work(t + 1);
-        const bool full = tile_full(r, t, a.S, a.causal, a.window);
-        // ---- V(t)
-        load_k8(t + 2);
-        if constexpr (!kPlain) load_k16(t + 1);
-        load_vt(t + 1);
-        uint32_t flags = 0;
-        if (w_cur) {
-            if (full) softmax(S, P, t, std::integral_constant<bool, false>{});
-            else softmax(S, P, t, std::integral_constant<bool, true>{});
-            rescale();
-            if constexpr (!kPlain)
+        // ---- ping-pong schedule ---------------------------------------------------------
+        // Waves 0-3 (one per SIMD) and waves 4-7 run the same sequence of phases,
+        // the second group one phase behind the first, so that on every SIMD one
+        // wave is in a vector phase while the other is in a matrix phase:
+        //   V(t): running max, exponentials, rescale and test of tile t, flags
+        //         out;
+        //   M(t): 16-bit recompute and P.V of tile t, Q.K^T of tile t+1,
+        //         and the LDS stores of K8(t+2), K16(t+1) and V^T(t+1) (loaded in
+        //         V(t)).
+        // A workgroup barrier ends every phase.  The two groups read the K16 and
+        // V^T tiles of t and the K8 tile of t+1 in two consecutive phases, M(t) of
+        // each; two slots of each array then suffice, and the stores of a phase
+        // never touch a slot read in it.  In the plain bf16 mode the Q.K^T tiles
+        // are K16 tiles, staged like K8, and there is no test or recompute.
+        const int grp = wave >> 2;
+        load_k8(t_begin);
+        store_k8(t_begin);
+        load_k8(t_begin + 1);
+        if constexpr (!kPlain) load_k16(t_begin);
+        load_vt(t_begin);
+        lds_barrier();
+        if (grp == 1) lds_barrier();
+        // M(t_begin - 1): the first Q.K^T and the stores for tile t_begin
+        if (work(t_begin)) qk(S, t_begin);
+        store_k8(t_begin + 1);
+        if constexpr (!kPlain) store_k16(t_begin & 1);
+        store_vt(t_begin & 1);
+        lds_barrier();
+        for (int t = t_begin; t <= t_end; ++t) {
+            const bool w_cur = work(t), w_next = work(t + 1);
+            const bool full = tile_full(r, t, a.S, a.causal, a.window);
+            // ---- V(t)
+            load_k8(t + 2);
+            if constexpr (!kPlain) load_k16(t + 1);
+            load_vt(t + 1);
+            uint32_t flags = 0;
+            if (w_cur) {
+                if (full) softmax(S, P, t, std::integral_constant<bool, false>{});
+                else softmax(S, P, t, std::integral_constant<bool, true>{});
+                rescale();
+                if constexpr (!kPlain)
+                    flags = full ? test(S, std::integral_constant<bool, false>{})
+                                 : test(S, std::integral_constant<bool, true>{});
+            }
+            if (lane == 0) flag_lds[wave] = flags;
+            lds_barrier();
+            // ---- M(t), at raised issue priority: the matrix-core work of this wave
+            // goes first and the vector work of the other wave fills around it
+            __builtin_amdgcn_s_setprio(1);
+            flags = 0;
+    #pragma unroll
+            for (int w = 0; w < C::kWavesPerBlock; ++w) flags |= flag_lds[blk * C::kWavesPerBlock + w];
+            flags = __builtin_amdgcn_readfirstlane(flags);
+            // the loads of V(t) have arrived; storing them first frees their registers
+            store_k8(t + 2);
+            if constexpr (!kPlain) store_k16((t + 1) & 1);
+            store_vt((t + 1) & 1);
+            if (w_cur) {
+                if constexpr (kPlain) {
+                    flags = 0xFu;   // every sub-block in 16-bit
+                } else if (flags != 0) {
+                    if (full) recompute(P, flags, std::integral_constant<bool, false>{}, t);
+                    else recompute(P, flags, std::integral_constant<bool, true>{}, t);
+                }
+                dump_p(P, t);
+                pv(P, t);
+                if (a.mask && wib == 0 && lane == 0)
+                    a.mask[(q_head * a.nT + r) * a.nT + t] = (uint8_t)(0x80u | flags);
+            }
+            if (w_next) qk(S, t + 1);
+            __builtin_amdgcn_s_setprio(0);
+            lds_barrier();
+        }
+        if (grp == 0) lds_barrier();
+    } else {
+        // ---- prologue staging and the first tile's Q.K^T ------------------------------
+        load_k8(t_begin);
+        load_k16(t_begin);
+        store_k8(t_begin);
+        store_k16(0);
+        load_k8(t_begin + 1);
+        store_k8(t_begin + 1);
+        lds_barrier();
+        if (work(t_begin)) qk(S, t_begin);
+        lds_barrier();   // every wave has read K8(t_begin) before its slot is refilled
+
+        // ---- the pipelined loop ---------------------------------------------------------
+        for (int t = t_begin; t <= t_end; ++t) {
+            // K16 of tile t (loaded in the previous iteration) into its single slot:
+            // every wave has finished the recompute of tile t-1, and the flag
+            // barrier below orders these stores before the recompute of tile t
+            if (t > t_begin) store_k16(0);
+            const bool w_prev = work(t - 1), w_cur = work(t), w_next = work(t + 1);
+            const bool full = tile_full(r, t, a.S, a.causal, a.window);
+            // P.V of tile t-1 is issued first (it reads P before the exponentials
+            // of tile t overwrite it) and runs on the matrix cores under the
+            // vector work of tile t
+            if (w_prev) pv(P, t - 1);
+            if (w_cur) {
+                if (full) softmax(S, P, t, std::integral_constant<bool, false>{});
+                else softmax(S, P, t, std::integral_constant<bool, true>{});
+            }
+            // loads for later tiles, stored to LDS before the barrier that ends this
+            // iteration
+            load_k8(t + 2);
+            load_k16(t + 1);
+            load_vt(t);
+            uint32_t flags = 0u;
+            if (w_cur)
                 flags = full ? test(S, std::integral_constant<bool, false>{})
                              : test(S, std::integral_constant<bool, true>{});
-        }
-        if (lane == 0) flag_lds[wave] = flags;
-        lds_barrier();
-        // ---- M(t), at raised issue priority: the matrix-core work of this wave
-        // goes first and the vector work of the other wave fills around it
-        __builtin_amdgcn_s_setprio(1);
-        flags = 0;
-#pragma unroll
-        for (int w = 0; w < C::kWavesPerBlock; ++w) flags |= flag_lds[blk * C::kWavesPerBlock + w];
-        flags = __builtin_amdgcn_readfirstlane(flags);
-        // the loads of V(t) have arrived; storing them first frees their registers
-        store_k8(t + 2);
-        if constexpr (!kPlain) store_k16((t + 1) & 1);
-        store_vt((t + 1) & 1);
-        if (w_cur) {
-            if constexpr (kPlain) {
-                flags = 0xFu;   // every sub-block in 16-bit
-            } else if (flags != 0) {
+            // the waves of a 64-row block OR their flags
+            if (lane == 0) flag_lds[wave] = flags;
+            lds_barrier();
+            flags = 0;
+    #pragma unroll
+            for (int w = 0; w < C::kWavesPerBlock; ++w) flags |= flag_lds[blk * C::kWavesPerBlock + w];
+            flags = __builtin_amdgcn_readfirstlane(flags);
+            if (w_cur && flags != 0) {
                 if (full) recompute(P, flags, std::integral_constant<bool, false>{}, t);
                 else recompute(P, flags, std::integral_constant<bool, true>{}, t);
             }
-            dump_p(P, t);
-            pv(P, t);
-            if (a.mask && wib == 0 && lane == 0)
-                a.mask[(q_head * a.nT + r) * a.nT + t] = (uint8_t)(0x80u | flags);
+            // Q.K^T of tile t+1 runs on the matrix cores under what follows
+            if (w_next) qk(S, t + 1);
+            if (w_cur) {
+                dump_p(P, t);
+                rescale();
+                // (7) mask byte
+                if (a.mask && wib == 0 && lane == 0)
+                    a.mask[(q_head * a.nT + r) * a.nT + t] = (uint8_t)(0x80u | flags);
+            }
+            // K8 of tile t+2 into the slot Q.K^T of tile t used; V^T of tile t into
+            // its single slot (every wave passed the flag barrier, so the P.V of
+            // tile t-1 has read it)
+            store_k8(t + 2);
+            store_vt(0);
+            lds_barrier();
         }
-        if (w_next) qk(S, t + 1);
-        __builtin_amdgcn_s_setprio(0);
-        lds_barrier();
-    }
-    if (grp == 0) lds_barrier();
-    } else {
-    // ---- prologue staging and the first tile's Q.K^T ------------------------------
-    load_k8(t_begin);
-    load_k16(t_begin);
-    store_k8(t_begin);
-    store_k16(0);
-    load_k8(t_begin + 1);
-    store_k8(t_begin + 1);
-    lds_barrier();
-    if (work(t_begin)) qk(S, t_begin);
-    lds_barrier();   // every wave has read K8(t_begin) before its slot is refilled
-
-    // ---- the pipelined loop ---------------------------------------------------------
-    for (int t = t_begin; t <= t_end; ++t) {
-        // K16 of tile t (loaded in the previous iteration) into its single slot:
-        // every wave has finished the recompute of tile t-1, and the flag
-        // barrier below orders these stores before the recompute of tile t
-        if (t > t_begin) store_k16(0);
-        const bool w_prev = work(t - 1), w_cur = work(t), w_next = work(t + 1);
-        const bool full = tile_full(r, t, a.S, a.causal, a.window);
-        // P.V of tile t-1 is issued first (it reads P before the exponentials
-        // of tile t overwrite it) and runs on the matrix cores under the
-        // vector work of tile t
-        if (w_prev) pv(P, t - 1);
-        if (w_cur) {
-            if (full) softmax(S, P, t, std::integral_constant<bool, false>{});
-            else softmax(S, P, t, std::integral_constant<bool, true>{});
-        }
-        // loads for later tiles, stored to LDS before the barrier that ends this
-        // iteration
-        load_k8(t + 2);
-        load_k16(t + 1);
-        load_vt(t);
-        uint32_t flags = 0u;
-        if (w_cur)
-            flags = full ? test(S, std::integral_constant<bool, false>{})
-                         : test(S, std::integral_constant<bool, true>{});
-        // the waves of a 64-row block OR their flags
-        if (lane == 0) flag_lds[wave] = flags;
-        lds_barrier();
-        flags = 0;
-#pragma unroll
-        for (int w = 0; w < C::kWavesPerBlock; ++w) flags |= flag_lds[blk * C::kWavesPerBlock + w];
-        flags = __builtin_amdgcn_readfirstlane(flags);
-        if (w_cur && flags != 0) {
-            if (full) recompute(P, flags, std::integral_constant<bool, false>{}, t);
-            else recompute(P, flags, std::integral_constant<bool, true>{}, t);
-        }
-        // Q.K^T of tile t+1 runs on the matrix cores under what follows
-        if (w_next) qk(S, t + 1);
-        if (w_cur) {
-            dump_p(P, t);
-            rescale();
-            // (7) mask byte
-            if (a.mask && wib == 0 && lane == 0)
-                a.mask[(q_head * a.nT + r) * a.nT + t] = (uint8_t)(0x80u | flags);
-        }
-        // K8 of tile t+2 into the slot Q.K^T of tile t used; V^T of tile t into
-        // its single slot (every wave passed the flag barrier, so the P.V of
-        // tile t-1 has read it)
-        store_k8(t + 2);
-        store_vt(0);
-        lds_barrier();
-    }
-    // P.V of the last tile
-    if (work(t_end)) pv(P, t_end);
+        // P.V of the last tile
+        if (work(t_end)) pv(P, t_end);
     }
 
     // ---- epilogue: out = O / l ------------------------------------------------------
