@@ -78,6 +78,7 @@ struct AttnArgs {
     int heads_per_wg;    // kBlocks, ..., 1
     int rows_per_wg;     // kBlocks / heads_per_wg
     int n_rg;            // row-block groups
+    int paired;          // 1: a workgroup runs row-block groups n_rg-1-level and level
     int n_wg;
 };
 
@@ -135,27 +136,38 @@ __global__ __launch_bounds__(kThreads, 1) void lamp_attn_kernel(AttnArgs a) {
     const int blk = wave / C::kWavesPerBlock;   // which (head, 64-row block) of the workgroup
     const int wib = wave % C::kWavesPerBlock;   // rows wib*kWaveRows .. of that block
 
-    // ---- workgroup -> (batch, kv head, head group, row-block group) ----------
+    // ---- workgroup -> (batch, kv head, head group) unit and row-block group(s)
     // Workgroups are dispatched in index order, round-robin over the XCDs.
-    // Index order is longest (causal) rows first, so that the CUs that free
-    // first take the longest of the remaining rows.  Within a level of equal
-    // length the (batch, kv head, head group) units are offset by the
-    // level's parity: an XCD then works on two units, alternately.  Units
-    // differ in how much they recompute, and one unit per XCD leaves the XCDs
-    // unevenly loaded; two share the load while the K/V tiles of a unit are
-    // fetched into two L2s only (spreading every unit over every XCD balances
-    // a little better but fetches each tile into every L2).
+    // Index order is longest (causal) rows first; consecutive indices are
+    // consecutive units, so with 8 units per level each XCD keeps to one unit
+    // and its K/V tiles stay in that XCD's L2.  Unpaired launches offset the
+    // units by the level's parity, so that each XCD alternates between two
+    // units: units differ in how much they recompute, and two share the
+    // load while each K/V tile is fetched into two L2s only.
     const int wg = blockIdx.x;
     const int n_hg = a.G / a.heads_per_wg;
-    const int n_u = a.n_wg / a.n_rg;
+    const int n_lv = a.paired ? (a.n_rg + 1) / 2 : a.n_rg;
+    const int n_u = a.n_wg / n_lv;
     const int level = wg / n_u;
-    const int rg = a.n_rg - 1 - level;
-    int u = (wg % n_u + (level & 1)) % n_u;
+    int u = (wg % n_u + (a.paired ? 0 : (level & 1))) % n_u;
     const int hg = u % n_hg;
     u /= n_hg;
     const int hk = u % a.Hkv;
     const int b = u / a.Hkv;
     const int hq = hk * a.G + hg * a.heads_per_wg + (blk % a.heads_per_wg);
+    const size_t kv_head = (size_t)b * a.Hkv + hk;
+    const size_t q_head = (size_t)b * a.Hq + hq;
+
+    // Paired launches: a workgroup runs two row-block groups back to back,
+    // n_rg-1-level and level.  Under a causal mask they visit n_rg+1 tiles
+    // together at every level, so all workgroups carry the same work and no
+    // CU waits on a long last workgroup (it pays where there are only about
+    // two workgroups per CU).  Otherwise a workgroup runs n_rg-1-level alone,
+    // longest rows first.  Between the two runs every wave has passed the
+    // last barrier of the first one's loop, after which no wave reads the LDS
+    // staged for it (the one-slot loop's final P.V reads only V^T, which the
+    // second one first writes after its prologue barrier).
+    auto run_rows = [&](const int rg) __attribute__((always_inline)) {
     const int r = rg * a.rows_per_wg + blk / a.heads_per_wg;
     const bool active = r < a.nT;
     const int r_first = rg * a.rows_per_wg;
@@ -163,9 +175,6 @@ __global__ __launch_bounds__(kThreads, 1) void lamp_attn_kernel(AttnArgs a) {
     const int t_begin = tile_lo(r_first, a.window);
     const int t_end = tile_hi(r_last, a.nT, a.causal);
     const int row0 = r * kTileRows + wib * kWaveRows;   // first query row of this wave
-
-    const size_t kv_head = (size_t)b * a.Hkv + hk;
-    const size_t q_head = (size_t)b * a.Hq + hq;
 
     uint8_t* q8_lds = lds + C::kQ8Off + wave * C::kQ8Bytes;
 
@@ -778,6 +787,25 @@ __global__ __launch_bounds__(kThreads, 1) void lamp_attn_kernel(AttnArgs a) {
             }
         }
     }
+    };
+    run_rows(a.n_rg - 1 - level);
+    // (D = 256 launches are never paired: they would carry the register cost
+    // of the second run without the balance it buys at these grid sizes)
+    if constexpr (C::kPP)
+        if (a.paired && level != a.n_rg - 1 - level) run_rows(level);
+}
+
+// Compute units of the current device (cached per device).
+int cu_count() {
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cached[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        cached[dev] = n;
+    }
+    return cached[dev];
 }
 
 template <int D>
@@ -797,7 +825,11 @@ hipError_t launch_d(const Shape& sh, const AttnParams& p, hipStream_t st) {
         if (a.G % h == 0) { a.heads_per_wg = h; break; }
     a.rows_per_wg = Cfg<D>::kBlocks / a.heads_per_wg;
     a.n_rg = (sh.nT + a.rows_per_wg - 1) / a.rows_per_wg;
-    a.n_wg = sh.B * sh.Hkv * (a.G / a.heads_per_wg) * a.n_rg;
+    // pair row-block groups where the unpaired grid gives at most two
+    // workgroups per CU and the rows differ in length (causal, no window)
+    const int n_u = sh.B * sh.Hkv * (a.G / a.heads_per_wg);
+    a.paired = Cfg<D>::kPP && p.causal && p.window == 0 && n_u * a.n_rg <= 2 * cu_count() ? 1 : 0;
+    a.n_wg = n_u * (a.paired ? (a.n_rg + 1) / 2 : a.n_rg);
     size_t lds = Cfg<D>::kLdsBytes;
     const bool dump = p.dump_s != nullptr && p.dump_p != nullptr;
     using Fn = void (*)(AttnArgs);
