@@ -113,10 +113,12 @@ def _bf16(bits):
     return sign * (1 + Fraction(m, 128)) * Fraction(2) ** (ef - 127)
 
 
-def brute_lamp(q_bits, k_bits, v_bits, causal, window, delta, tau):
+def brute_lamp(q_bits, k_bits, v_bits, causal, window, delta, tau, logit8=False):
     """Whole forward pass; returns (out as nested lists of float, mask dict).
 
-    mask[(b, hq, r, t)] = byte for visited tiles only.
+    mask[(b, hq, r, t)] = byte for visited tiles only.  ``logit8``: the
+    variant whose log2-domain logits are rounded to e4m3 before the running
+    max, the exponentials and the second stage read them.
     """
     B, Hq, S, D = (len(q_bits), len(q_bits[0]), len(q_bits[0][0]), len(q_bits[0][0][0]))
     Hkv = len(k_bits[0])
@@ -175,13 +177,16 @@ def brute_lamp(q_bits, k_bits, v_bits, causal, window, delta, tau):
                                 a = sum(q8[i][d] * k8[j][d] for d in range(D))
                                 acc8[i, j] = to_f32(a)
                                 s2[i, j] = to_f32(acc8[i, j] * c8)
+                                if logit8:
+                                    s2[i, j] = to_e4m3(s2[i, j])
                     m_new = {}
                     for i in rows:
                         cand = [s2[i, j] for j in keys if (i, j) in s2]
                         m_new[i] = max([m[i]] + cand) if cand else m[i]
                     p, flags = {}, [False] * 4
                     for (i, j), a in acc8.items():
-                        e = _exp2_f32(to_f32(a * c8 - m_new[i]))
+                        arg = s2[i, j] - m_new[i] if logit8 else a * c8 - m_new[i]
+                        e = _exp2_f32(to_f32(arg))
                         p8 = to_e4m3(e)
                         p[i, j] = p8
                         active = (delta <= 0) or (p8 >= Fraction(delta))

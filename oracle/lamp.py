@@ -33,6 +33,12 @@ The pages give no formula, format or tile size.  The readings taken here
   (the e4m3 unit roundoff) is 2^-4 * |s|, compared with tau;
 * a sub-block is flagged (recomputed in 16-bit) iff it holds a sensitive entry.
 
+A second reading of "accumulated in 8-bit formats" is kept as a variant
+(``logit8``): the log2-domain logit s = fl32(acc * c) is itself rounded to
+e4m3 (saturating at 448) before anything uses it.  The running max, the
+exponential's argument s8 - m (exact: both are e4m3 values) and the second
+stage all read the 8-bit logit; the 16-bit recompute is unchanged.
+
 Masking: causal (key j visible to query i iff j <= i) and an optional sliding
 window W (additionally i - j < W).  GQA: query head hq reads kv head hq // G.
 """
@@ -204,13 +210,19 @@ def run_unit(ctx, b, hq, r, flag_override=None, trace=None):
         # (a) 8-bit products, summed exactly (all partial sums are multiples of
         #     2^-18 below 2^26, so fp64 holds them exactly), rounded to fp32.
         acc8 = fl32(q8 @ k8.T)
-        s2 = np.where(vis, fl32(acc8 * c8), -np.inf)
+        s32 = f32 = fl32(acc8 * c8)
+        if ctx["logit8"]:
+            s32 = round_e4m3(f32)            # the 8-bit logit (variant)
+        s2 = np.where(vis, s32, -np.inf)
         # (b) running max over the 8-bit logits of this tile
         m_new = np.maximum(m, s2.max(axis=1))
         live = m_new > -np.inf
         safe_m = np.where(live, m_new, 0.0)
         # (c) 8-bit exponentials against the running max
-        x = np.where(vis, fma32(acc8, c8, -safe_m[:, None]), -np.inf)
+        if ctx["logit8"]:
+            x = np.where(vis, fl32(s32 - safe_m[:, None]), -np.inf)
+        else:
+            x = np.where(vis, fma32(acc8, c8, -safe_m[:, None]), -np.inf)
         e = np.where(vis, exp2_f32(x), 0.0)
         p8 = round_e4m3(e)
         # (d) look-ahead test, first and second stage
@@ -244,7 +256,7 @@ def run_unit(ctx, b, hq, r, flag_override=None, trace=None):
             byte |= int(flags[c]) << c
         mask[t] = byte
         if trace is not None:
-            trace.append(dict(t=t, cols=cols, vis=vis, acc8=acc8, s2=s2, e=e,
+            trace.append(dict(t=t, cols=cols, vis=vis, acc8=acc8, s2=s2, f32=f32, e=e,
                               p8=p8, p=p, e16=e16, flags=flags, m_new=m_new.copy(), T2=T2))
     # Step 5: normalise
     out = fl32(O / ell[:, None])
@@ -341,9 +353,10 @@ class PerHead:
         return self._cache[key][tuple(idx[2:])]
 
 
-def prepare(q_bits, k_bits, v_bits, causal, window, delta, tau):
+def prepare(q_bits, k_bits, v_bits, causal, window, delta, tau, logit8=False):
     """Scales of Q and K, and per-head access to everything the units read
-    (the e4m3 values of Q and K, and the bf16 values of Q, K and V)."""
+    (the e4m3 values of Q and K, and the bf16 values of Q, K and V).
+    ``logit8`` selects the variant whose log2-domain logits are e4m3 values."""
     B, Hq, S, D = q_bits.shape
     Hkv = k_bits.shape[1]
     assert Hq % Hkv == 0 and k_bits.shape == v_bits.shape == (B, Hkv, S, D)
@@ -359,7 +372,7 @@ def prepare(q_bits, k_bits, v_bits, causal, window, delta, tau):
 
     return dict(B=B, Hq=Hq, Hkv=Hkv, S=S, D=D, G=Hq // Hkv,
                 causal=bool(causal), window=int(window),
-                delta=float(delta), T2=tau_threshold(tau),
+                delta=float(delta), T2=tau_threshold(tau), logit8=bool(logit8),
                 q8=PerHead(e4m3_slab(q_bits, iq)), k8=PerHead(e4m3_slab(k_bits, ik)), sq=sq, sk=sk,
                 q16=PerHead(bf16_slab(q_bits)), k16=PerHead(bf16_slab(k_bits)),
                 v=PerHead(bf16_slab(v_bits)))
@@ -371,15 +384,16 @@ def all_units(B, Hq, S):
 
 
 def lamp_forward(q_bits, k_bits, v_bits, causal=True, window=0, delta=2.0 ** -8,
-                 tau=2.0 ** -1, units=None, flag_override=None):
+                 tau=2.0 ** -1, units=None, flag_override=None, logit8=False):
     """The LampAttention forward pass over ``units`` (default: all).
 
     q_bits [B, Hq, S, D], k_bits / v_bits [B, Hkv, S, D]: bf16 bit patterns.
     Returns (out fp32 [B, Hq, S, D] (rows of units not computed are NaN),
     mask uint8 [B, Hq, nT, nT]).  ``flag_override`` is a mask array of the
     same shape whose low 4 bits replace the computed flags of visited tiles.
+    ``logit8``: the variant with e4m3 logits.
     """
-    ctx = prepare(q_bits, k_bits, v_bits, causal, window, delta, tau)
+    ctx = prepare(q_bits, k_bits, v_bits, causal, window, delta, tau, logit8)
     B, Hq, S, D = ctx["B"], ctx["Hq"], ctx["S"], ctx["D"]
     nT = n_tiles(S)
     out = np.full((B, Hq, S, D), np.nan, dtype=np.float32)

@@ -299,3 +299,151 @@ def assert_parity(rep):
     assert not rep["unexcused"], f"unexcused mask mismatches: {rep['unexcused'][:10]}"
     assert not rep["rows_unexplained"], f"rows above {MAX_ABS}: {rep['rows_unexplained'][:10]}"
     assert rep["mean_abs"] <= MEAN_ABS, rep["mean_abs"]
+
+
+# --------------------------------------------------------------------------
+# the 8-bit-logit variant (lamp_attn_fwd_logit8 against the oracle's logit8)
+# --------------------------------------------------------------------------
+# The variant rounds the fp32 logit to e4m3.  Within the FP8 accumulation
+# window an fp32 logit near an e4m3 rounding midpoint can round to either
+# neighbour, a whole 8-bit step apart; where the row's running max is such a
+# logit, every weight of the row moves with it.  Those rows ("max-fragile")
+# are counted and left out of the output comparison; in all other rows each
+# entry's admissible 8-bit logits are {e4m3(f - ds), ..., e4m3(f + ds)} and the
+# protocol above applies to the weights they give.
+
+def logit8_unit(ctx, b, h, r, override=None):
+    """Windows of one unit of the variant.  Returns dict(out, trace,
+    max_fragile [rows] bool, fragile {t: 4-bit set}, bound [rows, D],
+    lo8/hi8 {t: [rows, cols]})."""
+    trace = []
+    out, _ = L.run_unit(ctx, b, h, r, flag_override=override, trace=trace)
+    fin = trace[-1]
+    G, D = ctx["G"], ctx["D"]
+    vv = ctx["v"][b, h // G]
+    c8, c16 = L.logit_constants(D, ctx["sq"][b, h], ctx["sk"][b, h // G])
+    n = out.shape[0]
+    rows = np.arange(r * 64, r * 64 + n)
+    q8, q16 = ctx["q8"][b, h, rows], ctx["q16"][b, h, rows]
+    mlo = np.full(n, -np.inf)
+    mhi = np.full(n, -np.inf)
+    max_fragile = np.zeros(n, dtype=bool)
+    fragile, lo8s, hi8s, alts = {}, {}, {}, {}
+    bound = np.zeros_like(out)
+    for rec in trace[:-1]:
+        vis, cols = rec["vis"], rec["cols"]
+        k8 = ctx["k8"][b, h // G, cols]
+        k16 = ctx["k16"][b, h // G, cols]
+        maxp8 = np.max(np.abs(q8[:, None, :] * k8[None, :, :]), axis=2)
+        maxp16 = np.max(np.abs(q16[:, None, :] * k16[None, :, :]), axis=2)
+        f = rec["f32"]
+        ds = c8 * EPS_ACC8 * maxp8 + np.spacing(np.abs(f).astype(np.float32)).astype(np.float64)
+        lo8 = np.where(vis, round_e4m3(f - ds), -np.inf)
+        hi8 = np.where(vis, round_e4m3(f + ds), -np.inf)
+        lo8s[rec["t"]], hi8s[rec["t"]] = lo8, hi8
+        mlo = np.maximum(mlo, lo8.max(axis=1))
+        mhi = np.maximum(mhi, hi8.max(axis=1))
+        max_fragile |= mlo != mhi
+        mlo_s = np.where(np.isfinite(mlo), mlo, 0.0)[:, None]
+        mhi_s = np.where(np.isfinite(mhi), mhi, 0.0)[:, None]
+        with np.errstate(invalid="ignore"):
+            e_lo = np.where(vis, L._ulp_step(np.exp2(lo8 - mhi_s), -EXP2_ULPS), 0.0)
+            e_hi = np.where(vis, L._ulp_step(np.exp2(hi8 - mlo_s), EXP2_ULPS), 0.0)
+        e_lo = np.maximum(e_lo, 0.0)
+        # |s8| over the admissible range
+        lo0, hi0 = np.where(vis, lo8, 0.0), np.where(vis, hi8, 0.0)
+        a_lo = np.where((lo0 <= 0) & (hi0 >= 0), 0.0, np.minimum(np.abs(lo0), np.abs(hi0)))
+        a_hi = np.maximum(np.abs(lo0), np.abs(hi0))
+        ext = []
+        for e_k, a_k in ((e_lo, a_lo), (e_hi, a_hi)):
+            act = L.stage_one(round_e4m3(e_k), vis, ctx["delta"])
+            ext.append(L.subblock_flags(act & (a_k >= rec["T2"])))
+        fragile[rec["t"]] = sum(int(x != y) << c for c, (x, y) in enumerate(zip(*ext)))
+        # weights that can round the other way (rows whose max is fixed)
+        p, e16 = rec["p"], rec["e16"]
+        rec16 = ~np.isnan(e16)
+        alt = np.zeros_like(p)
+        for e_k in (e_lo, e_hi):
+            alt = np.maximum(alt, np.where(vis & ~rec16, np.abs(round_e4m3(e_k) - p), 0.0))
+        dx16 = c16 * EPS_ACC16 * maxp16
+        lo16, hi16 = _e_bounds(np.where(rec16, e16, 0.0), dx16)
+        for e_k in (lo16, hi16):
+            alt = np.maximum(alt, np.where(vis & rec16, np.abs(round_bf16(e_k) - p), 0.0))
+        alts[rec["t"]] = alt
+        scale = np.exp2(rec["m_new"] - fin["m"]) / fin["ell"]
+        vj = vv[cols]
+        bound += np.einsum("ij,ijd->id", alt * scale[:, None], np.abs(vj[None, :, :] - out[:, None, :]))
+    return dict(out=out, trace=trace, max_fragile=max_fragile, fragile=fragile,
+                bound=1.1 * bound, lo8=lo8s, hi8=hi8s, alt=alts)
+
+
+def compare_logit8(q, k, v, causal, window, delta, tau, units=None, label="", gpu=None):
+    """GPU 8-bit-logit variant against the oracle's; returns a report dict.
+    ``gpu`` = (out, mask) arrays replaces the device run (protocol self-tests)."""
+    B, Hq, S, D = q.shape
+    if units is None:
+        units = L.all_units(B, Hq, S)
+    say(f"[parity-logit8] {label} B={B} Hq={Hq} Hkv={k.shape[1]} S={S} D={D} causal={causal} "
+        f"window={window} delta={delta} tau={tau} units={len(units)}")
+    if gpu is None:
+        import mixed_precision_attention_lamp_amd as lamp
+        out_d, mask_d = lamp.attention(to_device(q), to_device(k), to_device(v), causal, window, delta,
+                                       tau, logit8=True)
+        torch.cuda.synchronize()
+        out_g, mask_g = out_d.cpu().numpy(), mask_d.cpu().numpy()
+    else:
+        out_g, mask_g = gpu
+    ctx = L.prepare(q, k, v, causal, window, delta, tau, logit8=True)
+    nT = mask_g.shape[-1]
+    unexcused, n_excused, n_sub = [], 0, 0
+    n_rows = n_skipped = 0
+    explained, unexplained, diffs = 0, [], []
+    for (b, h, r) in units:
+        w = logit8_unit(ctx, b, h, r)
+        want = np.zeros(nT, dtype=np.uint8)
+        for rec in w["trace"][:-1]:
+            want[rec["t"]] = 0x80 | sum(int(f) << c for c, f in enumerate(rec["flags"]))
+        n_sub += int(((want & 0x80) != 0).sum()) * 4
+        diff_t = np.nonzero(mask_g[b, h, r] != want)[0]
+        for t in diff_t:
+            x = int(mask_g[b, h, r, t]) ^ int(want[t])
+            if (x & 0x80) == 0 and (x & ~w["fragile"].get(int(t), 0) & 0x0F) == 0:
+                n_excused += 1
+            else:
+                unexcused.append((b, h, r, int(t), int(mask_g[b, h, r, t]), int(want[t])))
+        if diff_t.size:
+            ov = {t: int(mask_g[b, h, r, t]) & 0x0F for t in range(nT)}
+            w = logit8_unit(ctx, b, h, r, override=ov)
+        n = w["out"].shape[0]
+        rows = slice(r * 64, r * 64 + n)
+        d = np.abs(out_g[b, h, rows].astype(np.float64) - w["out"].astype(np.float64))
+        keep = ~w["max_fragile"]
+        n_rows += n
+        n_skipped += int((~keep).sum())
+        if not np.isfinite(out_g[b, h, rows]).all():
+            unexplained.append((b, h, r, "non-finite"))
+        diffs.append(d[keep])
+        for i in np.nonzero(keep & (d > MAX_ABS).any(axis=1))[0]:
+            if np.all(d[i] <= MAX_ABS + w["bound"][i]):
+                explained += 1
+            else:
+                j = int(np.argmax(d[i] - w["bound"][i]))
+                unexplained.append((b, h, r * 64 + int(i), j, float(d[i, j]), float(w["bound"][i, j])))
+    d = np.concatenate([x.reshape(-1) for x in diffs]) if diffs else np.zeros(1)
+    rep = dict(max_abs=float(d.max()), mean_abs=float(d.mean()), unexcused=unexcused,
+               excused=n_excused, n_subblocks=n_sub, rows=n_rows, rows_max_fragile=n_skipped,
+               rows_explained=explained, rows_unexplained=unexplained,
+               finite=bool(np.isfinite(out_g).all()))
+    say(f"[parity-logit8] {label} max|dO|={rep['max_abs']:.3e} mean|dO|={rep['mean_abs']:.3e} "
+        f"mask mismatches {n_excused + len(unexcused)} of {n_sub} sub-blocks (excused {n_excused}); "
+        f"rows with a max-fragile logit {n_skipped} of {n_rows} (not compared); rows above "
+        f"{MAX_ABS:g}: {explained + len(unexplained)} (explained {explained})")
+    return rep
+
+
+def assert_parity_logit8(rep, max_skipped=0.1):
+    assert rep["finite"], "non-finite outputs"
+    assert not rep["unexcused"], f"unexcused mask mismatches: {rep['unexcused'][:10]}"
+    assert not rep["rows_unexplained"], f"rows above {MAX_ABS}: {rep['rows_unexplained'][:10]}"
+    assert rep["mean_abs"] <= MEAN_ABS, rep["mean_abs"]
+    assert rep["rows_max_fragile"] <= max_skipped * rep["rows"], rep["rows_max_fragile"]

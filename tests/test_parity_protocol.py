@@ -1,0 +1,41 @@
+"""The parity protocols themselves, on the CPU: each accepts the oracle it
+checks against and rejects a planted mistake (the other reading of the
+8-bit logits, fed in as if a device had computed it).  No GPU."""
+import numpy as np
+
+from inputs import make_inputs
+from oracle import lamp as L
+from parity import assert_parity, assert_parity_logit8, compare, compare_logit8
+
+CASE = (1, 2, 1, 150, 64, 1, 0, 2.0 ** -8, 2.0 ** -1, "channels", 41)
+
+
+def _inputs():
+    B, Hq, Hkv, S, D, causal, window, delta, tau, st, seed = CASE
+    q, k, v = make_inputs(B, Hq, Hkv, S, D, seed, st)
+    return q, k, v, causal, window, delta, tau
+
+
+def test_logit8_protocol_accepts_the_oracle():
+    q, k, v, causal, window, delta, tau = _inputs()
+    dev = L.lamp_forward(q, k, v, causal, window, delta, tau, logit8=True)
+    rep = compare_logit8(q, k, v, causal, window, delta, tau, gpu=dev, label="self")
+    assert_parity_logit8(rep)
+    assert rep["max_abs"] == 0.0 and rep["excused"] == 0
+
+
+def test_logit8_protocol_rejects_the_default_reading():
+    q, k, v, causal, window, delta, tau = _inputs()
+    dev = L.lamp_forward(q, k, v, causal, window, delta, tau)
+    rep = compare_logit8(q, k, v, causal, window, delta, tau, gpu=dev, label="planted")
+    bad = bool(rep["unexcused"]) or bool(rep["rows_unexplained"]) or rep["mean_abs"] > 5e-4
+    assert bad, rep
+
+
+def test_default_protocol_accepts_the_oracle_and_rejects_logit8():
+    q, k, v, causal, window, delta, tau = _inputs()
+    dev = L.lamp_forward(q, k, v, causal, window, delta, tau)
+    assert_parity(compare(q, k, v, causal, window, delta, tau, gpu=dev, label="self"))
+    dev8 = L.lamp_forward(q, k, v, causal, window, delta, tau, logit8=True)
+    rep = compare(q, k, v, causal, window, delta, tau, gpu=dev8, label="planted")
+    assert bool(rep["unexcused"]) or bool(rep["rows_unexplained"]) or rep["mean_abs"] > 5e-4, rep
