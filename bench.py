@@ -130,11 +130,15 @@ GRID_DELTAS = (0.0, 2.0 ** -8, 2.0 ** -4)
 GRID_TAUS = tuple(2.0 ** -i for i in range(6))
 GRID_ENDPOINTS = ((2.0 ** -8, float("inf"), "8-bit Q.K^T only"), (0.0, 0.0, "all sub-blocks 16-bit"))
 PLAIN_NOTE = "plain bf16 FlashAttention (no 8-bit pass)"
+LOGIT8_NOTE = "8-bit logits (e4m3-rounded log2-domain logit)"
+LOGIT8_POINTS = ((2.0 ** -8, 2.0 ** -1), (2.0 ** -8, float("inf")), (2.0 ** -4, 2.0 ** -1))
 
 
-def measure(lamp, torch, tensors, shape, causal, window, delta, tau, steps, warmup, plain=False):
-    """Time `steps` calls of lamp_attn_fwd (lamp_attn_fwd_bf16 when plain)
-    after `warmup` untimed ones; returns the step time, the attention kernel
+def measure(lamp, torch, tensors, shape, causal, window, delta, tau, steps, warmup, plain=False,
+            logit8=False):
+    """Time `steps` calls of lamp_attn_fwd (lamp_attn_fwd_bf16 when plain,
+    lamp_attn_fwd_logit8 when logit8) after `warmup` untimed ones; returns the
+    step time, the attention kernel
     time (HIP events on its stream), the algorithmic FLOP counts and the
     sub-block statistics of the last call."""
     qd, kd, vd, out, mask = tensors
@@ -143,6 +147,8 @@ def measure(lamp, torch, tensors, shape, causal, window, delta, tau, steps, warm
     def step():
         if plain:
             lamp.lamp_attn_fwd_bf16(qd, kd, vd, out, causal, window, mask)
+        elif logit8:
+            lamp.lamp_attn_fwd_logit8(qd, kd, vd, out, causal, window, delta, tau, mask)
         else:
             lamp.lamp_attn_fwd(qd, kd, vd, out, causal, window, delta, tau, mask)
 
@@ -186,9 +192,10 @@ def run_grid(args, lamp, torch, tensors, shape, causal, window, cfg):
     runs = [(d, t, "") for d in GRID_DELTAS for t in GRID_TAUS] + list(GRID_ENDPOINTS)
     if shape[4] <= 128:
         runs.append((0.0, 0.0, PLAIN_NOTE))
+    runs += [(d, t, LOGIT8_NOTE) for d, t in LOGIT8_POINTS]
     for delta, tau, note in runs:
         m = measure(lamp, torch, tensors, shape, causal, window, delta, tau, args.steps, args.warmup,
-                    plain=note == PLAIN_NOTE)
+                    plain=note == PLAIN_NOTE, logit8=note == LOGIT8_NOTE)
         achieved, peak = roofline_of(m)
         print(json.dumps({
             "grid": args.workload, "delta": delta, "tau": tau if tau != float("inf") else "inf",

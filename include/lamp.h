@@ -69,6 +69,18 @@ int lamp_attn_fwd(const void* q, const void* k, const void* v, float* out,
                   int causal, int window, float delta, float tau,
                   uint8_t* subblock_mask_out);
 
+/* The forward pass under the literal reading of "key-query products accumulated
+ * in 8-bit formats" ("LampAttention", abstract): the log2-domain logit
+ * c * acc (c = log2(e)/sqrt(D) times the Q and K scales) is itself rounded to
+ * e4m3 (magnitudes clamped to 448, nearest even) before the running row max,
+ * the 8-bit exponentials 2^(s8 - m) and the second stage |s8| >= 16 tau log2(e)
+ * read it.  The 16-bit recompute is that of lamp_attn_fwd.  Arguments, layout,
+ * sizes and errors as lamp_attn_fwd. */
+int lamp_attn_fwd_logit8(const void* q, const void* k, const void* v, float* out,
+                         int B, int Hq, int Hkv, int S, int D,
+                         int causal, int window, float delta, float tau,
+                         uint8_t* subblock_mask_out);
+
 /* The 16-bit baseline: plain bf16 FlashAttention on the same tiles ("16-bit"
  * column of tables 1-6 read as a kernel; no 8-bit pass).  Logits are the bf16
  * products accumulated in fp32 on the matrix cores, the running row max comes
@@ -117,6 +129,14 @@ int lamp_debug_attn_dump(const void* q, const void* k, const void* v, float* out
                          int B, int Hq, int Hkv, int S, int D,
                          int causal, int window, float delta, float tau,
                          uint8_t* subblock_mask_out, float* acc8_out, uint16_t* p_out);
+
+/* lamp_debug_attn_dump for lamp_attn_fwd_logit8: logit8_out [B, Hq, S, S] fp32
+ * receives the 8-bit logit (an e4m3 value) of every visible entry instead of
+ * the accumulator; p_out, sizes and errors as lamp_debug_attn_dump. */
+int lamp_debug_attn_dump_logit8(const void* q, const void* k, const void* v, float* out,
+                                int B, int Hq, int Hkv, int S, int D,
+                                int causal, int window, float delta, float tau,
+                                uint8_t* subblock_mask_out, float* logit8_out, uint16_t* p_out);
 
 /* Per-kernel timing with HIP events recorded on the library's stream, for
  * benches.  While enabled (enable = 1), every lamp_attn_fwd call records one

@@ -9,7 +9,8 @@ package only marshals torch tensors into the C entry points (see _lib.py) and
 allocates outputs.
 """
 from ._lib import (LAMP_STATS_LEN, LampError, declared_symbols, lamp_attn_fwd,  # noqa: F401
-                   lamp_attn_fwd_bf16, lamp_debug_attn_dump, lamp_debug_convert, lamp_last_error,
+                   lamp_attn_fwd_bf16, lamp_attn_fwd_logit8, lamp_debug_attn_dump,
+                   lamp_debug_attn_dump_logit8, lamp_debug_convert, lamp_last_error,
                    lamp_quantize_qk, lamp_read_timing, lamp_release_workspace, lamp_set_stream,
                    lamp_set_timing, lamp_subblock_stats, lamp_version, load)
 
@@ -20,8 +21,10 @@ def n_tiles(S):
     return (S + TILE - 1) // TILE
 
 
-def attention(q, k, v, causal=True, window=0, delta=2.0 ** -8, tau=2.0 ** -1, with_mask=True):
-    """Allocate the outputs and run lamp_attn_fwd; returns (out, mask or None)."""
+def attention(q, k, v, causal=True, window=0, delta=2.0 ** -8, tau=2.0 ** -1, with_mask=True,
+              logit8=False):
+    """Allocate the outputs and run lamp_attn_fwd (lamp_attn_fwd_logit8 when
+    logit8); returns (out, mask or None)."""
     import torch
     B, Hq, S, D = q.shape
     out = torch.empty((B, Hq, S, D), dtype=torch.float32, device=q.device)
@@ -29,7 +32,8 @@ def attention(q, k, v, causal=True, window=0, delta=2.0 ** -8, tau=2.0 ** -1, wi
     if with_mask:
         nT = n_tiles(S)
         mask = torch.empty((B, Hq, nT, nT), dtype=torch.uint8, device=q.device)
-    lamp_attn_fwd(q, k, v, out, int(causal), int(window), delta, tau, mask)
+    fwd = lamp_attn_fwd_logit8 if logit8 else lamp_attn_fwd
+    fwd(q, k, v, out, int(causal), int(window), delta, tau, mask)
     return out, mask
 
 

@@ -41,11 +41,16 @@ def load():
     vp, i32, f32, i64 = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_int64
     lib.lamp_attn_fwd.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, f32, f32, vp]
     lib.lamp_attn_fwd.restype = i32
+    lib.lamp_attn_fwd_logit8.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, f32, f32, vp]
+    lib.lamp_attn_fwd_logit8.restype = i32
     lib.lamp_attn_fwd_bf16.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, vp]
     lib.lamp_attn_fwd_bf16.restype = i32
     lib.lamp_debug_attn_dump.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, f32, f32,
                                          vp, vp, vp]
     lib.lamp_debug_attn_dump.restype = i32
+    lib.lamp_debug_attn_dump_logit8.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, f32,
+                                                f32, vp, vp, vp]
+    lib.lamp_debug_attn_dump_logit8.restype = i32
     lib.lamp_subblock_stats.argtypes = [vp, i32, i32, i32, i32, i32, vp]
     lib.lamp_subblock_stats.restype = i32
     lib.lamp_quantize_qk.argtypes = [vp, vp, i32, i32, i32, i32, i32, vp, vp, vp, vp]
@@ -129,6 +134,18 @@ def lamp_attn_fwd(q, k, v, out, causal=1, window=0, delta=2.0 ** -8, tau=2.0 ** 
                              _ptr(subblock_mask_out)))
 
 
+def lamp_attn_fwd_logit8(q, k, v, out, causal=1, window=0, delta=2.0 ** -8, tau=2.0 ** -1,
+                         subblock_mask_out=None):
+    """The variant with e4m3 logits; arguments as lamp_attn_fwd."""
+    lib = load()
+    B, Hq, S, D = q.shape
+    Hkv = k.shape[1]
+    _sync_stream(lib)
+    _check(lib.lamp_attn_fwd_logit8(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, Hq, Hkv, S, D,
+                                    int(causal), int(window), float(delta), float(tau),
+                                    _ptr(subblock_mask_out)))
+
+
 def lamp_attn_fwd_bf16(q, k, v, out, causal=1, window=0, subblock_mask_out=None):
     """The plain bf16 FlashAttention baseline; arguments as lamp_attn_fwd."""
     lib = load()
@@ -148,6 +165,17 @@ def lamp_debug_attn_dump(q, k, v, out, causal, window, delta, tau, subblock_mask
     _check(lib.lamp_debug_attn_dump(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, Hq, Hkv, S, D,
                                     int(causal), int(window), float(delta), float(tau),
                                     _ptr(subblock_mask_out), _ptr(acc8_out), _ptr(p_out)))
+
+
+def lamp_debug_attn_dump_logit8(q, k, v, out, causal, window, delta, tau, subblock_mask_out,
+                                logit8_out, p_out):
+    lib = load()
+    B, Hq, S, D = q.shape
+    Hkv = k.shape[1]
+    _sync_stream(lib)
+    _check(lib.lamp_debug_attn_dump_logit8(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, Hq, Hkv, S, D,
+                                           int(causal), int(window), float(delta), float(tau),
+                                           _ptr(subblock_mask_out), _ptr(logit8_out), _ptr(p_out)))
 
 
 def lamp_subblock_stats(subblock_mask, B, Hq, S, causal, window, stats_out):

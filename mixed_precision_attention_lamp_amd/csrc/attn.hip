@@ -117,10 +117,14 @@ struct Cfg {
 // kMode: 0 = no test (second stage off), 1 = both stages, 2 = second stage
 // only, 3 = plain bf16 FlashAttention (the 16-bit baseline: no 8-bit pass,
 // Q.K^T of every sub-block on the bf16 matrix cores, exponentials rounded to
-// bf16; ping-pong schedule only).
+// bf16; ping-pong schedule only); 4 + (0, 1, 2): the test modes 0-2 with
+// 8-bit logits (the log2-domain logit c8 acc itself rounded to e4m3 before the
+// running max, the exponentials and the test read it).
 template <int D, bool kDump, int kMode>
 __global__ __launch_bounds__(kThreads, 1) void lamp_attn_kernel(AttnArgs a) {
     constexpr bool kPlain = kMode == 3;
+    constexpr bool kLogit8 = kMode >= 4;
+    constexpr int kTest = kMode & 3;
     using C = Cfg<D, kPlain>;
     static_assert(!kPlain || C::kPP, "the plain bf16 mode runs on the ping-pong schedule");
     constexpr int kQG = C::kQG;
@@ -256,7 +260,7 @@ __global__ __launch_bounds__(kThreads, 1) void lamp_attn_kernel(AttnArgs a) {
     };
 
     // ---- prologue: this wave's Q16 operand into registers, Q8 rows into its LDS ----
-    float m_run[kQG], c8 = 0.0f, inv_c8 = 0.0f, a2 = 0.0f;
+    float m_run[kQG], c8 = 0.0f, inv_c8 = 0.0f, a2 = 0.0f, c8_log = 0.0f;
     const float c16 = (float)a.l_d;
     v8bf qb[C::kDC][kQG];     // bf16 operand of 16-query group qg, 32-deep step ch
 #pragma unroll
@@ -300,6 +304,12 @@ __global__ __launch_bounds__(kThreads, 1) void lamp_attn_kernel(AttnArgs a) {
     if (active) {
         if constexpr (!kPlain) {
             c8 = (float)((double)a.q_scale[q_head] * (double)a.k_scale[kv_head] * a.l_d);
+            // with 8-bit logits everything after the rounding reads logits
+            // directly: the accumulator factor becomes 1
+            if constexpr (kLogit8) {
+                c8_log = c8;
+                c8 = 1.0f;
+            }
             a2 = acc_threshold(a.t2, c8);
             inv_c8 = 1.0f / c8;
         }
@@ -420,10 +430,28 @@ __global__ __launch_bounds__(kThreads, 1) void lamp_attn_kernel(AttnArgs a) {
         }
     };
 
+    // (2') 8-bit logits: s = e4m3(c8 acc), magnitudes clamped to 448 first
+    // (e4m3fn saturates there), nearest even, back in fp32 exactly
+    auto round_logits = [&](v4f (&s)[kQG][4]) __attribute__((always_inline)) {
+        if constexpr (kLogit8) {
+#pragma unroll
+            for (int qg = 0; qg < kQG; ++qg)
+#pragma unroll
+                for (int kb = 0; kb < 4; ++kb) {
+                    float y[4];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) y[i] = s[qg][kb][i] * c8_log;
+                    const uint32_t w = cvt_pk_e4m3<true>(y[2], y[3], cvt_pk_e4m3<false>(y[0], y[1], __float_as_uint(y[0])));
+                    const v2f lo = e4m3x2_to_f32x2<false>(w), hi = e4m3x2_to_f32x2<true>(w);
+                    s[qg][kb] = v4f{lo[0], lo[1], hi[0], hi[1]};
+                }
+        }
+    };
+
     // ---- per-tile vector state ---------------------------------------------------------
     float alpha[kQG], m_use[kQG];
     float smax[kQG][4];                 // per (lane, sub-block) maxima of the 8-bit accumulators
-    float smin[kMode == 2 ? kQG : 1][4];    // and minima, when the first stage is off
+    float smin[kTest == 2 ? kQG : 1][4];    // and minima, when the first stage is off
     uint32_t vis[kQG];                  // masked tiles: bit kb*4+i = entry visible
 
     // (2)-(3): running max and 8-bit exponentials of tile t, straight-line code.
@@ -461,7 +489,7 @@ __global__ __launch_bounds__(kThreads, 1) void lamp_attn_kernel(AttnArgs a) {
                     }
                 }
                 smax[qg][kb] = __builtin_fmaxf(__builtin_fmaxf(v[0], v[1]), __builtin_fmaxf(v[2], v[3]));
-                if constexpr (kMode == 2)
+                if constexpr (kTest == 2)
                     smin[qg][kb] = __builtin_fminf(__builtin_fminf(w[0], w[1]), __builtin_fminf(w[2], w[3]));
             }
             float mx = __builtin_fmaxf(__builtin_fmaxf(smax[qg][0], smax[qg][1]),
@@ -521,7 +549,7 @@ __global__ __launch_bounds__(kThreads, 1) void lamp_attn_kernel(AttnArgs a) {
     auto test = [&](const v4f (&s)[kQG][4], auto masked_tag) __attribute__((always_inline)) -> uint32_t {
         constexpr bool kMasked = decltype(masked_tag)::value;
         uint64_t hit[4] = {0, 0, 0, 0};
-        if constexpr (kMode == 1) {
+        if constexpr (kTest == 1) {
             bool slow = false;
 #pragma unroll
             for (int qg = 0; qg < kQG; ++qg) {
@@ -549,7 +577,7 @@ __global__ __launch_bounds__(kThreads, 1) void lamp_attn_kernel(AttnArgs a) {
                             hit[kb] |= h;
                         }
             }
-        } else if constexpr (kMode == 2) {
+        } else if constexpr (kTest == 2) {
             // first stage off: every visible entry is active; |acc| >= a2 holds
             // for some entry iff the sub-block maximum or minus its minimum does
 #pragma unroll
@@ -668,6 +696,7 @@ __global__ __launch_bounds__(kThreads, 1) void lamp_attn_kernel(AttnArgs a) {
             load_vt(t + 1);
             uint32_t flags = 0;
             if (w_cur) {
+                round_logits(S);
                 if (full) softmax(S, P, t, std::integral_constant<bool, false>{});
                 else softmax(S, P, t, std::integral_constant<bool, true>{});
                 rescale();
@@ -730,6 +759,7 @@ __global__ __launch_bounds__(kThreads, 1) void lamp_attn_kernel(AttnArgs a) {
             // vector work of tile t
             if (w_prev) pv(P, t - 1);
             if (w_cur) {
+                round_logits(S);
                 if (full) softmax(S, P, t, std::integral_constant<bool, false>{});
                 else softmax(S, P, t, std::integral_constant<bool, true>{});
             }
@@ -833,10 +863,12 @@ hipError_t launch_d(const Shape& sh, const AttnParams& p, hipStream_t st) {
     size_t lds = Cfg<D>::kLdsBytes;
     const bool dump = p.dump_s != nullptr && p.dump_p != nullptr;
     using Fn = void (*)(AttnArgs);
-    static const Fn table[2][3] = {
-        {lamp_attn_kernel<D, false, 0>, lamp_attn_kernel<D, false, 1>, lamp_attn_kernel<D, false, 2>},
-        {lamp_attn_kernel<D, true, 0>, lamp_attn_kernel<D, true, 1>, lamp_attn_kernel<D, true, 2>}};
-    Fn fn = table[dump ? 1 : 0][a.test_mode];
+    static const Fn table[2][2][3] = {
+        {{lamp_attn_kernel<D, false, 0>, lamp_attn_kernel<D, false, 1>, lamp_attn_kernel<D, false, 2>},
+         {lamp_attn_kernel<D, true, 0>, lamp_attn_kernel<D, true, 1>, lamp_attn_kernel<D, true, 2>}},
+        {{lamp_attn_kernel<D, false, 4>, lamp_attn_kernel<D, false, 5>, lamp_attn_kernel<D, false, 6>},
+         {lamp_attn_kernel<D, true, 4>, lamp_attn_kernel<D, true, 5>, lamp_attn_kernel<D, true, 6>}}};
+    Fn fn = table[p.logit8 ? 1 : 0][dump ? 1 : 0][a.test_mode];
     if (p.plain) {
         if constexpr (Cfg<D>::kPP) {
             fn = dump ? lamp_attn_kernel<D, true, 3> : lamp_attn_kernel<D, false, 3>;

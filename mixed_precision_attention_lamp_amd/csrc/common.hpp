@@ -22,6 +22,7 @@ typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef float v2f __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ float bf16_bits_to_float(uint32_t h) {
     return __uint_as_float(h << 16);
@@ -48,6 +49,12 @@ template <bool Hi>
 __device__ __forceinline__ uint32_t e4m3x2_to_bf16x2(uint32_t w) {
     v2bf r = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, Hi);
     return __builtin_bit_cast(uint32_t, r);
+}
+
+// Two e4m3 codes (low or high 16 bits of w) -> two fp32 values, exact.
+template <bool Hi>
+__device__ __forceinline__ v2f e4m3x2_to_f32x2(uint32_t w) {
+    return __builtin_amdgcn_cvt_pk_f32_fp8((int)w, Hi);
 }
 
 // fp32 -> bf16, round to nearest even (hardware conversion).

@@ -56,6 +56,7 @@ struct AttnParams {
     float t2;               // second-stage threshold on |log2-domain logit|
     int causal, window;
     int plain = 0;          // 1: plain bf16 FlashAttention (no 8-bit pass; D <= 128)
+    int logit8 = 0;         // 1: log2-domain logits rounded to e4m3 before use
 };
 
 // The forward attention kernel (16-bit recompute inside the tile loop).

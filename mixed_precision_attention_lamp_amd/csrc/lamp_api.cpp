@@ -155,7 +155,8 @@ Layout workspace_layout(const lamp::Shape& sh) {
 // plain = 1: plain bf16 FlashAttention (delta and tau unused).
 static int attn_fwd_impl(const void* q, const void* k, const void* v, float* out, int B, int Hq, int Hkv,
                          int S, int D, int causal, int window, float delta, float tau,
-                         uint8_t* subblock_mask_out, float* dump_s, uint16_t* dump_p, int plain) {
+                         uint8_t* subblock_mask_out, float* dump_s, uint16_t* dump_p, int plain,
+                         int logit8) {
     if (!q || !k || !v || !out) return fail(LAMP_ERR_INVALID, "q, k, v and out must be non-null");
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
         return fail(LAMP_ERR_INVALID, "q, k, v and out must be 16-byte aligned");
@@ -215,6 +216,7 @@ static int attn_fwd_impl(const void* q, const void* k, const void* v, float* out
     p.causal = causal; p.window = window;
     p.dump_s = dump_s; p.dump_p = dump_p;
     p.plain = plain;
+    p.logit8 = logit8;
     e = lamp::launch_attention(sh, p, g_stream);
     if (e != hipSuccess) return hip_fail(e, "attention launch");
     if (ev) (void)hipEventRecord(ev[2], g_stream);
@@ -227,22 +229,43 @@ int lamp_attn_fwd(const void* q, const void* k, const void* v, float* out, int B
                   int S, int D, int causal, int window, float delta, float tau,
                   uint8_t* subblock_mask_out) {
     return attn_fwd_impl(q, k, v, out, B, Hq, Hkv, S, D, causal, window, delta, tau, subblock_mask_out,
-                         nullptr, nullptr, 0);
+                         nullptr, nullptr, 0, 0);
+}
+
+int lamp_attn_fwd_logit8(const void* q, const void* k, const void* v, float* out, int B, int Hq, int Hkv,
+                         int S, int D, int causal, int window, float delta, float tau,
+                         uint8_t* subblock_mask_out) {
+    return attn_fwd_impl(q, k, v, out, B, Hq, Hkv, S, D, causal, window, delta, tau, subblock_mask_out,
+                         nullptr, nullptr, 0, 1);
 }
 
 int lamp_attn_fwd_bf16(const void* q, const void* k, const void* v, float* out, int B, int Hq, int Hkv,
                        int S, int D, int causal, int window, uint8_t* subblock_mask_out) {
     return attn_fwd_impl(q, k, v, out, B, Hq, Hkv, S, D, causal, window, 0.0f, 0.0f, subblock_mask_out,
-                         nullptr, nullptr, 1);
+                         nullptr, nullptr, 1, 0);
+}
+
+static int attn_dump_impl(const void* q, const void* k, const void* v, float* out, int B, int Hq, int Hkv,
+                          int S, int D, int causal, int window, float delta, float tau,
+                          uint8_t* subblock_mask_out, float* acc8_out, uint16_t* p_out, int logit8) {
+    if (!acc8_out || !p_out) return fail(LAMP_ERR_INVALID, "acc8_out and p_out must be non-null");
+    if (S > 2048) return fail(LAMP_ERR_UNSUPPORTED, "debug dump needs S <= 2048 (got %d)", S);
+    return attn_fwd_impl(q, k, v, out, B, Hq, Hkv, S, D, causal, window, delta, tau, subblock_mask_out,
+                         acc8_out, p_out, 0, logit8);
 }
 
 int lamp_debug_attn_dump(const void* q, const void* k, const void* v, float* out, int B, int Hq, int Hkv,
                          int S, int D, int causal, int window, float delta, float tau,
                          uint8_t* subblock_mask_out, float* acc8_out, uint16_t* p_out) {
-    if (!acc8_out || !p_out) return fail(LAMP_ERR_INVALID, "acc8_out and p_out must be non-null");
-    if (S > 2048) return fail(LAMP_ERR_UNSUPPORTED, "debug dump needs S <= 2048 (got %d)", S);
-    return attn_fwd_impl(q, k, v, out, B, Hq, Hkv, S, D, causal, window, delta, tau, subblock_mask_out,
-                         acc8_out, p_out, 0);
+    return attn_dump_impl(q, k, v, out, B, Hq, Hkv, S, D, causal, window, delta, tau, subblock_mask_out,
+                          acc8_out, p_out, 0);
+}
+
+int lamp_debug_attn_dump_logit8(const void* q, const void* k, const void* v, float* out, int B, int Hq,
+                                int Hkv, int S, int D, int causal, int window, float delta, float tau,
+                                uint8_t* subblock_mask_out, float* logit8_out, uint16_t* p_out) {
+    return attn_dump_impl(q, k, v, out, B, Hq, Hkv, S, D, causal, window, delta, tau, subblock_mask_out,
+                          logit8_out, p_out, 1);
 }
 
 int lamp_set_timing(int enable) {

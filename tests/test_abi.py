@@ -23,7 +23,8 @@ def test_exports_every_declared_symbol(lib):
     assert {"lamp_attn_fwd", "lamp_subblock_stats", "lamp_quantize_qk", "lamp_set_stream",
             "lamp_last_error", "lamp_release_workspace", "lamp_version",
             "lamp_debug_convert", "lamp_set_timing", "lamp_read_timing",
-            "lamp_debug_attn_dump", "lamp_attn_fwd_bf16"} <= set(names)
+            "lamp_debug_attn_dump", "lamp_attn_fwd_bf16", "lamp_attn_fwd_logit8",
+            "lamp_debug_attn_dump_logit8"} <= set(names)
     out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
     exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
@@ -99,3 +100,16 @@ def test_bf16_baseline_rejects_before_hip(lib):
     assert lib.lamp_attn_fwd_bf16(ALIGNED, ALIGNED, ALIGNED, ALIGNED, 1, 2, 1, 128, 256, 1, 0, None) == -2
     assert "D <= 128" in lib.lamp_last_error().decode()
     assert lib.lamp_attn_fwd_bf16(ALIGNED, ALIGNED, ALIGNED, ALIGNED, 1, 3, 2, 128, 128, 1, 0, None) == -1
+
+
+def test_logit8_variant_rejects_before_hip(lib):
+    # the 8-bit-logit variant validates its arguments as lamp_attn_fwd does
+    f = lib.lamp_attn_fwd_logit8
+    assert f(ALIGNED, ALIGNED, ALIGNED, ALIGNED, 1, 2, 1, 128, 96, 1, 0, 0.0039, 0.5, None) == -2
+    assert f(ALIGNED, ALIGNED, ALIGNED, ALIGNED, 1, 2, 1, 128, 128, 1, 0, math.nan, 0.5, None) == -1
+    assert "NaN" in lamp.lamp_last_error()
+    assert f(None, ALIGNED, ALIGNED, ALIGNED, 1, 2, 1, 128, 128, 1, 0, 0.0039, 0.5, None) == -1
+    d = lib.lamp_debug_attn_dump_logit8
+    assert d(ALIGNED, ALIGNED, ALIGNED, ALIGNED, 1, 1, 1, 64, 64, 1, 0, 0.0, 0.5, None, None, ALIGNED) == -1
+    assert d(ALIGNED, ALIGNED, ALIGNED, ALIGNED, 1, 1, 1, 4096, 64, 1, 0, 0.0, 0.5, None, ALIGNED,
+             ALIGNED) == -2

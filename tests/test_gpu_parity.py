@@ -19,8 +19,9 @@ from oracle import lamp as L
 from oracle.formats import (bf16_bits_to_f64, e4m3_decode, e4m3_encode, exp2_f32, round_bf16,
                             round_e4m3)
 
-from parity import (EPS_ACC8, assert_parity, assert_parity_plain, compare, compare_plain,
-                    fragile_alternatives, run_gpu, say, to_device)
+from parity import (EPS_ACC8, assert_parity, assert_parity_logit8, assert_parity_plain, compare,
+                    compare_logit8, compare_plain, fragile_alternatives, logit8_unit, run_gpu, say,
+                    to_device)
 
 pytestmark = pytest.mark.gpu
 
@@ -287,6 +288,84 @@ def test_plain_bf16_rejects_d256():
     q, k, v = make_inputs(1, 1, 1, 64, 256, 87, "plain")
     with pytest.raises(lamp.LampError):
         lamp.attention_bf16(to_device(q), to_device(k), to_device(v), True, 0)
+
+
+# --------------------------------------------------------------------------
+# the 8-bit-logit variant
+# --------------------------------------------------------------------------
+LOGIT8 = [
+    # B, Hq, Hkv, S, D, causal, window, delta, tau, structure, seed
+    (1, 1, 1, 256, 64, 1, 0, 2 ** -8, 2 ** -1, "sinks", 91),
+    (1, 4, 1, 300, 128, 1, 0, 2 ** -8, 2 ** -1, "channels", 92),    # G = 4, ragged tail
+    (2, 8, 2, 200, 128, 1, 0, 2 ** -8, 2 ** -3, "channels", 93),    # G = 4, B = 2
+    (1, 3, 3, 130, 128, 0, 0, 2 ** -8, 2 ** -1, "channels", 94),    # non-causal
+    (1, 2, 2, 333, 128, 1, 100, 2 ** -8, 2 ** -1, "channels", 95),  # sliding window
+    (1, 4, 4, 257, 64, 1, 64, 0.0, 2 ** -2, "channels", 96),        # first stage off
+    (1, 2, 1, 260, 128, 1, 0, 2 ** -8, np.inf, "channels", 97),     # second stage off
+    (1, 4, 1, 500, 128, 1, 0, 2 ** -8, 2 ** -5, "channels+drift", 98),
+    (1, 2, 1, 200, 256, 1, 0, 2 ** -8, 2 ** -1, "channels", 99),    # D = 256
+    (1, 3, 3, 290, 256, 1, 100, 2 ** -4, 2 ** -2, "channels", 100), # D = 256, window
+    (1, 1, 1, 1, 64, 1, 0, 2 ** -8, 2 ** -1, "plain", 101),         # S = 1
+]
+
+
+@pytest.mark.parametrize("case", LOGIT8)
+def test_logit8_parity_small(case):
+    B, Hq, Hkv, S, D, causal, window, delta, tau, st, seed = case
+    q, k, v = make_inputs(B, Hq, Hkv, S, D, seed, st)
+    assert_parity_logit8(compare_logit8(q, k, v, causal, window, delta, tau, label=str(case)))
+
+
+@pytest.mark.parametrize("case", [LOGIT8[1], LOGIT8[5], LOGIT8[8]])
+def test_logit8_dump(case):
+    """Every 8-bit logit the device uses is an e4m3 value within the
+    admissible range of the oracle's fp32 logit, and every weight that differs
+    from the oracle's (replayed with the device's flags) is one that the
+    protocol's windows allow to round the other way."""
+    import mixed_precision_attention_lamp_amd as lamp
+    B, Hq, Hkv, S, D, causal, window, delta, tau, st, seed = case
+    q, k, v = make_inputs(B, Hq, Hkv, S, D, seed, st)
+    nT = L.n_tiles(S)
+    out = torch.empty((B, Hq, S, D), dtype=torch.float32, device="cuda")
+    mask = torch.empty((B, Hq, nT, nT), dtype=torch.uint8, device="cuda")
+    s8 = torch.full((B, Hq, S, S), float("nan"), dtype=torch.float32, device="cuda")
+    pw = torch.zeros((B, Hq, S, S), dtype=torch.int16, device="cuda")
+    lamp.lamp_debug_attn_dump_logit8(to_device(q), to_device(k), to_device(v), out, causal, window,
+                                     delta, tau, mask, s8, pw)
+    torch.cuda.synchronize()
+    s8_g = s8.cpu().numpy().astype(np.float64)
+    p_g = bf16_bits_to_f64(pw.cpu().numpy().view(np.uint16))
+    mask_g = mask.cpu().numpy()
+    ctx = L.prepare(q, k, v, causal, window, delta, tau, logit8=True)
+    n_vis = n_flip = n_p_bad = n_p_unexplained = n_outside = n_off_grid = 0
+    for (b, h, r) in L.all_units(B, Hq, S):
+        ov = {t: int(mask_g[b, h, r, t]) & 0x0F for t in range(nT)}
+        w = logit8_unit(ctx, b, h, r, override=ov)
+        keep = ~w["max_fragile"]
+        for rec in w["trace"][:-1]:
+            t, vis = rec["t"], rec["vis"]
+            rows = np.arange(r * 64, r * 64 + vis.shape[0])
+            gs = s8_g[b, h][np.ix_(rows, rec["cols"])]
+            gp = p_g[b, h][np.ix_(rows, rec["cols"])]
+            n_vis += int(vis.sum())
+            n_off_grid += int((e4m3_decode(e4m3_encode(gs[vis])) != gs[vis]).sum())
+            n_outside += int((vis & ((gs < w["lo8"][t]) | (gs > w["hi8"][t]))).sum())
+            n_flip += int((vis & (gs != rec["s2"])).sum())
+            bad = vis & keep[:, None] & (gp != rec["p"])
+            n_p_bad += int(bad.sum())
+            n_p_unexplained += int((bad & (w["alt"][t] == 0)).sum())
+    say(f"[dump-logit8] {case}: visible {n_vis}; 8-bit logits off the e4m3 grid {n_off_grid}, "
+        f"outside their window {n_outside}, rounded the other way {n_flip}; weights differing "
+        f"{n_p_bad} (rows with a fixed max), unexplained {n_p_unexplained}")
+    assert n_off_grid == 0 and n_outside == 0 and n_p_unexplained == 0
+
+
+def test_logit8_parity_full_size():
+    """The Qwen3-8B-shaped workload in one call, sampled units."""
+    q, k, v, cfg = make_config_inputs("qwen3-8b")
+    units = _sample_units(cfg["B"], cfg["Hq"], cfg["S"], 8, 11)
+    assert_parity_logit8(compare_logit8(q, k, v, cfg["causal"], cfg["window"], 2 ** -8, 2 ** -1,
+                                        units=units, label="qwen3-8b sampled"))
 
 
 # --------------------------------------------------------------------------
