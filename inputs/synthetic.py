@@ -15,6 +15,9 @@ shapes.  Recipe (numpy PCG64, ``default_rng(seed)``), draw order fixed:
    1, and key j < 16 gets 6 sqrt(D) (1 - j/16) u added, which lifts the logit
    of key j by about 6 (1 - j/16) (keys biased toward the first positions).
 4. Cast to bf16 with torch's round-to-nearest-even; returned as uint16 bits.
+
+Decode inputs (Sq < S query rows, the last Sq positions of the sequence)
+draw Q as [B,Hq,Sq,D] in step 1; everything else is unchanged.
 """
 import numpy as np
 import torch
@@ -39,6 +42,10 @@ CONFIGS = {
     "qwen3-30b-a3b": dict(B=1, Hq=32, Hkv=4, S=32768, D=128, causal=1, window=0,
                           structure="channels+drift", seed=5,
                           desc="Qwen3-30B-A3B-shaped long-context GQA prefill, S=32768"),
+    # decode: Sq query rows (the last Sq positions) against S cached keys
+    "qwen3-8b-decode": dict(B=8, Hq=32, Hkv=8, S=16384, Sq=16, D=128, causal=1, window=0,
+                            structure="channels", seed=6,
+                            desc="Qwen3-8B-shaped decode, 16 queries against 16384 cached keys, B=8"),
 }
 
 
@@ -47,10 +54,11 @@ def _to_bf16_bits(x):
     return t.view(torch.int16).numpy().view(np.uint16)
 
 
-def make_inputs(B, Hq, Hkv, S, D, seed, structure="plain", **_):
-    """Draw (q_bits, k_bits, v_bits) as uint16 bf16 bit patterns."""
+def make_inputs(B, Hq, Hkv, S, D, seed, structure="plain", Sq=None, **_):
+    """Draw (q_bits, k_bits, v_bits) as uint16 bf16 bit patterns; Q has Sq
+    rows (default S)."""
     rng = np.random.default_rng(seed)
-    q = rng.standard_normal((B, Hq, S, D), dtype=np.float32)
+    q = rng.standard_normal((B, Hq, S if Sq is None else Sq, D), dtype=np.float32)
     k = rng.standard_normal((B, Hkv, S, D), dtype=np.float32)
     v = rng.standard_normal((B, Hkv, S, D), dtype=np.float32)
     if structure == "sinks":

@@ -214,3 +214,104 @@ def brute_lamp(q_bits, k_bits, v_bits, causal, window, delta, tau, logit8=False)
                 for i in rows:
                     out[b][hq][i] = [float(to_f32(o / ell[i])) for o in acc_o[i]]
     return out, mask
+
+
+def brute_decode(q_bits, k_bits, v_bits, causal, window, delta, tau, tiles_per_split):
+    """Split-KV decode, one entry at a time in exact rationals.
+
+    q_bits [B][Hq][Sq][D] are the queries at positions Skv - Sq .. Skv - 1 of
+    k_bits / v_bits [B][Hkv][Skv][D].  The KV tiles are cut into runs of
+    ``tiles_per_split``; each run is processed from an empty state and the
+    runs are merged exactly.  Returns (out as nested lists of float, mask
+    dict {(b, hq, t): byte} for visited tiles).
+    """
+    B, Hq, Sq, D = (len(q_bits), len(q_bits[0]), len(q_bits[0][0]), len(q_bits[0][0][0]))
+    Hkv, Skv = len(k_bits[0]), len(k_bits[0][0])
+    G = Hq // Hkv
+    q = [[[[_bf16(x) for x in row] for row in h] for h in bb] for bb in q_bits]
+    k = [[[[_bf16(x) for x in row] for row in h] for h in bb] for bb in k_bits]
+    v = [[[[_bf16(x) for x in row] for row in h] for h in bb] for bb in v_bits]
+
+    def scales(rows):
+        a = max(abs(x) for row in rows for x in row)
+        if a == 0:
+            return Fraction(1), Fraction(1)
+        return to_f32(a / 448), to_f32(Fraction(448) / a)
+
+    L = Fraction(LOG2E / math.sqrt(D))
+    c16 = to_f32(L)
+    T2 = to_f32(Fraction(16 * float(tau) * LOG2E)) if math.isfinite(16 * float(tau) * LOG2E) \
+        else (math.inf if tau > 0 else -math.inf)
+    off = Skv - Sq
+
+    def seen(i, j):
+        """Query row i (position off + i) sees key j."""
+        p = off + i
+        if j >= Skv or (causal and j > p) or (window > 0 and p - j >= window):
+            return False
+        return True
+
+    nT = (Skv + 63) // 64
+    out = [[None] * Hq for _ in range(B)]
+    mask = {}
+    for b in range(B):
+        for hq in range(Hq):
+            hk = hq // G
+            sq, iq = scales(q[b][hq])
+            sk, ik = scales(k[b][hk])
+            q8 = [[to_e4m3(to_f32(x * iq)) for x in row] for row in q[b][hq]]
+            k8 = [[to_e4m3(to_f32(x * ik)) for x in row] for row in k[b][hk]]
+            c8 = to_f32(Fraction(float(sq) * float(sk) * float(L)))
+            runs = []                       # per split: {i: (m, ell, acc)}
+            for t0 in range(0, nT, tiles_per_split):
+                m = {i: -math.inf for i in range(Sq)}
+                ell = {i: Fraction(0) for i in range(Sq)}
+                acc = {i: [Fraction(0)] * D for i in range(Sq)}
+                for t in range(t0, min(t0 + tiles_per_split, nT)):
+                    keys = range(64 * t, 64 * t + 64)
+                    pairs = [(i, j) for i in range(Sq) for j in keys if seen(i, j)]
+                    if not pairs:
+                        continue
+                    s2 = {(i, j): to_f32(to_f32(sum(q8[i][d] * k8[j][d] for d in range(D))) * c8)
+                          for (i, j) in pairs}
+                    m_new = dict(m)
+                    for (i, j), x in s2.items():
+                        m_new[i] = max(m_new[i], x)
+                    p, flags = {}, [False] * 4
+                    for (i, j) in pairs:
+                        a8 = to_f32(sum(q8[i][d] * k8[j][d] for d in range(D)))
+                        p8 = to_e4m3(_exp2_f32(to_f32(a8 * c8 - m_new[i])))
+                        p[i, j] = p8
+                        if ((delta <= 0) or (p8 >= Fraction(delta))) and abs(s2[i, j]) >= T2:
+                            flags[(j - 64 * t) // 16] = True
+                    for (i, j) in pairs:
+                        if flags[(j - 64 * t) // 16]:
+                            a16 = to_f32(sum(q[b][hq][i][d] * k[b][hk][j][d] for d in range(D)))
+                            p[i, j] = to_bf16(_exp2_f32(to_f32(a16 * c16 - m_new[i])))
+                    for i in range(Sq):
+                        if m_new[i] == -math.inf:
+                            continue
+                        f = Fraction(0) if m[i] == -math.inf else \
+                            Fraction(math.pow(2.0, float(m[i] - m_new[i])))
+                        ell[i] *= f
+                        acc[i] = [f * o for o in acc[i]]
+                        for j in keys:
+                            if (i, j) in p:
+                                ell[i] += p[i, j]
+                                acc[i] = [o + p[i, j] * v[b][hk][j][d] for d, o in enumerate(acc[i])]
+                        m[i] = m_new[i]
+                    mask[b, hq, t] = 0x80 | sum(int(x) << c for c, x in enumerate(flags))
+                runs.append((m, ell, acc))
+            rows = []
+            for i in range(Sq):
+                top = max(r[0][i] for r in runs)
+                num, den = [Fraction(0)] * D, Fraction(0)
+                for m, ell, acc in runs:
+                    if m[i] == -math.inf:
+                        continue
+                    w = Fraction(math.pow(2.0, float(m[i] - top)))
+                    den += w * ell[i]
+                    num = [n + w * o for n, o in zip(num, acc[i])]
+                rows.append([float(to_f32(n / den)) for n in num])
+            out[b][hq] = rows
+    return out, mask

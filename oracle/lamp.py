@@ -180,16 +180,20 @@ def fragile_flags(e, s2, vis, delta, T2, k):
 # --------------------------------------------------------------------------
 # The forward pass of one unit (batch b, query head hq, row block r)
 # --------------------------------------------------------------------------
-def run_unit(ctx, b, hq, r, flag_override=None, trace=None):
+def run_unit(ctx, b, hq, r, flag_override=None, trace=None, tiles=None):
     """Process one 64-row query block through its visible KV tiles.
 
     Returns (out rows fp32 values [n, D], {t: mask byte}).  ``flag_override``
     maps t -> 4-bit flags replacing the computed ones (used to replay a run
     whose flags are given).  ``trace`` (a list) receives per-tile records.
+    ``tiles`` restricts the KV tiles visited (default: all, ascending).
+    Query row i of the slab sits at sequence position i + q_off (q_off > 0
+    when the queries are the last rows of a longer key sequence).
     """
     S, D, G = ctx["S"], ctx["D"], ctx["G"]
     hk = hq // G
-    rows = np.arange(r * BR, min(r * BR + BR, S))
+    rows = np.arange(r * BR, min(r * BR + BR, ctx["Sq"]))   # query rows of the slab
+    pos = rows + ctx["q_off"]                               # their sequence positions
     nr = rows.size
     c8, c16 = logit_constants(D, ctx["sq"][b, hq], ctx["sk"][b, hk])
     T2 = ctx["T2"]
@@ -201,9 +205,9 @@ def run_unit(ctx, b, hq, r, flag_override=None, trace=None):
     ell = np.zeros(nr)                    # running sum of weights (fp64)
     O = np.zeros((nr, D))                 # running weighted sum of V rows (fp64)
     mask = {}
-    for t in range(n_tiles(S)):
+    for t in (tiles if tiles is not None else range(n_tiles(S))):
         cols = np.arange(t * BC, min(t * BC + BC, S))
-        vis = visible(rows, cols, ctx["causal"], ctx["window"])
+        vis = visible(pos, cols, ctx["causal"], ctx["window"])
         if not vis.any():
             continue
         k8 = ctx["k8"][b, hk, cols]
@@ -356,10 +360,12 @@ class PerHead:
 def prepare(q_bits, k_bits, v_bits, causal, window, delta, tau, logit8=False):
     """Scales of Q and K, and per-head access to everything the units read
     (the e4m3 values of Q and K, and the bf16 values of Q, K and V).
-    ``logit8`` selects the variant whose log2-domain logits are e4m3 values."""
-    B, Hq, S, D = q_bits.shape
-    Hkv = k_bits.shape[1]
-    assert Hq % Hkv == 0 and k_bits.shape == v_bits.shape == (B, Hkv, S, D)
+    ``logit8`` selects the variant whose log2-domain logits are e4m3 values.
+    Q may hold fewer rows than K and V (decode): they are then the last
+    positions of the sequence."""
+    B, Hq, Sq, D = q_bits.shape
+    Hkv, S = k_bits.shape[1], k_bits.shape[2]
+    assert Hq % Hkv == 0 and k_bits.shape == v_bits.shape == (B, Hkv, S, D) and Sq <= S
     sq, iq = head_scales(q_bits)
     sk, ik = head_scales(k_bits)
 
@@ -370,7 +376,7 @@ def prepare(q_bits, k_bits, v_bits, causal, window, delta, tau, logit8=False):
     def bf16_slab(bits):
         return lambda b, h: bf16_bits_to_f64(bits[b, h])
 
-    return dict(B=B, Hq=Hq, Hkv=Hkv, S=S, D=D, G=Hq // Hkv,
+    return dict(B=B, Hq=Hq, Hkv=Hkv, S=S, D=D, G=Hq // Hkv, Sq=Sq, q_off=S - Sq,
                 causal=bool(causal), window=int(window),
                 delta=float(delta), T2=tau_threshold(tau), logit8=bool(logit8),
                 q8=PerHead(e4m3_slab(q_bits, iq)), k8=PerHead(e4m3_slab(k_bits, ik)), sq=sq, sk=sk,
@@ -406,6 +412,70 @@ def lamp_forward(q_bits, k_bits, v_bits, causal=True, window=0, delta=2.0 ** -8,
         out[b, hq, r * BR:r * BR + o.shape[0]] = o.astype(np.float32)
         for t, byte in mk.items():
             mask[b, hq, r, t] = byte
+    return out, mask
+
+
+# --------------------------------------------------------------------------
+# Decode: a few query rows against a long key sequence, split over KV tiles
+# --------------------------------------------------------------------------
+def split_tiles(nT, tiles_per_split):
+    """The KV-tile ranges of the splits: contiguous, ascending, each
+    ``tiles_per_split`` tiles long except possibly the last."""
+    return [range(t0, min(t0 + tiles_per_split, nT)) for t0 in range(0, nT, tiles_per_split)]
+
+
+def merge_splits(parts):
+    """Combine per-split (m, ell, O) of the same rows: with M the largest m,
+    out = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) ell_s (fp64, rounded once
+    to fp32).  A split whose running max is -inf (no visible key) weighs 0."""
+    M = np.max(np.stack([m for m, _, _ in parts]), axis=0)
+    num = np.zeros_like(parts[0][2])
+    den = np.zeros_like(parts[0][1])
+    for m, ell, O in parts:
+        w = np.where(np.isneginf(m), 0.0, np.exp2(np.where(np.isneginf(m), 0.0, m) -
+                                                 np.where(np.isneginf(M), 0.0, M)))
+        num += w[:, None] * O
+        den += w * ell
+    with np.errstate(invalid="ignore", divide="ignore"):
+        return fl32(num / den[:, None])
+
+
+def decode_forward(q_bits, k_bits, v_bits, causal=True, window=0, delta=2.0 ** -8, tau=2.0 ** -1,
+                   tiles_per_split=None, heads=None, logit8=False):
+    """Split-KV decode (reading of the method for a few queries against a
+    long key sequence).
+
+    q_bits [B, Hq, Sq, D] holds the queries at the last Sq positions
+    (Skv - Sq .. Skv - 1) of k_bits / v_bits [B, Hkv, Skv, D]; Sq <= 64, so
+    the Sq rows of a head form one row block (the unit of the look-ahead
+    test).  The KV tiles are cut into contiguous splits of
+    ``tiles_per_split`` tiles (default: one split).  Each split runs the
+    method of ``run_unit`` on its own tiles from an empty state (its own
+    running max, sum and output); the splits are then merged exactly
+    (``merge_splits``).  Scales are the per-head amax scales of the Sq query
+    rows and of all Skv keys.
+
+    Returns (out fp32 [B, Hq, Sq, D] (heads not computed are NaN), mask uint8
+    [B, Hq, nT]: 0x80 | flags for visited tiles).
+    """
+    ctx = prepare(q_bits, k_bits, v_bits, causal, window, delta, tau, logit8)
+    B, Hq, Sq, S, D = ctx["B"], ctx["Hq"], ctx["Sq"], ctx["S"], ctx["D"]
+    assert Sq <= BR
+    nT = n_tiles(S)
+    tps = tiles_per_split if tiles_per_split else nT
+    out = np.full((B, Hq, Sq, D), np.nan, dtype=np.float32)
+    mask = np.zeros((B, Hq, nT), dtype=np.uint8)
+    for (b, hq) in (heads if heads is not None else [(b, h) for b in range(B) for h in range(Hq)]):
+        parts = []
+        for tr in split_tiles(nT, tps):
+            trace = []
+            with np.errstate(invalid="ignore", divide="ignore"):
+                _, mk = run_unit(ctx, b, hq, 0, trace=trace, tiles=tr)
+            fin = trace[-1]
+            parts.append((fin["m"], fin["ell"], fin["O"]))
+            for t, byte in mk.items():
+                mask[b, hq, t] = byte
+        out[b, hq] = merge_splits(parts).astype(np.float32)
     return out, mask
 
 
