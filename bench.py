@@ -4,6 +4,7 @@
                     [--delta D] [--tau T] [--no-cpu-baseline]
     python bench.py --copy-calibrate      # plain 1 GiB device copy (counter calibration)
     python bench.py --grid [--workload W] # speed/recompute curve over (delta, tau)
+    python bench.py --workload qwen3-8b-decode   # split-KV decode (lamp_attn_decode)
 
 A step is one lamp_attn_fwd call (quantisation pass, V transpose and the fused
 attention kernel) over one batch of seeded synthetic input already resident
@@ -35,8 +36,23 @@ COPY_BYTES = 1 << 30       # size of the calibration copy
 # by the same counter's reading for a plain copy of COPY_BYTES (see
 # profiles/attn_qwen3_8b_hbm_traffic.md).  Valid only for the kernel source
 # whose hash is recorded; any change to it makes the figure null.
-TRAFFIC = {"kernel_hash": "c6b3f2ee327894fc", "workload": "qwen3-8b", "delta": 2.0 ** -8, "tau": 2.0 ** -1,
-           "bytes_per_launch": 143762113.4}
+TRAFFIC = {"kernel_hash": "d173aea78b167779", "workload": "qwen3-8b", "delta": 2.0 ** -8, "tau": 2.0 ** -1,
+           "bytes_per_launch": 143855977.7}
+
+
+# The same for the decode kernel on the qwen3-8b-decode workload
+# (profiles/decode_qwen3_8b_hbm_traffic.md), library split.
+TRAFFIC_DECODE = {"kernel_hash": "a14361c8b945b249", "workload": "qwen3-8b-decode", "delta": 2.0 ** -8,
+                  "tau": 2.0 ** -1, "bytes_per_launch": 555436322.5}
+
+
+def decode_source_hash():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "mixed_precision_attention_lamp_amd", "csrc")
+    for name in ("decode.hip", "tiles.hpp", "common.hpp"):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def kernel_source_hash():
@@ -121,6 +137,178 @@ def cpu_baseline(q, k, v, cfg, delta, tau, budget_s, cores):
                 sample=f"{len(sample)} random (batch, head, 64-row block) units of the same "
                        f"workload ({flops / 1e9:.2f} GFLOP nominal), {wall:.1f} s wall",
                 wall_s=wall)
+
+
+# --------------------------------------------------------------------------
+# decode workloads (lamp_attn_decode)
+# --------------------------------------------------------------------------
+def decode_pairs_per_head(Sq, Skv, causal, window):
+    """Visible (query, key) pairs of one head; query i sits at Skv - Sq + i."""
+    p = np.arange(Skv - Sq, Skv, dtype=np.int64)
+    hi = p if causal else np.full(Sq, Skv - 1)
+    lo = np.maximum(0, p - window + 1) if window > 0 else np.zeros(Sq, dtype=np.int64)
+    return int(np.maximum(0, hi - lo + 1).sum())
+
+
+def decode_subblock_entries(Sq, Skv, causal, window):
+    """[nT, 4] visible entries per (tile, sub-block) of one head."""
+    nT = (Skv + 63) // 64
+    p = np.arange(Skv - Sq, Skv, dtype=np.int64)[:, None]
+    j = np.arange(nT * 64, dtype=np.int64)[None, :]
+    vis = j < Skv
+    if causal:
+        vis = vis & (j <= p)
+    if window > 0:
+        vis = vis & (p - j < window)
+    return vis.sum(axis=0).reshape(nT, 4, 16).sum(axis=2)
+
+
+def measure_decode(lamp, torch, tensors, shape, causal, window, delta, tau, tps, steps, warmup):
+    """Time `steps` lamp_attn_decode calls after `warmup`; returns the step
+    time, the decode (+ merge) kernel time and the scale pass time (HIP
+    events on the library's stream), FLOP counts and the recompute counts."""
+    qd, kd, vd, out, mask = tensors
+    B, Hq, Hkv, Sq, Skv, D = shape
+
+    def step():
+        lamp.lamp_attn_decode(qd, kd, vd, out, causal, window, delta, tau, tps, mask)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    lamp.lamp_set_timing(1)
+    lamp.lamp_read_timing()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for _ in range(steps):
+        step()
+    end.record()
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(end)
+    prep_ms, attn_ms, ncalls = lamp.lamp_read_timing()
+    lamp.lamp_set_timing(0)
+    m = mask.cpu().numpy()
+    ent = decode_subblock_entries(Sq, Skv, causal, window)            # [nT, 4]
+    bits = np.stack([(m >> c) & 1 for c in range(4)], axis=-1)         # [B, Hq, nT, 4]
+    visited = (m & 0x80) != 0
+    pairs = decode_pairs_per_head(Sq, Skv, causal, window) * B * Hq
+    flagged = int((bits * ent[None, None]).sum())
+    vsb = int(((ent[None, None] > 0) & visited[..., None]).sum())
+    fsb = int((bits * (ent[None, None] > 0)).sum())
+    return dict(ms_per_step=total_ms / steps, attn_ms=attn_ms / max(ncalls, 1),
+                prep_ms=prep_ms / max(ncalls, 1), pairs=pairs, f_nom=4.0 * D * pairs,
+                f_qk8=2.0 * D * pairs, f_pv=2.0 * D * pairs, f_qk16=2.0 * D * flagged,
+                stats=dict(r_sb=fsb / vsb if vsb else 0.0, r_e=flagged / pairs if pairs else 0.0,
+                           visited_subblocks=vsb, flagged_subblocks=fsb))
+
+
+def _oracle_decode_head(head):
+    """Worker: one (b, hq) decode head through the oracle (CPU baseline only)."""
+    from oracle import lamp as L
+    b, hq, tps = head
+    for tr in L.split_tiles(L.n_tiles(_CTX["S"]), tps):
+        with np.errstate(invalid="ignore", divide="ignore"):
+            L.run_unit(_CTX, b, hq, 0, tiles=tr)
+    return head
+
+
+def cpu_baseline_decode(q, k, v, cfg, delta, tau, tps, budget_s, cores):
+    """Time the oracle on sampled heads of the decode workload (reported baseline)."""
+    global _CTX
+    import multiprocessing as mp
+    from threadpoolctl import threadpool_limits
+    from oracle import lamp as L
+    threadpool_limits(1)
+    _CTX = L.prepare(q, k, v, cfg["causal"], cfg["window"], delta, tau)
+    B, Hq, Sq, D = q.shape
+    Skv = k.shape[2]
+    rng = np.random.default_rng(321)
+    heads = [(int(rng.integers(B)), int(rng.integers(Hq)), tps) for _ in range(4096)]
+    t0 = time.perf_counter()
+    _oracle_decode_head(heads[0])
+    one = max(time.perf_counter() - t0, 1e-3)
+    n = max(1, min(len(heads), int(budget_s * cores / one)))
+    sample = heads[:n]
+    t0 = time.perf_counter()
+    if cores > 1 and n > 1:
+        with mp.get_context("fork").Pool(min(cores, n)) as pool:
+            for _ in pool.imap_unordered(_oracle_decode_head, sample, chunksize=1):
+                pass
+    else:
+        for h in sample:
+            _oracle_decode_head(h)
+    wall = time.perf_counter() - t0
+    flops = 4.0 * D * decode_pairs_per_head(Sq, Skv, cfg["causal"], cfg["window"]) * len(sample)
+    return dict(value=flops / wall / 1e12, unit="TFLOP/s", cores=min(cores, n), kind="oracle",
+                sample=f"{len(sample)} random (batch, query head) decode heads of the same workload, "
+                       f"{tps} tiles per split ({flops / 1e9:.2f} GFLOP nominal), {wall:.1f} s wall")
+
+
+def run_decode(args, cfg, q, k, v):
+    """The decode bench line: lamp_attn_decode on a decode workload."""
+    B, Hq, Sq, D = q.shape
+    Hkv, Skv = k.shape[1], k.shape[2]
+    causal, window = cfg["causal"], cfg["window"]
+    # the library's split choice depends on the device; the CPU baseline
+    # needs it before the GPU is touched, so it asks in a child process
+    import subprocess
+    tps = int(subprocess.run(
+        [sys.executable, "-c", "import mixed_precision_attention_lamp_amd as l; "
+         f"print(l.lamp_decode_tiles_per_split({B}, {Hq}, {Hkv}, {Sq}, {Skv}, {D}))"],
+        capture_output=True, text=True, check=True, cwd=ROOT).stdout.strip())
+    cb = None
+    if not args.no_cpu_baseline:
+        cores = max(1, min(len(os.sched_getaffinity(0)), 16))
+        cb = cpu_baseline_decode(q, k, v, cfg, args.delta, args.tau, tps, args.cpu_budget, cores)
+    import torch
+    import mixed_precision_attention_lamp_amd as lamp
+    dev = torch.device("cuda:0")
+
+    def dev_t(x):
+        return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    qd, kd, vd = dev_t(q), dev_t(k), dev_t(v)
+    nT = lamp.n_tiles(Skv)
+    out = torch.empty((B, Hq, Sq, D), dtype=torch.float32, device=dev)
+    mask = torch.empty((B, Hq, nT), dtype=torch.uint8, device=dev)
+    m = measure_decode(lamp, torch, (qd, kd, vd, out, mask), (B, Hq, Hkv, Sq, Skv, D), causal, window,
+                       args.delta, args.tau, tps, args.steps, args.warmup)
+    n_split = (nT + tps - 1) // tps
+    # algorithmic bytes of the decode kernel and its merge: K and V read once
+    # (bf16), Q read, split results written and read back, output written
+    part = 4.0 * B * Hq * n_split * Sq * (D + 2)
+    kv_bytes = 2.0 * 2.0 * B * Hkv * Skv * D
+    alg_bytes = kv_bytes + 2.0 * B * Hq * Sq * D + 2.0 * part + 4.0 * B * Hq * Sq * D
+    achieved = alg_bytes / (m["attn_ms"] * 1e-3)
+    traffic = None
+    if (TRAFFIC_DECODE["kernel_hash"] == decode_source_hash() and TRAFFIC_DECODE["workload"] == args.workload
+            and TRAFFIC_DECODE["delta"] == args.delta and TRAFFIC_DECODE["tau"] == args.tau):
+        traffic = TRAFFIC_DECODE["bytes_per_launch"]
+    res = {
+        "metric": METRIC,
+        "value": m["f_nom"] / (m["ms_per_step"] * 1e-3) / 1e12,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": m["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "e4m3+bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{args.workload}: {cfg['desc']}", "B": B, "Hq": Hq, "Hkv": Hkv,
+                   "Sq": Sq, "Skv": Skv, "D": D, "causal": causal, "window": window,
+                   "delta": args.delta, "tau": args.tau, "tiles_per_split": tps, "splits": n_split},
+        "roofline": {"bound": "hbm", "achieved": achieved / 1e9, "peak": PEAK_HBM / 1e9, "unit": "GB/s",
+                     "frac": achieved / PEAK_HBM, "traffic": traffic},
+        "kernel_ms": {"decode_and_merge": m["attn_ms"], "scales": m["prep_ms"]},
+        "step_hbm_frac": (kv_bytes + 2.0 * B * Hkv * Skv * D) / (m["ms_per_step"] * 1e-3) / PEAK_HBM,
+        "recompute": {"r_sb": m["stats"]["r_sb"], "r_e": m["stats"]["r_e"]},
+        "cpu_baseline": cb,
+    }
+    print(json.dumps(res), flush=True)
 
 
 # The (delta, tau) grid of the pages' tables and figures, plus the two
@@ -230,6 +418,9 @@ def main():
     from inputs import make_config_inputs
 
     q, k, v, cfg = make_config_inputs(args.workload)
+    if "Sq" in cfg:
+        run_decode(args, cfg, q, k, v)
+        return
     B, Hq, S, D = q.shape
     Hkv = k.shape[1]
     causal, window = cfg["causal"], cfg["window"]

@@ -81,6 +81,37 @@ int lamp_attn_fwd_logit8(const void* q, const void* k, const void* v, float* out
                          int causal, int window, float delta, float tau,
                          uint8_t* subblock_mask_out);
 
+/* Decode: Sq query rows, the last positions (Skv - Sq .. Skv - 1) of a sequence,
+ * against all Skv cached keys ("LampAttention", abstract: the method per tile as
+ * in lamp_attn_fwd).  The Sq rows of a query head form the row block the
+ * look-ahead test flags.  The KV tiles (64 keys each) are cut into contiguous
+ * splits of tiles_per_split tiles; each split runs the tile loop from an empty
+ * state (its own running max, row sum and output) and the splits are merged:
+ * out = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s, M the largest running max.
+ * The split is part of the operation: the 8-bit exponentials of a split are taken
+ * against that split's running max.
+ *   q         bf16 device tensor [B, Hq, Sq, D]; k, v bf16 [B, Hkv, Skv, D].
+ *   out       fp32 device tensor [B, Hq, Sq, D].
+ *   causal, window, delta, tau as in lamp_attn_fwd, with query row i at
+ *             position Skv - Sq + i.
+ *   tiles_per_split  >= 1: KV tiles per split (clamped to the tile count);
+ *             0: the library's choice, lamp_decode_tiles_per_split.
+ *   subblock_mask_out  nullable; uint8 device tensor [B, Hq, nT], nT = ceil(Skv/64):
+ *             byte (b, hq, t) as in lamp_attn_fwd for the one row block.
+ * Sizes: 1 <= Sq <= 16, Sq <= Skv, Hq % Hkv == 0, Hq/Hkv <= 8, D in {64, 128, 256}
+ * (LAMP_ERR_UNSUPPORTED otherwise).  Per call the library workspace also holds
+ * B*Hq*n_split*Sq*(D+2) fp32 split results. */
+int lamp_attn_decode(const void* q, const void* k, const void* v, float* out,
+                     int B, int Hq, int Hkv, int Sq, int Skv, int D,
+                     int causal, int window, float delta, float tau,
+                     int tiles_per_split, uint8_t* subblock_mask_out);
+
+/* The tiles_per_split lamp_attn_decode uses when passed 0: the fewest tiles per
+ * split that still give one workgroup slot of the current device a split (two
+ * per compute unit, one when Hq/Hkv > 4 or D = 256); a negative error code for
+ * sizes lamp_attn_decode rejects.  Launches nothing. */
+int lamp_decode_tiles_per_split(int B, int Hq, int Hkv, int Sq, int Skv, int D);
+
 /* The 16-bit baseline: plain bf16 FlashAttention on the same tiles ("16-bit"
  * column of tables 1-6 read as a kernel; no 8-bit pass).  Logits are the bf16
  * products accumulated in fp32 on the matrix cores, the running row max comes

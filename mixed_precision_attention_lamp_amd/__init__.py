@@ -8,8 +8,9 @@ softmax and P.V.  All of it runs in the kernels of ``liblamp.so``; this
 package only marshals torch tensors into the C entry points (see _lib.py) and
 allocates outputs.
 """
-from ._lib import (LAMP_STATS_LEN, LampError, declared_symbols, lamp_attn_fwd,  # noqa: F401
-                   lamp_attn_fwd_bf16, lamp_attn_fwd_logit8, lamp_debug_attn_dump,
+from ._lib import (LAMP_STATS_LEN, LampError, declared_symbols, lamp_attn_decode,  # noqa: F401
+                   lamp_attn_fwd, lamp_attn_fwd_bf16, lamp_attn_fwd_logit8, lamp_debug_attn_dump,
+                   lamp_decode_tiles_per_split,
                    lamp_debug_attn_dump_logit8, lamp_debug_convert, lamp_last_error,
                    lamp_quantize_qk, lamp_read_timing, lamp_release_workspace, lamp_set_stream,
                    lamp_set_timing, lamp_subblock_stats, lamp_version, load)
@@ -47,6 +48,19 @@ def attention_bf16(q, k, v, causal=True, window=0, with_mask=True):
         nT = n_tiles(S)
         mask = torch.empty((B, Hq, nT, nT), dtype=torch.uint8, device=q.device)
     lamp_attn_fwd_bf16(q, k, v, out, int(causal), int(window), mask)
+    return out, mask
+
+
+def attention_decode(q, k, v, causal=True, window=0, delta=2.0 ** -8, tau=2.0 ** -1,
+                     tiles_per_split=0, with_mask=True):
+    """Allocate the outputs and run lamp_attn_decode; returns (out, mask or None)."""
+    import torch
+    B, Hq, Sq, D = q.shape
+    out = torch.empty((B, Hq, Sq, D), dtype=torch.float32, device=q.device)
+    mask = None
+    if with_mask:
+        mask = torch.empty((B, Hq, n_tiles(k.shape[2])), dtype=torch.uint8, device=q.device)
+    lamp_attn_decode(q, k, v, out, int(causal), int(window), delta, tau, tiles_per_split, mask)
     return out, mask
 
 

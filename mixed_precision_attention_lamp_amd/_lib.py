@@ -44,6 +44,11 @@ def load():
     lib.lamp_attn_fwd_logit8.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, f32, f32, vp]
     lib.lamp_attn_fwd_logit8.restype = i32
     lib.lamp_attn_fwd_bf16.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, vp]
+    lib.lamp_attn_decode.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, i32, f32, f32,
+                                     i32, vp]
+    lib.lamp_attn_decode.restype = i32
+    lib.lamp_decode_tiles_per_split.argtypes = [i32, i32, i32, i32, i32, i32]
+    lib.lamp_decode_tiles_per_split.restype = i32
     lib.lamp_attn_fwd_bf16.restype = i32
     lib.lamp_debug_attn_dump.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, f32, f32,
                                          vp, vp, vp]
@@ -144,6 +149,25 @@ def lamp_attn_fwd_logit8(q, k, v, out, causal=1, window=0, delta=2.0 ** -8, tau=
     _check(lib.lamp_attn_fwd_logit8(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, Hq, Hkv, S, D,
                                     int(causal), int(window), float(delta), float(tau),
                                     _ptr(subblock_mask_out)))
+
+
+def lamp_attn_decode(q, k, v, out, causal=1, window=0, delta=2.0 ** -8, tau=2.0 ** -1,
+                     tiles_per_split=0, subblock_mask_out=None):
+    """q [B,Hq,Sq,D] (the last Sq positions), k/v [B,Hkv,Skv,D] bf16; out
+    [B,Hq,Sq,D] fp32; optional uint8 mask [B,Hq,ceil(Skv/64)]."""
+    lib = load()
+    B, Hq, Sq, D = q.shape
+    Hkv, Skv = k.shape[1], k.shape[2]
+    _sync_stream(lib)
+    _check(lib.lamp_attn_decode(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, Hq, Hkv, Sq, Skv, D,
+                                int(causal), int(window), float(delta), float(tau),
+                                int(tiles_per_split), _ptr(subblock_mask_out)))
+
+
+def lamp_decode_tiles_per_split(B, Hq, Hkv, Sq, Skv, D):
+    rc = load().lamp_decode_tiles_per_split(B, Hq, Hkv, Sq, Skv, D)
+    _check(min(rc, 0))
+    return rc
 
 
 def lamp_attn_fwd_bf16(q, k, v, out, causal=1, window=0, subblock_mask_out=None):

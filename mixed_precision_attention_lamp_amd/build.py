@@ -18,11 +18,11 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "liblamp.so")
-SOURCES = ["quant.hip", "attn.hip", "stats.hip", "lamp_api.cpp"]
+SOURCES = ["quant.hip", "attn.hip", "decode.hip", "stats.hip", "lamp_api.cpp"]
 # Device sources: inputs are finite (documented in lamp.h), so max/min need no
 # NaN quieting.  Not for lamp_api.cpp, whose argument checks test for NaN.
 DEVICE_FLAGS = {"quant.hip": ["-fno-honor-nans"], "attn.hip": ["-fno-honor-nans"],
-                "stats.hip": ["-fno-honor-nans"]}
+                "decode.hip": ["-fno-honor-nans"], "stats.hip": ["-fno-honor-nans"]}
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

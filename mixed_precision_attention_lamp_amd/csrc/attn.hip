@@ -825,19 +825,6 @@ __global__ __launch_bounds__(kThreads, 1) void lamp_attn_kernel(AttnArgs a) {
         if (a.paired && level != a.n_rg - 1 - level) run_rows(level);
 }
 
-// Compute units of the current device (cached per device).
-int cu_count() {
-    static int cached[64] = {0};
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-    if (cached[dev] == 0) {
-        int n = 0;
-        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-        cached[dev] = n;
-    }
-    return cached[dev];
-}
-
 template <int D>
 hipError_t launch_d(const Shape& sh, const AttnParams& p, hipStream_t st) {
     AttnArgs a;

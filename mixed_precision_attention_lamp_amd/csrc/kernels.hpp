@@ -62,6 +62,45 @@ struct AttnParams {
 // The forward attention kernel (16-bit recompute inside the tile loop).
 hipError_t launch_attention(const Shape& sh, const AttnParams& p, hipStream_t st);
 
+// Split-KV decode: Sq <= 16 query rows (the last positions) against Skv keys.
+struct DecodeShape {
+    int B, Hq, Hkv, Sq, Skv, D;
+    int nT;        // ceil(Skv / 64) KV tiles
+    int tps;       // KV tiles per split
+    int n_split;   // ceil(nT / tps)
+};
+
+struct DecodeParams {
+    const uint16_t* q16;    // [B, Hq, Sq, D] bf16
+    const uint16_t* k16;    // [B, Hkv, Skv, D] bf16
+    const uint16_t* v16;    // [B, Hkv, Skv, D] bf16
+    const float* q_scale;   // [B * Hq]
+    const float* q_inv;
+    const float* k_scale;   // [B * Hkv]
+    const float* k_inv;
+    float* part_o;          // [B, Hq, n_split, Sq, D] workspace
+    float* part_ml;         // [B, Hq, n_split, Sq, 2] workspace
+    float* out;             // [B, Hq, Sq, D]
+    uint8_t* mask;          // [B, Hq, nT] or null
+    double log2e_over_sqrt_d;
+    float e_delta, t2;
+    int causal, window;
+};
+
+// Per-head scales and inverse scales of the decode inputs: Q heads over
+// their Sq rows, K heads over all Skv rows (partial must hold
+// B * Hkv * amax_chunks(Skv, D) uint32 values).
+hipError_t launch_decode_scales(const DecodeShape& sh, const uint16_t* q, const uint16_t* k,
+                                uint32_t* partial, float* q_scale, float* q_inv, float* k_scale,
+                                float* k_inv, hipStream_t st);
+
+// The decode kernel (one workgroup per batch, kv head and split) and the merge
+// of the splits into out.
+hipError_t launch_decode(const DecodeShape& sh, const DecodeParams& p, hipStream_t st);
+
+// Compute units of the current device (256 when it cannot be queried).
+int cu_count();
+
 // Sub-block statistics of a mask (see lamp_subblock_stats).
 hipError_t launch_subblock_stats(const uint8_t* mask, int B, int Hq, int S, int causal,
                                  int window, int64_t* stats, hipStream_t st);

@@ -150,7 +150,58 @@ Layout workspace_layout(const lamp::Shape& sh) {
     return L;
 }
 
+// KV tiles per split of a decode call: enough splits that one round of
+// workgroups fills the device (two four-wave or one eight-wave workgroup per
+// compute unit: eight waves of two per SIMD), each split at least one tile.
+int decode_tiles_per_split(int B, int Hq, int Hkv, int Skv, int D) {
+    const int nT = (Skv + 63) / 64;
+    const int units = B * Hkv;
+    const bool wide = Hq / Hkv > 4 || D == 256;
+    const int want = (wide ? 1 : 2) * lamp::cu_count();
+    int n_split = (want + units - 1) / units;
+    if (n_split > nT) n_split = nT;
+    if (n_split < 1) n_split = 1;
+    return (nT + n_split - 1) / n_split;
+}
+
+int check_decode(int B, int Hq, int Hkv, int Sq, int Skv, int D) {
+    if (B < 1 || Hq < 1 || Hkv < 1 || Sq < 1 || Skv < 1)
+        return fail(LAMP_ERR_INVALID, "sizes must be >= 1 (B=%d Hq=%d Hkv=%d Sq=%d Skv=%d)", B, Hq, Hkv, Sq, Skv);
+    if (Hq % Hkv != 0) return fail(LAMP_ERR_INVALID, "Hq (%d) must be a multiple of Hkv (%d)", Hq, Hkv);
+    if (Sq > Skv) return fail(LAMP_ERR_INVALID, "Sq (%d) must not exceed Skv (%d)", Sq, Skv);
+    if (D != 64 && D != 128 && D != 256)
+        return fail(LAMP_ERR_UNSUPPORTED, "head dimension D=%d (supported: 64, 128, 256)", D);
+    if (Sq > 16) return fail(LAMP_ERR_UNSUPPORTED, "decode needs Sq <= 16 (got %d)", Sq);
+    if (Hq / Hkv > 8) return fail(LAMP_ERR_UNSUPPORTED, "decode needs Hq/Hkv <= 8 (got %d)", Hq / Hkv);
+    const int64_t nT = (Skv + 63) / 64;
+    if ((int64_t)B * Hkv * nT * 64 * D >= ((int64_t)1 << 31) || (int64_t)B * Hq * Sq * D * nT >= ((int64_t)1 << 31))
+        return fail(LAMP_ERR_UNSUPPORTED, "decode sizes exceed 2^31 elements");
+    return LAMP_OK;
+}
+
 }  // namespace
+
+namespace lamp {
+
+int cu_count() {
+    static int cached[kMaxDevices] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+        (void)hipGetLastError();
+        return 256;
+    }
+    if (cached[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) {
+            (void)hipGetLastError();
+            n = 256;
+        }
+        cached[dev] = n;
+    }
+    return cached[dev];
+}
+
+}  // namespace lamp
 
 // plain = 1: plain bf16 FlashAttention (delta and tau unused).
 static int attn_fwd_impl(const void* q, const void* k, const void* v, float* out, int B, int Hq, int Hkv,
@@ -266,6 +317,87 @@ int lamp_debug_attn_dump_logit8(const void* q, const void* k, const void* v, flo
                                 uint8_t* subblock_mask_out, float* logit8_out, uint16_t* p_out) {
     return attn_dump_impl(q, k, v, out, B, Hq, Hkv, S, D, causal, window, delta, tau, subblock_mask_out,
                           logit8_out, p_out, 1);
+}
+
+int lamp_decode_tiles_per_split(int B, int Hq, int Hkv, int Sq, int Skv, int D) {
+    const int rc = check_decode(B, Hq, Hkv, Sq, Skv, D);
+    if (rc != LAMP_OK) return rc;
+    return decode_tiles_per_split(B, Hq, Hkv, Skv, D);
+}
+
+int lamp_attn_decode(const void* q, const void* k, const void* v, float* out, int B, int Hq, int Hkv,
+                     int Sq, int Skv, int D, int causal, int window, float delta, float tau,
+                     int tiles_per_split, uint8_t* subblock_mask_out) {
+    if (!q || !k || !v || !out) return fail(LAMP_ERR_INVALID, "q, k, v and out must be non-null");
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
+        return fail(LAMP_ERR_INVALID, "q, k, v and out must be 16-byte aligned");
+    int rc = check_decode(B, Hq, Hkv, Sq, Skv, D);
+    if (rc != LAMP_OK) return rc;
+    if (causal != 0 && causal != 1) return fail(LAMP_ERR_INVALID, "causal must be 0 or 1 (got %d)", causal);
+    if (window < 0) return fail(LAMP_ERR_INVALID, "window must be >= 0 (got %d)", window);
+    if (window > 0 && !causal) return fail(LAMP_ERR_INVALID, "a sliding window requires causal = 1");
+    if (std::isnan(delta) || std::isnan(tau)) return fail(LAMP_ERR_INVALID, "delta and tau must not be NaN");
+    if (tiles_per_split < 0)
+        return fail(LAMP_ERR_INVALID, "tiles_per_split must be >= 0 (got %d)", tiles_per_split);
+
+    lamp::DecodeShape sh;
+    sh.B = B; sh.Hq = Hq; sh.Hkv = Hkv; sh.Sq = Sq; sh.Skv = Skv; sh.D = D;
+    sh.nT = (Skv + 63) / 64;
+    sh.tps = tiles_per_split > 0 ? (tiles_per_split < sh.nT ? tiles_per_split : sh.nT)
+                                 : decode_tiles_per_split(B, Hq, Hkv, Skv, D);
+    sh.n_split = (sh.nT + sh.tps - 1) / sh.tps;
+
+    size_t off = 0;
+    auto take = [&](size_t bytes) { size_t o = off; off = round_up(off + bytes, 256); return o; };
+    const size_t o_partial = take((size_t)B * Hkv * lamp::amax_chunks(Skv, D) * sizeof(uint32_t));
+    const size_t o_qs = take((size_t)B * Hq * sizeof(float));
+    const size_t o_qi = take((size_t)B * Hq * sizeof(float));
+    const size_t o_ks = take((size_t)B * Hkv * sizeof(float));
+    const size_t o_ki = take((size_t)B * Hkv * sizeof(float));
+    const size_t o_po = take((size_t)B * Hq * sh.n_split * Sq * D * sizeof(float));
+    const size_t o_ml = take((size_t)B * Hq * sh.n_split * Sq * 2 * sizeof(float));
+    void* ws = nullptr;
+    rc = get_workspace(off, &ws);
+    if (rc != LAMP_OK) return rc;
+    uint8_t* base = static_cast<uint8_t*>(ws);
+
+    lamp::DecodeParams p;
+    p.q16 = static_cast<const uint16_t*>(q);
+    p.k16 = static_cast<const uint16_t*>(k);
+    p.v16 = static_cast<const uint16_t*>(v);
+    p.q_scale = reinterpret_cast<float*>(base + o_qs);
+    p.q_inv = reinterpret_cast<float*>(base + o_qi);
+    p.k_scale = reinterpret_cast<float*>(base + o_ks);
+    p.k_inv = reinterpret_cast<float*>(base + o_ki);
+    p.part_o = reinterpret_cast<float*>(base + o_po);
+    p.part_ml = reinterpret_cast<float*>(base + o_ml);
+    p.out = out;
+    p.mask = subblock_mask_out;
+    p.log2e_over_sqrt_d = kLog2e / std::sqrt((double)D);
+    p.e_delta = exponential_threshold(delta);
+    p.t2 = (float)(16.0 * (double)tau * kLog2e);
+    p.causal = causal;
+    p.window = window;
+
+    hipEvent_t* ev = nullptr;
+    if (g_timing && g_n_timed < kMaxTimed) {
+        ev = g_events[g_n_timed];
+        for (int i = 0; i < 3 && ev; ++i)
+            if (!ev[i] && hipEventCreate(&ev[i]) != hipSuccess) ev = nullptr;
+        if (ev) ++g_n_timed;
+    }
+    if (ev) (void)hipEventRecord(ev[0], g_stream);
+    hipError_t e = lamp::launch_decode_scales(sh, p.q16, p.k16, reinterpret_cast<uint32_t*>(base + o_partial),
+                                              reinterpret_cast<float*>(base + o_qs),
+                                              reinterpret_cast<float*>(base + o_qi),
+                                              reinterpret_cast<float*>(base + o_ks),
+                                              reinterpret_cast<float*>(base + o_ki), g_stream);
+    if (e != hipSuccess) return hip_fail(e, "decode scale launch");
+    if (ev) (void)hipEventRecord(ev[1], g_stream);
+    e = lamp::launch_decode(sh, p, g_stream);
+    if (e != hipSuccess) return hip_fail(e, "decode launch");
+    if (ev) (void)hipEventRecord(ev[2], g_stream);
+    return LAMP_OK;
 }
 
 int lamp_set_timing(int enable) {

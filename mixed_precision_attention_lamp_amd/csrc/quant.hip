@@ -189,6 +189,40 @@ __global__ __launch_bounds__(kThreads) void amax_transpose_kernel(
     transpose_v_block<D>(v, vt, S, nT, tb % nT, tb / nT, tile);
 }
 
+// Decode scales: blocks [0, nq) are query heads (amax over their q_len
+// values, read directly), the rest kv heads (max of their nch partial maxima).
+// scale = fl32(amax / 448), inv = fl32(448 / amax); 1 and 1 for amax = 0.
+__global__ __launch_bounds__(kThreads) void decode_scales_kernel(
+    const uint16_t* __restrict__ q, const uint32_t* __restrict__ partial, float* __restrict__ q_scale,
+    float* __restrict__ q_inv, float* __restrict__ k_scale, float* __restrict__ k_inv, int nq, int q_len,
+    int nch) {
+    __shared__ uint32_t red[kThreads / 64];
+    const int h = blockIdx.x;
+    uint32_t m = 0;
+    if (h < nq) {
+        const uint16_t* src = q + (size_t)h * q_len;
+        for (int i = threadIdx.x * 8; i < q_len; i += kThreads * 8)
+            m = max(m, max_bf16_mag(*reinterpret_cast<const u32x4*>(src + i)));
+    } else {
+        for (int i = threadIdx.x; i < nch; i += kThreads) m = max(m, partial[(size_t)(h - nq) * nch + i]);
+    }
+    m = block_max_u32(m, red);
+    if (threadIdx.x != 0) return;
+    const float amax = bf16_bits_to_float(m);
+    float scale = 1.0f, inv = 1.0f;
+    if (amax > 0.0f) {
+        scale = (float)((double)amax / 448.0);
+        inv = (float)(448.0 / (double)amax);
+    }
+    if (h < nq) {
+        q_scale[h] = scale;
+        q_inv[h] = inv;
+    } else {
+        k_scale[h - nq] = scale;
+        k_inv[h - nq] = inv;
+    }
+}
+
 __global__ void debug_convert_kernel(const float* __restrict__ x, int64_t n, uint8_t* e4m3,
                                      uint16_t* e4m3_bf16, uint16_t* bf16, float* exp2) {
     for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n;
@@ -248,6 +282,20 @@ hipError_t launch_amax_transpose(const Shape& sh, const uint16_t* q, const uint1
     else
         hipLaunchKernelGGL(amax_transpose_kernel<256>, dim3(n_blocks), dim3(kThreads), 0, st, q, k, partial,
                            nq, slab_len, nch, n_amax, v, vt, sh.S, sh.nT);
+    return hipGetLastError();
+}
+
+hipError_t launch_decode_scales(const DecodeShape& sh, const uint16_t* q, const uint16_t* k,
+                                uint32_t* partial, float* q_scale, float* q_inv, float* k_scale,
+                                float* k_inv, hipStream_t st) {
+    const int nq = sh.B * sh.Hq, nk = sh.B * sh.Hkv;
+    const int nch = amax_chunks(sh.Skv, sh.D);
+    // K partial maxima (every slab is a K slab)
+    hipLaunchKernelGGL(amax_kernel, dim3(nch, nk), dim3(kThreads), 0, st, q, k, partial, 0, sh.Skv * sh.D, nch);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(decode_scales_kernel, dim3(nq + nk), dim3(kThreads), 0, st, q, partial, q_scale, q_inv,
+                       k_scale, k_inv, nq, sh.Sq * sh.D, nch);
     return hipGetLastError();
 }
 

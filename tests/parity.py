@@ -447,3 +447,114 @@ def assert_parity_logit8(rep, max_skipped=0.1):
     assert not rep["rows_unexplained"], f"rows above {MAX_ABS}: {rep['rows_unexplained'][:10]}"
     assert rep["mean_abs"] <= MEAN_ABS, rep["mean_abs"]
     assert rep["rows_max_fragile"] <= max_skipped * rep["rows"], rep["rows_max_fragile"]
+
+
+# --------------------------------------------------------------------------
+# split-KV decode (lamp_attn_decode against oracle.lamp.decode_forward)
+# --------------------------------------------------------------------------
+def decode_unit(ctx, b, h, tps, override=None):
+    """The oracle for one decode head: (merged rows, {t: mask byte}, per-split traces)."""
+    nT = L.n_tiles(ctx["S"])
+    traces, parts, mask = [], [], {}
+    for tr in L.split_tiles(nT, tps):
+        trace = []
+        with np.errstate(invalid="ignore", divide="ignore"):
+            _, mk = L.run_unit(ctx, b, h, 0, flag_override=override, trace=trace, tiles=tr)
+        traces.append(trace)
+        fin = trace[-1]
+        parts.append((fin["m"], fin["ell"], fin["O"]))
+        mask.update(mk)
+    return L.merge_splits(parts), mask, traces
+
+
+def decode_flip_bound(ctx, b, h, traces, out):
+    """Bound on |dO| of the merged rows from weights that can round the other
+    way: a weight p of tile t in split s moves the merged output by
+    dp 2^(m_t - M) |v - out| / sum_s 2^(m_s - M) l_s."""
+    G = ctx["G"]
+    vv = ctx["v"][b, h // G]
+    ms = np.stack([tr[-1]["m"] for tr in traces])
+    M = ms.max(axis=0)
+    with np.errstate(invalid="ignore", over="ignore"):
+        Lt = sum(np.where(np.isneginf(tr[-1]["m"]), 0.0, np.exp2(tr[-1]["m"] - M)) * tr[-1]["ell"]
+                 for tr in traces)
+        bound = np.zeros_like(out)
+        for trace in traces:
+            for rec in trace[:-1]:
+                alt = fragile_alternatives(ctx, b, h, 0, rec)
+                scale = np.where(np.isneginf(rec["m_new"]), 0.0, np.exp2(rec["m_new"] - M)) / Lt
+                vj = vv[rec["cols"]]
+                bound += np.einsum("ij,ijd->id", alt * scale[:, None],
+                                   np.abs(vj[None, :, :] - out[:, None, :]))
+    return 1.1 * bound
+
+
+def run_gpu_decode(q, k, v, causal, window, delta, tau, tps):
+    import mixed_precision_attention_lamp_amd as lamp
+    out, mask = lamp.attention_decode(to_device(q), to_device(k), to_device(v), causal, window, delta,
+                                      tau, tiles_per_split=tps)
+    torch.cuda.synchronize()
+    return out.cpu().numpy(), mask.cpu().numpy()
+
+
+def compare_decode(q, k, v, causal, window, delta, tau, tps, heads=None, label="", gpu=None):
+    """GPU split-KV decode against the oracle under the protocol of ``compare``
+    (mask exact up to excused flags, outputs after a replay with the device's
+    flags within MAX_ABS plus the flip bound, mean within MEAN_ABS)."""
+    B, Hq, Sq, D = q.shape
+    Skv = k.shape[2]
+    nT = L.n_tiles(Skv)
+    if heads is None:
+        heads = [(b, h) for b in range(B) for h in range(Hq)]
+    say(f"[parity-decode] {label} B={B} Hq={Hq} Hkv={k.shape[1]} Sq={Sq} Skv={Skv} D={D} "
+        f"causal={causal} window={window} delta={delta} tau={tau} tiles/split={tps} heads={len(heads)}")
+    out_g, mask_g = gpu if gpu is not None else run_gpu_decode(q, k, v, causal, window, delta, tau, tps)
+    ctx = L.prepare(q, k, v, causal, window, delta, tau)
+    unexcused, n_excused, n_sub, diffs = [], 0, 0, []
+    explained, unexplained = 0, []
+    for (b, h) in heads:
+        out_o, mk, traces = decode_unit(ctx, b, h, tps)
+        want = np.zeros(nT, dtype=np.uint8)
+        for t, byte in mk.items():
+            want[t] = byte
+        n_sub += int(((want & 0x80) != 0).sum()) * 4
+        recs = {rec["t"]: rec for tr in traces for rec in tr[:-1]}
+        diff_t = np.nonzero(mask_g[b, h] != want)[0]
+        for t in diff_t:
+            x = int(mask_g[b, h, t]) ^ int(want[t])
+            rec = recs.get(int(t))
+            wide = fragile_mask_bits(ctx, b, h, 0, rec) if rec is not None else 0
+            if (x & 0x80) == 0 and (x & ~wide & 0x0F) == 0:
+                n_excused += 1
+            else:
+                unexcused.append((b, h, int(t), int(mask_g[b, h, t]), int(want[t])))
+        if diff_t.size:
+            ov = {t: int(mask_g[b, h, t]) & 0x0F for t in range(nT)}
+            out_o, _, traces = decode_unit(ctx, b, h, tps, override=ov)
+        d = np.abs(out_g[b, h].astype(np.float64) - out_o.astype(np.float64))
+        diffs.append(d)
+        if not np.isfinite(out_g[b, h]).all():
+            unexplained.append((b, h, "non-finite"))
+        if (d > MAX_ABS).any():
+            bnd = decode_flip_bound(ctx, b, h, traces, out_o)
+            for i in np.nonzero((d > MAX_ABS).any(axis=1))[0]:
+                if np.all(d[i] <= MAX_ABS + bnd[i]):
+                    explained += 1
+                else:
+                    j = int(np.argmax(d[i] - bnd[i]))
+                    unexplained.append((b, h, int(i), j, float(d[i, j]), float(bnd[i, j])))
+    d = np.concatenate([x.reshape(-1) for x in diffs])
+    rep = dict(max_abs=float(d.max()), mean_abs=float(d.mean()), unexcused=unexcused,
+               excused=n_excused, n_subblocks=n_sub, rows_explained=explained,
+               rows_unexplained=unexplained, finite=bool(np.isfinite(d).all()))
+    say(f"[parity-decode] {label} max|dO|={rep['max_abs']:.3e} mean|dO|={rep['mean_abs']:.3e} "
+        f"mask mismatches {n_excused + len(unexcused)} of {n_sub} sub-blocks (excused {n_excused}); "
+        f"rows above {MAX_ABS:g}: {explained + len(unexplained)} (explained {explained})")
+    return rep
+
+
+def assert_parity_decode(rep):
+    assert rep["finite"], "non-finite outputs"
+    assert not rep["unexcused"], f"unexcused mask mismatches: {rep['unexcused'][:10]}"
+    assert not rep["rows_unexplained"], f"rows above {MAX_ABS}: {rep['rows_unexplained'][:10]}"
+    assert rep["mean_abs"] <= MEAN_ABS, rep["mean_abs"]

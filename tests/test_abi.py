@@ -113,3 +113,30 @@ def test_logit8_variant_rejects_before_hip(lib):
     assert d(ALIGNED, ALIGNED, ALIGNED, ALIGNED, 1, 1, 1, 64, 64, 1, 0, 0.0, 0.5, None, None, ALIGNED) == -1
     assert d(ALIGNED, ALIGNED, ALIGNED, ALIGNED, 1, 1, 1, 4096, 64, 1, 0, 0.0, 0.5, None, ALIGNED,
              ALIGNED) == -2
+
+
+def test_decode_rejects_before_hip(lib):
+    f = lib.lamp_attn_decode
+    A = ALIGNED
+    # Sq > 16, Sq > Skv, G > 8, D = 96: unsupported or invalid, nothing launched
+    assert f(A, A, A, A, 1, 2, 1, 17, 64, 128, 1, 0, 0.0039, 0.5, 0, None) == -2
+    assert "Sq <= 16" in lamp.lamp_last_error()
+    assert f(A, A, A, A, 1, 2, 1, 8, 4, 128, 1, 0, 0.0039, 0.5, 0, None) == -1
+    assert f(A, A, A, A, 1, 16, 1, 8, 64, 128, 1, 0, 0.0039, 0.5, 0, None) == -2
+    assert f(A, A, A, A, 1, 2, 1, 8, 64, 96, 1, 0, 0.0039, 0.5, 0, None) == -2
+    assert f(A, A, A, A, 1, 2, 1, 8, 64, 128, 0, 8, 0.0039, 0.5, 0, None) == -1
+    assert f(A, A, A, A, 1, 2, 1, 8, 64, 128, 1, 0, math.nan, 0.5, 0, None) == -1
+    assert f(A, A, A, A, 1, 2, 1, 8, 64, 128, 1, 0, 0.0039, 0.5, -1, None) == -1
+    assert f(None, A, A, A, 1, 2, 1, 8, 64, 128, 1, 0, 0.0039, 0.5, 0, None) == -1
+    assert lib.lamp_decode_tiles_per_split(1, 2, 1, 17, 64, 128) == -2
+
+
+@pytest.mark.skipif(torch.cuda.is_available(), reason="checks the default compute-unit count")
+def test_decode_split_choice_without_device(lib):
+    # 256 compute units assumed: 512 four-wave workgroups; 64 (batch, kv head)
+    # units of 256 tiles give 8 splits of 32 tiles; G = 8 takes eight-wave
+    # workgroups, 256 of them; few tiles give 1 per split
+    assert lib.lamp_decode_tiles_per_split(8, 32, 8, 16, 16384, 128) == 32
+    assert lib.lamp_decode_tiles_per_split(8, 64, 8, 16, 16384, 128) == 64
+    assert lib.lamp_decode_tiles_per_split(1, 4, 1, 1, 300, 64) == 1
+    assert lib.lamp_decode_tiles_per_split(64, 64, 16, 16, 4096, 128) == 64

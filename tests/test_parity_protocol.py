@@ -39,3 +39,15 @@ def test_default_protocol_accepts_the_oracle_and_rejects_logit8():
     dev8 = L.lamp_forward(q, k, v, causal, window, delta, tau, logit8=True)
     rep = compare(q, k, v, causal, window, delta, tau, gpu=dev8, label="planted")
     assert bool(rep["unexcused"]) or bool(rep["rows_unexplained"]) or rep["mean_abs"] > 5e-4, rep
+
+
+def test_decode_protocol_accepts_the_oracle_and_rejects_other_splits():
+    from parity import assert_parity_decode, compare_decode
+    from inputs import make_inputs as mk
+    q, k, v = mk(1, 4, 2, 700, 64, 43, "channels", Sq=9)
+    dev = L.decode_forward(q, k, v, 1, 0, 2.0 ** -8, 2.0 ** -2, tiles_per_split=3)
+    assert_parity_decode(compare_decode(q, k, v, 1, 0, 2.0 ** -8, 2.0 ** -2, 3, gpu=dev, label="self"))
+    # a device that split differently (one split) computes a different result
+    dev1 = L.decode_forward(q, k, v, 1, 0, 2.0 ** -8, 2.0 ** -2, tiles_per_split=11)
+    rep = compare_decode(q, k, v, 1, 0, 2.0 ** -8, 2.0 ** -2, 3, gpu=dev1, label="planted")
+    assert bool(rep["unexcused"]) or bool(rep["rows_unexplained"]) or rep["mean_abs"] > 5e-4, rep
