@@ -79,6 +79,15 @@ struct DCfg {
     static constexpr int kRuns = kCh / kRun;                     // runs per thread and tile
 };
 
+// Byte offset of 16-byte chunk `chunk` of row d of the staged V^T tile (64
+// positions, 128 bytes per row).  The chunks are XOR-swizzled by
+// (d ^ d / 8) mod 8: the P.V operand reads (rows d .. d+15 at one chunk) and
+// the transposing stores (rows 8c + x for 16 columns c at one position) both
+// spread over all eight chunk slots.
+__device__ __forceinline__ int vt_off(int d, int chunk) {
+    return d * (2 * kTileKeys) + ((chunk ^ ((d ^ (d >> 3)) & 7)) << 4);
+}
+
 // Query row i (sequence position Skv - Sq + i) sees key j.
 __device__ __forceinline__ bool dec_visible(int i, int j, int Sq, int Skv, int causal, int window) {
     const int p = Skv - Sq + i;
@@ -247,7 +256,7 @@ __global__ __launch_bounds__(kW * 64, 2) void lamp_decode_kernel(DecodeArgs a) {
                     const uint32_t w = rv[r * C::kRun + e][x >> 1];
                     v16[e] = (x & 1) ? (w >> 16) : (w & 0xFFFFu);
                 }
-                uint8_t* dst = vtl + lds_off<C::kVtRow>(d, pos >> 3) + (pos & 7) * 2;
+                uint8_t* dst = vtl + vt_off(d, pos >> 3) + (pos & 7) * 2;
                 if constexpr (C::kRun == 4)
                     *reinterpret_cast<u32x2*>(dst) = u32x2{v16[0] | (v16[1] << 16), v16[2] | (v16[3] << 16)};
                 else if constexpr (C::kRun == 2)
@@ -422,7 +431,7 @@ __global__ __launch_bounds__(kW * 64, 2) void lamp_decode_kernel(DecodeArgs a) {
                 }
 #pragma unroll
                 for (int db = 0; db < C::kDB; ++db) {
-                    const v8bf va = *reinterpret_cast<const v8bf*>(vtl + lds_off<C::kVtRow>(db * 16 + n16, h * 4 + g));
+                    const v8bf va = *reinterpret_cast<const v8bf*>(vtl + vt_off(db * 16 + n16, h * 4 + g));
 #pragma unroll
                     for (int j = 0; j < kQG; ++j)
                         acc_o[j][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb[j], acc_o[j][db], 0, 0, 0);
