@@ -42,8 +42,8 @@ TRAFFIC = {"kernel_hash": "d173aea78b167779", "workload": "qwen3-8b", "delta": 2
 
 # The same for the decode kernel on the qwen3-8b-decode workload
 # (profiles/decode_qwen3_8b_hbm_traffic.md), library split.
-TRAFFIC_DECODE = {"kernel_hash": "a14361c8b945b249", "workload": "qwen3-8b-decode", "delta": 2.0 ** -8,
-                  "tau": 2.0 ** -1, "bytes_per_launch": 555436322.5}
+TRAFFIC_DECODE = {"kernel_hash": "6838e8b817d23988", "workload": "qwen3-8b-decode", "delta": 2.0 ** -8,
+                  "tau": 2.0 ** -1, "bytes_per_launch": 556377644.4}
 
 
 def decode_source_hash():
