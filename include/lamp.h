@@ -69,8 +69,8 @@ int lamp_attn_fwd(const void* q, const void* k, const void* v, float* out,
                   int causal, int window, float delta, float tau,
                   uint8_t* subblock_mask_out);
 
-/* The forward pass under the literal reading of "key-query products accumulated
- * in 8-bit formats" ("LampAttention", abstract): the log2-domain logit
+/* The forward pass under a literal reading of the 8-bit accumulation of
+ * key-query products ("LampAttention", abstract): the log2-domain logit
  * c * acc (c = log2(e)/sqrt(D) times the Q and K scales) is itself rounded to
  * e4m3 (magnitudes clamped to 448, nearest even) before the running row max,
  * the 8-bit exponentials 2^(s8 - m) and the second stage |s8| >= 16 tau log2(e)

@@ -1,9 +1,9 @@
 """Software rounding to the formats the method uses (oracle; test infrastructure).
 
 The method of "LampAttention: Look-Ahead Mixed-Precision FlashAttention for
-Dedicated Accelerators" (abstract) evaluates key-query products and
-exponentials "in 8-bit formats" and recomputes sensitive sub-blocks "in 16-bit
-formats".  The pages do not name the formats; the readings used here are
+Dedicated Accelerators" (abstract) computes key-query products and
+exponentials with 8-bit number formats and redoes sensitive sub-blocks with
+16-bit ones.  The pages do not name the formats; the readings used here are
 
 * 8-bit  = OCP FP8 E4M3 ("e4m3fn"): 1 sign, 4 exponent bits (bias 7),
   3 fraction bits, no infinities, largest finite 448, subnormal spacing 2^-9.

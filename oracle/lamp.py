@@ -2,9 +2,9 @@
 
 Source: "LampAttention: Look-Ahead Mixed-Precision FlashAttention for
 Dedicated Accelerators".  The abstract fixes the pipeline: a FlashAttention
-whose key-query products are accumulated and whose exponentials are evaluated
-in 8-bit formats, after which sensitive sub-blocks are identified adaptively
-and recomputed in 16-bit formats.  The title calls the identification
+that sums key-query products and takes exponentials with 8-bit number
+formats, then finds the sensitive sub-blocks adaptively and redoes them with
+16-bit ones.  The title calls the identification
 "look-ahead".  Tables 1-6 count "16-bit sub-blocks per tile" (0 / 1 / 2+), so
 the decision unit is a sub-block of a tile.  Every table and figure caption
 runs the method with two parameters, delta = 2^-8 and tau = 2^-1; figures 6
@@ -33,7 +33,7 @@ The pages give no formula, format or tile size.  The readings taken here
   (the e4m3 unit roundoff) is 2^-4 * |s|, compared with tau;
 * a sub-block is flagged (recomputed in 16-bit) iff it holds a sensitive entry.
 
-A second reading of "accumulated in 8-bit formats" is kept as a variant
+A second, literal reading of the abstract's 8-bit accumulation is kept as a variant
 (``logit8``): the log2-domain logit s = fl32(acc * c) is itself rounded to
 e4m3 (saturating at 448) before anything uses it.  The running max, the
 exponential's argument s8 - m (exact: both are e4m3 values) and the second

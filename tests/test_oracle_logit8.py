@@ -1,8 +1,9 @@
 """Pins of the oracle's literal 8-bit-logit variant (``logit8``).  No GPU.
 
-The variant reads "key-query products accumulated in 8-bit formats" (the
+The variant takes the 8-bit accumulation of key-query products that the
 abstract of "LampAttention: Look-Ahead Mixed-Precision FlashAttention for
-Dedicated Accelerators") literally: the log2-domain logit is an e4m3 value.
+Dedicated Accelerators" describes literally: the log2-domain logit is an
+e4m3 value.
 Pinned here by
 
 * a two-key input whose logits and weights are worked out by hand, where
