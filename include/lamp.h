@@ -94,7 +94,8 @@ int lamp_attn_fwd_logit8(const void* q, const void* k, const void* v, float* out
  *   out       fp32 device tensor [B, Hq, Sq, D].
  *   causal, window, delta, tau as in lamp_attn_fwd, with query row i at
  *             position Skv - Sq + i.
- *   tiles_per_split  >= 1: KV tiles per split (clamped to the tile count);
+ *   tiles_per_split  >= 1: KV tiles per split (clamped to the tile count; more
+ *             than 8192 after clamping is LAMP_ERR_UNSUPPORTED);
  *             0: the library's choice, lamp_decode_tiles_per_split.
  *   subblock_mask_out  nullable; uint8 device tensor [B, Hq, nT], nT = ceil(Skv/64):
  *             byte (b, hq, t) as in lamp_attn_fwd for the one row block.

@@ -153,6 +153,10 @@ Layout workspace_layout(const lamp::Shape& sh) {
 // KV tiles per split of a decode call: enough splits that one round of
 // workgroups fills the device (two four-wave or one eight-wave workgroup per
 // compute unit: eight waves of two per SIMD), each split at least one tile.
+// The decode kernel keeps a split's mask bytes in LDS: at most this many
+// tiles per split.
+constexpr int kMaxTilesPerSplit = 8192;
+
 int decode_tiles_per_split(int B, int Hq, int Hkv, int Skv, int D) {
     const int nT = (Skv + 63) / 64;
     const int units = B * Hkv;
@@ -160,6 +164,8 @@ int decode_tiles_per_split(int B, int Hq, int Hkv, int Skv, int D) {
     const int want = (wide ? 1 : 2) * lamp::cu_count();
     int n_split = (want + units - 1) / units;
     if (n_split > nT) n_split = nT;
+    if (n_split < (nT + kMaxTilesPerSplit - 1) / kMaxTilesPerSplit)
+        n_split = (nT + kMaxTilesPerSplit - 1) / kMaxTilesPerSplit;
     if (n_split < 1) n_split = 1;
     return (nT + n_split - 1) / n_split;
 }
@@ -345,6 +351,8 @@ int lamp_attn_decode(const void* q, const void* k, const void* v, float* out, in
     sh.nT = (Skv + 63) / 64;
     sh.tps = tiles_per_split > 0 ? (tiles_per_split < sh.nT ? tiles_per_split : sh.nT)
                                  : decode_tiles_per_split(B, Hq, Hkv, Skv, D);
+    if (sh.tps > kMaxTilesPerSplit)
+        return fail(LAMP_ERR_UNSUPPORTED, "tiles_per_split %d exceeds %d", sh.tps, kMaxTilesPerSplit);
     sh.n_split = (sh.nT + sh.tps - 1) / sh.tps;
 
     size_t off = 0;

@@ -128,6 +128,9 @@ def test_decode_rejects_before_hip(lib):
     assert f(A, A, A, A, 1, 2, 1, 8, 64, 128, 1, 0, math.nan, 0.5, 0, None) == -1
     assert f(A, A, A, A, 1, 2, 1, 8, 64, 128, 1, 0, 0.0039, 0.5, -1, None) == -1
     assert f(None, A, A, A, 1, 2, 1, 8, 64, 128, 1, 0, 0.0039, 0.5, 0, None) == -1
+    # a split of more than 8192 tiles (Skv = 1M keys in one split)
+    assert f(A, A, A, A, 1, 2, 1, 8, 1 << 20, 64, 1, 0, 0.0039, 0.5, 9000, None) == -2
+    assert "tiles_per_split" in lamp.lamp_last_error()
     assert lib.lamp_decode_tiles_per_split(1, 2, 1, 17, 64, 128) == -2
 
 
@@ -140,3 +143,5 @@ def test_decode_split_choice_without_device(lib):
     assert lib.lamp_decode_tiles_per_split(8, 64, 8, 16, 16384, 128) == 64
     assert lib.lamp_decode_tiles_per_split(1, 4, 1, 1, 300, 64) == 1
     assert lib.lamp_decode_tiles_per_split(64, 64, 16, 16, 4096, 128) == 64
+    # one unit and 1M keys: 512 splits of 32 tiles
+    assert lib.lamp_decode_tiles_per_split(1, 8, 1, 16, 1 << 20, 128) == 32
