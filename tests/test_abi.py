@@ -143,5 +143,5 @@ def test_decode_split_choice_without_device(lib):
     assert lib.lamp_decode_tiles_per_split(8, 64, 8, 16, 16384, 128) == 64
     assert lib.lamp_decode_tiles_per_split(1, 4, 1, 1, 300, 64) == 1
     assert lib.lamp_decode_tiles_per_split(64, 64, 16, 16, 4096, 128) == 64
-    # one unit and 1M keys: 512 splits of 32 tiles
-    assert lib.lamp_decode_tiles_per_split(1, 8, 1, 16, 1 << 20, 128) == 32
+    # one unit (G = 8: eight-wave workgroups) and 1M keys: 256 splits of 64 tiles
+    assert lib.lamp_decode_tiles_per_split(1, 8, 1, 16, 1 << 20, 128) == 64
