@@ -119,11 +119,13 @@ struct Cfg {
 // Q.K^T of every sub-block on the bf16 matrix cores, exponentials rounded to
 // bf16; ping-pong schedule only); 4 + (0, 1, 2): the test modes 0-2 with
 // 8-bit logits (the log2-domain logit c8 acc itself rounded to e4m3 before the
-// running max, the exponentials and the test read it).
+// running max, the exponentials and the test read it); 9: mode 1 with the
+// per-entry test in vector form (for small tau, where most waves need it).
 template <int D, bool kDump, int kMode>
 __global__ __launch_bounds__(kThreads, 1) void lamp_attn_kernel(AttnArgs a) {
     constexpr bool kPlain = kMode == 3;
-    constexpr bool kLogit8 = kMode >= 4;
+    constexpr bool kLogit8 = (kMode & 4) != 0;
+    constexpr bool kDense = (kMode & 8) != 0;
     constexpr int kTest = kMode & 3;
     using C = Cfg<D, kPlain>;
     static_assert(!kPlain || C::kPP, "the plain bf16 mode runs on the ping-pong schedule");
@@ -560,22 +562,43 @@ __global__ __launch_bounds__(kThreads, 1) void lamp_attn_kernel(AttnArgs a) {
                 for (int kb = 0; kb < 4; ++kb) hit[kb] |= wave_ballot(smax[qg][kb] >= thr);
             }
             if (wave_ballot(slow) != 0) {
+                if constexpr (kDense) {
+                    // an entry is sensitive iff max(x_delta - x, a2 - |acc|) <= 0
+                    // (each difference is exact in sign); the lane's minimum
+                    // over a sub-block decides with one ballot
 #pragma unroll
-                for (int kb = 0; kb < 4; ++kb) hit[kb] = 0;
+                    for (int qg = 0; qg < kQG; ++qg)
 #pragma unroll
-                for (int qg = 0; qg < kQG; ++qg)
+                        for (int kb = 0; kb < 4; ++kb) {
+                            float dmin = __builtin_inff();
 #pragma unroll
-                    for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) {
-                            // each ballot of a compare is that compare's lane
-                            // mask; the masks combine in scalar registers
-                            const float v = s[qg][kb][i];
-                            uint64_t h = wave_ballot(__builtin_fmaf(v, c8, -m_use[qg]) >= a.x_delta) &
-                                         wave_ballot(__builtin_fabsf(v) >= a2);
-                            if constexpr (kMasked) h &= wave_ballot((vis[qg] >> (kb * 4 + i)) & 1u);
-                            hit[kb] |= h;
+                            for (int i = 0; i < 4; ++i) {
+                                const float v = s[qg][kb][i];
+                                float d = __builtin_fmaxf(a.x_delta - __builtin_fmaf(v, c8, -m_use[qg]),
+                                                          a2 - __builtin_fabsf(v));
+                                if constexpr (kMasked) d = ((vis[qg] >> (kb * 4 + i)) & 1u) ? d : __builtin_inff();
+                                dmin = __builtin_fminf(dmin, d);
+                            }
+                            hit[kb] = (qg == 0 ? 0 : hit[kb]) | wave_ballot(dmin <= 0.0f);
                         }
+                } else {
+#pragma unroll
+                    for (int kb = 0; kb < 4; ++kb) hit[kb] = 0;
+#pragma unroll
+                    for (int qg = 0; qg < kQG; ++qg)
+#pragma unroll
+                        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+                            for (int i = 0; i < 4; ++i) {
+                                // each ballot of a compare is that compare's lane
+                                // mask; the masks combine in scalar registers
+                                const float v = s[qg][kb][i];
+                                uint64_t h = wave_ballot(__builtin_fmaf(v, c8, -m_use[qg]) >= a.x_delta) &
+                                             wave_ballot(__builtin_fabsf(v) >= a2);
+                                if constexpr (kMasked) h &= wave_ballot((vis[qg] >> (kb * 4 + i)) & 1u);
+                                hit[kb] |= h;
+                            }
+                }
             }
         } else if constexpr (kTest == 2) {
             // first stage off: every visible entry is active; |acc| >= a2 holds
@@ -856,6 +879,12 @@ hipError_t launch_d(const Shape& sh, const AttnParams& p, hipStream_t st) {
         {{lamp_attn_kernel<D, false, 4>, lamp_attn_kernel<D, false, 5>, lamp_attn_kernel<D, false, 6>},
          {lamp_attn_kernel<D, true, 4>, lamp_attn_kernel<D, true, 5>, lamp_attn_kernel<D, true, 6>}}};
     Fn fn = table[p.logit8 ? 1 : 0][dump ? 1 : 0][a.test_mode];
+    // Small tau: rows whose running max is below -t2 - x_delta take the
+    // per-entry test, and with t2 + x_delta <= -5 nearly every wave does;
+    // there its vector form is faster (measured 256 against 275 us at
+    // tau = 2^-3, qwen3-8b), elsewhere slower (240 against 221 at 2^-2).
+    if (!p.logit8 && !p.plain && a.test_mode == 1 && a.t2 + a.x_delta <= -5.0f)
+        fn = dump ? lamp_attn_kernel<D, true, 9> : lamp_attn_kernel<D, false, 9>;
     if (p.plain) {
         if constexpr (Cfg<D>::kPP) {
             fn = dump ? lamp_attn_kernel<D, true, 3> : lamp_attn_kernel<D, false, 3>;
