@@ -260,7 +260,10 @@ def run_decode(args, cfg, q, k, v):
     cb = None
     if not args.no_cpu_baseline:
         cores = max(1, min(len(os.sched_getaffinity(0)), 16))
-        cb = cpu_baseline_decode(q, k, v, cfg, args.delta, args.tau, tps, args.cpu_budget, cores)
+        # the first head also quantises its K and V slabs, so it overstates the
+        # per-head time about fourfold: a quarter of the budget gives the
+        # prefill line's 20-30 s of CPU work
+        cb = cpu_baseline_decode(q, k, v, cfg, args.delta, args.tau, tps, args.cpu_budget / 4, cores)
     import torch
     import mixed_precision_attention_lamp_amd as lamp
     dev = torch.device("cuda:0")
