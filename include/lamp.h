@@ -2,11 +2,11 @@
  * lamp.h -- C ABI of the MI355X (gfx950) LampAttention forward pass.
  *
  * The method is the one of "LampAttention: Look-Ahead Mixed-Precision
- * FlashAttention for Dedicated Accelerators" (abstract): a FlashAttention whose
- * key-query products are accumulated and whose exponentials are evaluated in
- * 8-bit formats; sensitive sub-blocks are then identified (look-ahead test with
- * parameters delta and tau, figure 1-8 captions) and recomputed in 16-bit
- * formats.  Tables 1-6 report the number of 16-bit sub-blocks per tile.
+ * FlashAttention for Dedicated Accelerators" (abstract): a FlashAttention that
+ * sums key-query products and takes exponentials with 8-bit number formats,
+ * finds the sensitive sub-blocks (look-ahead test with parameters delta and
+ * tau, figure 1-8 captions) and redoes only those with 16-bit ones.  Tables
+ * 1-6 count the 16-bit sub-blocks of each tile.
  *
  * Readings this library implements (the pages give no formula, format or size):
  *   - tiles of 64 query rows x 64 keys, four 64 x 16 sub-blocks per tile;
@@ -29,7 +29,10 @@
  *     nothing is launched and nothing is written.  The return value is LAMP_OK
  *     or a negative error code; lamp_last_error() gives a message.
  *   - The library owns one device workspace per device (K8, a transposed copy
- *     of V, scales); it only grows, and lamp_release_workspace() frees it.
+ *     of V, scales, decode split results); it only grows, and
+ *     lamp_release_workspace() frees it.  Every call's kernels use it, so calls
+ *     on one device must not overlap in time: issue them on one stream, or
+ *     synchronise before switching streams.
  *   - Inputs must be finite.  Not thread-safe for concurrent calls sharing a
  *     device; the stream and the last error are per host thread.
  */
