@@ -46,6 +46,9 @@ CONFIGS = {
     "qwen3-8b-decode": dict(B=8, Hq=32, Hkv=8, S=16384, Sq=16, D=128, causal=1, window=0,
                             structure="channels", seed=6,
                             desc="Qwen3-8B-shaped decode, 16 queries against 16384 cached keys, B=8"),
+    "qwen3-8b-decode-1": dict(B=8, Hq=32, Hkv=8, S=16384, Sq=1, D=128, causal=1, window=0,
+                              structure="channels", seed=6,
+                              desc="Qwen3-8B-shaped decode, one query against 16384 cached keys, B=8"),
 }
 
 
