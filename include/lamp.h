@@ -33,8 +33,11 @@
  *     lamp_release_workspace() frees it.  Every call's kernels use it, so calls
  *     on one device must not overlap in time: issue them on one stream, or
  *     synchronise before switching streams.
- *   - Inputs must be finite.  Not thread-safe for concurrent calls sharing a
- *     device; the stream and the last error are per host thread.
+ *   - Inputs must be finite, and every Q and K head whose largest magnitude
+ *     is not 0 has it at least 2^-119, so that the inverse scale 448/amax is
+ *     finite in fp32 (then no scaled value rounds beyond +-448).  Not
+ *     thread-safe for concurrent calls sharing a device; the stream and the
+ *     last error are per host thread.
  */
 #ifndef LAMP_H
 #define LAMP_H

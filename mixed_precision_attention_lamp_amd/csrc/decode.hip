@@ -60,38 +60,62 @@ struct DCfg {
     static constexpr int kKS = D >= 128 ? D / 128 : 1;   // 128-deep FP8 steps
     static constexpr int kK8Row = D;
     static constexpr int kK16Row = 2 * D;
-    static constexpr int kVtRow = 2 * kTileKeys;
+    static constexpr int kVRow = 2 * D;
     static constexpr int kK8Bytes = kTileKeys * kK8Row;
     static constexpr int kK16Bytes = kTileKeys * kK16Row;
-    static constexpr int kVtBytes = D * kVtRow;
+    static constexpr int kVBytes = kTileKeys * kVRow;
     static constexpr int kK8Off = 0;
     static constexpr int kK16Off = kK8Bytes;
-    static constexpr int kVtOff = kK16Off + kK16Bytes;
-    static constexpr int kLdsBytes = kVtOff + kVtBytes;
+    static constexpr int kVOff = kK16Off + kK16Bytes;
+    static constexpr int kLdsBytes = kVOff + kVBytes;
     static constexpr int kDB = D / 16;
     static constexpr int kDC = D / 32;
     static constexpr int kRowChunks = D / 8;                     // 16-byte chunks per K/V row
     static constexpr int kCh = kTileKeys * kRowChunks / kThreads;   // chunks per thread and tile
     static_assert(kCh * kThreads == kTileKeys * kRowChunks, "tile chunks must split evenly");
-    // A thread stages runs of kRun consecutive keys at one 16-byte column, so
-    // that the transposed V values of a run fill kRun adjacent positions.
+    // A thread stages runs of kRun consecutive keys at one 16-byte column.
     static constexpr int kRun = kCh < 4 ? kCh : 4;
     static constexpr int kRuns = kCh / kRun;                     // runs per thread and tile
 };
 
-// Byte offset of 16-byte chunk `chunk` of row d of the staged V^T tile (64
-// positions, 128 bytes per row).  The chunks are XOR-swizzled by
-// (d ^ d / 8) mod 8: the P.V operand reads (rows d .. d+15 at one chunk) and
-// the transposing stores (rows 8c + x for 16 columns c at one position) both
-// spread over all eight chunk slots.
-__device__ __forceinline__ int vt_off(int d, int chunk) {
-    return d * (2 * kTileKeys) + ((chunk ^ ((d ^ (d >> 3)) & 7)) << 4);
+// Two fp32 values -> two e4m3fn codes, without the clamp of cvt_pk_e4m3: for
+// values below 464 in magnitude, which round to at most 448.
+template <bool Hi>
+__device__ __forceinline__ uint32_t cvt_pk_e4m3_in_range(float a, float b, uint32_t old) {
+    return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, (int)old, Hi);
+}
+
+// The P.V operand of d-block db and key half h, read from the staged V tile
+// (row-major, one row per key, 16-byte chunks swizzled like the K16 tile) by
+// two transposing LDS reads.  ds_read_b64_tr_b16 treats each 16-lane group as
+// a 16 x 4 matrix of 16-bit values (lane l' supplies the 4 values at its
+// address) and hands lane m element k of row 4k + m/4, column m % 4 (checked
+// on the device).  So lane 4k + jj of group g reads 4 consecutive depths
+// 16db + 4jj .. of key K(g, k), and lane n16 of group g receives depth
+// 16db + n16 of keys K(g, 0..3).  K(g, k) = 32h + 4g + k (first read) and
+// that + 16 (second): the order in which the exponentials of the Q.K^T
+// output layout sit in the P operand of lane group g.
+template <int D>
+__device__ __forceinline__ v8bf v_operand_tr(const uint8_t* vl, int h, int db, int n16, int g) {
+    typedef short v4s __attribute__((ext_vector_type(4)));
+    typedef short v8s __attribute__((ext_vector_type(8)));
+    typedef __attribute__((address_space(3))) v4s lds_v4s;
+    const int key = 32 * h + 4 * g + (n16 >> 2);
+    const int dd = 16 * db + 4 * (n16 & 3);   // first depth of this lane's read
+    const int in_chunk = (dd & 7) * 2;
+    const uint8_t* p0 = vl + lds_off<2 * D>(key, dd >> 3) + in_chunk;
+    const uint8_t* p1 = vl + lds_off<2 * D>(key + 16, dd >> 3) + in_chunk;
+    const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(__attribute__((address_space(3))) const void*)p0);
+    const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(__attribute__((address_space(3))) const void*)p1);
+    const v8s x = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    return __builtin_bit_cast(v8bf, x);
 }
 
 // Query row i (sequence position Skv - Sq + i) sees key j.
 __device__ __forceinline__ bool dec_visible(int i, int j, int Sq, int Skv, int causal, int window) {
     const int p = Skv - Sq + i;
-    return i < Sq && j < Skv && (!causal || j <= p) && (window <= 0 || p - j < window);
+    // bitwise, not short-circuit: selects rather than branches
+    return (i < Sq) & (j < Skv) & ((causal == 0) | (j <= p)) & ((window <= 0) | (p - j < window));
 }
 
 // kW waves; kMode: 0 = no test (second stage off), 1 = both stages, 2 =
@@ -123,6 +147,7 @@ __global__ __launch_bounds__(kW * 64, 2) void lamp_decode_kernel(DecodeArgs a) {
         hq[j] = hk * a.G + (hv[j] ? gh : 0);
     }
     const bool row_ok = n16 < a.Sq;
+    const uint64_t row_mask = wave_ballot(row_ok);   // lanes of rows 0 .. Sq-1
 
     // tiles of this split; with a window the tiles before t_lo hold no visible key
     const int t_begin = split * a.tps;
@@ -219,7 +244,7 @@ __global__ __launch_bounds__(kW * 64, 2) void lamp_decode_kernel(DecodeArgs a) {
     };
     uint8_t* k8l = lds + C::kK8Off;
     uint8_t* k16l = lds + C::kK16Off;
-    uint8_t* vtl = lds + C::kVtOff;
+    uint8_t* vl = lds + C::kVOff;
     auto store = [&](const u32x4 (&rk)[C::kCh], const u32x4 (&rv)[C::kCh]) __attribute__((always_inline)) {
 #pragma unroll
         for (int r = 0; r < C::kRuns; ++r) {
@@ -232,37 +257,18 @@ __global__ __launch_bounds__(kW * 64, 2) void lamp_decode_kernel(DecodeArgs a) {
                 // K16 tile: logical chunk col of row key
                 *reinterpret_cast<u32x4*>(k16l + lds_off<C::kK16Row>(key, col)) = w;
                 // K8 tile: the 8 codes of depth 8col.. fill half of logical chunk col / 2
+                // (|k| <= amax, so |k * k_inv| rounds to at most 448: no clamp)
                 float y[8];
 #pragma unroll
                 for (int x = 0; x < 4; ++x) {
                     y[2 * x] = bf16_bits_to_float(w[x] & 0xFFFFu) * k_inv;
                     y[2 * x + 1] = bf16_bits_to_float(w[x] >> 16) * k_inv;
                 }
-                const u32x2 o = {cvt_pk_e4m3<true>(y[2], y[3], cvt_pk_e4m3<false>(y[0], y[1], 0u)),
-                                 cvt_pk_e4m3<true>(y[6], y[7], cvt_pk_e4m3<false>(y[4], y[5], 0u))};
+                const u32x2 o = {cvt_pk_e4m3_in_range<true>(y[2], y[3], cvt_pk_e4m3_in_range<false>(y[0], y[1], 0u)),
+                                 cvt_pk_e4m3_in_range<true>(y[6], y[7], cvt_pk_e4m3_in_range<false>(y[4], y[5], 0u))};
                 *reinterpret_cast<u32x2*>(k8l + lds_off<C::kK8Row>(key, col >> 1) + (col & 1) * 8) = o;
-            }
-            // V^T tile: within each 32-key half, key 16 hi + 4 gk + i sits at
-            // position 8 gk + 4 hi + i of rows d = 8col .. 8col+7 (the order in
-            // which lane group gk of the P.V operand reads its 8 positions); the
-            // kRun keys of a run (i = key0 % 4 ..) fill adjacent positions
-            const int pos = (key0 & 32) + ((key0 & 15) >> 2) * 8 + ((key0 & 16) >> 2) + (key0 & 3);
-#pragma unroll
-            for (int x = 0; x < 8; ++x) {
-                const int d = col * 8 + x;
-                uint32_t v16[C::kRun];
-#pragma unroll
-                for (int e = 0; e < C::kRun; ++e) {
-                    const uint32_t w = rv[r * C::kRun + e][x >> 1];
-                    v16[e] = (x & 1) ? (w >> 16) : (w & 0xFFFFu);
-                }
-                uint8_t* dst = vtl + vt_off(d, pos >> 3) + (pos & 7) * 2;
-                if constexpr (C::kRun == 4)
-                    *reinterpret_cast<u32x2*>(dst) = u32x2{v16[0] | (v16[1] << 16), v16[2] | (v16[3] << 16)};
-                else if constexpr (C::kRun == 2)
-                    *reinterpret_cast<uint32_t*>(dst) = v16[0] | (v16[1] << 16);
-                else
-                    *reinterpret_cast<uint16_t*>(dst) = (uint16_t)v16[0];
+                // V tile: as loaded, at the K16 tile's offsets (the P.V reads transpose)
+                *reinterpret_cast<u32x4*>(vl + lds_off<C::kVRow>(key, col)) = rv[r * C::kRun + e];
             }
         }
     };
@@ -286,20 +292,23 @@ __global__ __launch_bounds__(kW * 64, 2) void lamp_decode_kernel(DecodeArgs a) {
                         s[j][kb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
                             ka, qf[j][st], st == 0 ? v4f{0.f, 0.f, 0.f, 0.f} : s[j][kb], 0, 0, 0, 0, 0, 0);
                 }
-            // visibility of this lane's 16 entries (bit 4kb + i)
+            // visibility: an entry whose key its row does not see gets the logit
+            // -inf, so that its exponential is 0 and the sub-block maxima ignore
+            // it.  Tiles that every row sees whole (all but the causal, window
+            // and Skv edges) skip this; there the rows past Sq (zero Q operands,
+            // logits 0) are left out of the test by row_mask.
             const int j_last = t * kTileKeys + kTileKeys - 1;
             const bool all_rows_see_all = j_last < a.Skv && (!a.causal || j_last <= a.Skv - a.Sq) &&
                                           (a.window <= 0 || (a.Skv - 1) - t * kTileKeys < a.window);
-            uint32_t vis = 0u;
-            if (all_rows_see_all) {
-                vis = row_ok ? 0xFFFFu : 0u;
-            } else {
+            if (!all_rows_see_all) {
 #pragma unroll
                 for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-                    for (int i = 0; i < 4; ++i)
-                        vis |= (dec_visible(n16, t * kTileKeys + kb * 16 + g * 4 + i, a.Sq, a.Skv, a.causal, a.window)
-                                    ? 1u : 0u) << (kb * 4 + i);
+                    for (int i = 0; i < 4; ++i) {
+                        const bool vv = dec_visible(n16, t * kTileKeys + kb * 16 + g * 4 + i, a.Sq, a.Skv, a.causal, a.window);
+#pragma unroll
+                        for (int j = 0; j < kQG; ++j) s[j][kb][i] = vv ? s[j][kb][i] : kNegInf;
+                    }
             }
 
             // ---- (2)-(3) running max and 8-bit exponentials, per query head
@@ -313,9 +322,9 @@ __global__ __launch_bounds__(kW * 64, 2) void lamp_decode_kernel(DecodeArgs a) {
                     float hi = kNegInf, lo = -kNegInf;
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
-                        const bool vv = (vis >> (kb * 4 + i)) & 1u;
-                        hi = __builtin_fmaxf(hi, vv ? s[j][kb][i] : kNegInf);
-                        lo = __builtin_fminf(lo, vv ? s[j][kb][i] : -kNegInf);
+                        hi = __builtin_fmaxf(hi, s[j][kb][i]);
+                        if constexpr (kMode == 2)   // the minimum over seen keys only
+                            lo = __builtin_fminf(lo, s[j][kb][i] == kNegInf ? -kNegInf : s[j][kb][i]);
                     }
                     smax[j][kb] = hi;
                     smin[j][kb] = lo;
@@ -334,10 +343,8 @@ __global__ __launch_bounds__(kW * 64, 2) void lamp_decode_kernel(DecodeArgs a) {
                 for (int kb = 0; kb < 4; ++kb) {
                     float e[4];
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
+                    for (int i = 0; i < 4; ++i)   // 2^-inf = 0 for unseen keys
                         e[i] = fast_exp2(__builtin_fmaf(s[j][kb][i], c8[j], -m_use[j]));
-                        e[i] = ((vis >> (kb * 4 + i)) & 1u) ? e[i] : 0.0f;
-                    }
                     const uint32_t w = cvt_pk_e4m3_unit<true>(
                         e[2], e[3], cvt_pk_e4m3_unit<false>(e[0], e[1], __float_as_uint(e[0])));
                     P[j][kb] = u32x2{e4m3x2_to_bf16x2<false>(w), e4m3x2_to_bf16x2<true>(w)};
@@ -363,10 +370,11 @@ __global__ __launch_bounds__(kW * 64, 2) void lamp_decode_kernel(DecodeArgs a) {
                             hit[kb] = 0;
 #pragma unroll
                             for (int i = 0; i < 4; ++i) {
+                                // (x_delta may be -inf: unseen keys are excluded explicitly)
                                 const float v = s[j][kb][i];
                                 hit[kb] |= wave_ballot(__builtin_fmaf(v, c8[j], -m_use[j]) >= a.x_delta) &
                                            wave_ballot(__builtin_fabsf(v) >= a2[j]) &
-                                           wave_ballot((vis >> (kb * 4 + i)) & 1u);
+                                           wave_ballot(v != kNegInf);
                             }
                         }
                     }
@@ -377,7 +385,7 @@ __global__ __launch_bounds__(kW * 64, 2) void lamp_decode_kernel(DecodeArgs a) {
                 }
                 uint32_t f = 0;
 #pragma unroll
-                for (int kb = 0; kb < 4; ++kb) f |= (hit[kb] != 0 ? 1u : 0u) << kb;
+                for (int kb = 0; kb < 4; ++kb) f |= ((hit[kb] & row_mask) != 0 ? 1u : 0u) << kb;
                 flags[j] = hv[j] ? f : 0u;
             }
 
@@ -404,9 +412,9 @@ __global__ __launch_bounds__(kW * 64, 2) void lamp_decode_kernel(DecodeArgs a) {
                     if (!((flags[j] >> c) & 1u)) continue;
                     float e[4];
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
+                    for (int i = 0; i < 4; ++i) {   // unseen keys: 8-bit logit -inf
                         e[i] = fast_exp2(__builtin_fmaf(acc16[j][i], c16, -m_use[j]));
-                        e[i] = ((vis >> (c * 4 + i)) & 1u) ? e[i] : 0.0f;
+                        e[i] = s[j][c][i] == kNegInf ? 0.0f : e[i];
                     }
                     P[j][c] = u32x2{f32x2_to_bf16x2(e[0], e[1]), f32x2_to_bf16x2(e[2], e[3])};
                 }
@@ -431,7 +439,7 @@ __global__ __launch_bounds__(kW * 64, 2) void lamp_decode_kernel(DecodeArgs a) {
                 }
 #pragma unroll
                 for (int db = 0; db < C::kDB; ++db) {
-                    const v8bf va = *reinterpret_cast<const v8bf*>(vtl + vt_off(db * 16 + n16, h * 4 + g));
+                    const v8bf va = v_operand_tr<D>(vl, h, db, n16, g);
 #pragma unroll
                     for (int j = 0; j < kQG; ++j)
                         acc_o[j][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb[j], acc_o[j][db], 0, 0, 0);
