@@ -42,6 +42,10 @@ DECODE = [
     (1, 4, 2, 16, 2000, 128, 1, 0, 0.0, 0.0, 4, "channels", 211),            # every sub-block 16-bit
     (1, 12, 2, 16, 800, 128, 1, 0, 2 ** -8, 2 ** -1, 2, "channels", 212),    # G = 6
     (1, 8, 2, 16, 1100, 64, 1, 0, 2 ** -8, 2 ** -3, 100, "channels+drift", 213),  # one split
+    # rows past Sq and window / Skv edge tiles with the first stage off
+    (1, 4, 2, 7, 1300, 128, 1, 200, 0.0, 2 ** -3, 3, "channels", 214),
+    # the same with both stages, on drifting keys (per-entry test on edge tiles)
+    (1, 8, 2, 5, 1250, 128, 1, 150, 2 ** -8, 2 ** -4, 2, "channels+drift", 215),
 ]
 
 
