@@ -42,8 +42,8 @@ TRAFFIC = {"kernel_hash": "83dce971bb47ae85", "workload": "qwen3-8b", "delta": 2
 
 # The same for the decode kernel on the qwen3-8b-decode workload
 # (profiles/decode_qwen3_8b_hbm_traffic.md), library split.
-TRAFFIC_DECODE = {"kernel_hash": "b5f41ec6cf1f2a94", "workload": "qwen3-8b-decode", "delta": 2.0 ** -8,
-                  "tau": 2.0 ** -1, "bytes_per_launch": 555263352.5}
+TRAFFIC_DECODE = {"kernel_hash": "165cea9948202861", "workload": "qwen3-8b-decode", "delta": 2.0 ** -8,
+                  "tau": 2.0 ** -1, "bytes_per_launch": 555159408.6}
 
 
 def decode_source_hash():

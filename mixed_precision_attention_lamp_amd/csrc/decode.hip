@@ -161,7 +161,15 @@ __global__ __launch_bounds__(kW * 64, 2) void lamp_decode_kernel(DecodeArgs a) {
     // mask bytes of the split's tiles collect in LDS (one row of tps bytes per
     // wave) and go out after the loop: no global store inside the loop, where
     // it would make the compiler wait for every outstanding load
+    // mask bytes of the split's tiles.  D <= 128: lane i of mask_reg holds the
+    // byte of tile t_first + 64 c + i; the 64 bytes of chunk c go out when the
+    // loop leaves it (one global store per 64 tiles).  D = 256: one row of tps
+    // bytes per wave in LDS, written out after the loop.  Either way no global
+    // store in every iteration, where it would make the compiler wait for
+    // every outstanding load.
     uint8_t* mask_lds = lds + C::kLdsBytes + wave * a.tps_pad;
+    uint32_t mask_reg = 0;
+    uint8_t* const mrow = a.mask && hv[0] ? a.mask + ((size_t)b * a.Hq + hq[0]) * a.nT : nullptr;
 
     // ---- prologue: Q operands and constants per query head -------------------------
     v8i qf[kQG][C::kKS];
@@ -227,7 +235,7 @@ __global__ __launch_bounds__(kW * 64, 2) void lamp_decode_kernel(DecodeArgs a) {
     const uint16_t* v_head = a.v16 + kv_head * (size_t)a.Skv * D;
     // two register sets (D <= 128): tiles t+1 and t+2 are in flight while
     // tile t is computed
-    u32x4 rkA[C::kCh], rvA[C::kCh], rkB[C::kCh], rvB[C::kCh];
+    u32x4 rkA[C::kCh], rvA[C::kCh];
     auto load = [&](int t, u32x4 (&rk)[C::kCh], u32x4 (&rv)[C::kCh]) __attribute__((always_inline)) {
 #pragma unroll
         for (int r = 0; r < C::kRuns; ++r) {
@@ -245,7 +253,7 @@ __global__ __launch_bounds__(kW * 64, 2) void lamp_decode_kernel(DecodeArgs a) {
     uint8_t* k8l = lds + C::kK8Off;
     uint8_t* k16l = lds + C::kK16Off;
     uint8_t* vl = lds + C::kVOff;
-    auto store = [&](const u32x4 (&rk)[C::kCh], const u32x4 (&rv)[C::kCh]) __attribute__((always_inline)) {
+    auto store = [&](const u32x4 (&rk)[C::kCh], const u32x4 (&rv)[C::kCh], const int so) __attribute__((always_inline)) {
 #pragma unroll
         for (int r = 0; r < C::kRuns; ++r) {
             const int u = tid + r * kDThreads;
@@ -255,7 +263,7 @@ __global__ __launch_bounds__(kW * 64, 2) void lamp_decode_kernel(DecodeArgs a) {
                 const int key = key0 + e;
                 const u32x4 w = rk[r * C::kRun + e];
                 // K16 tile: logical chunk col of row key
-                *reinterpret_cast<u32x4*>(k16l + lds_off<C::kK16Row>(key, col)) = w;
+                *reinterpret_cast<u32x4*>(k16l + so + lds_off<C::kK16Row>(key, col)) = w;
                 // K8 tile: the 8 codes of depth 8col.. fill half of logical chunk col / 2
                 // (|k| <= amax, so |k * k_inv| rounds to at most 448: no clamp)
                 float y[8];
@@ -266,9 +274,9 @@ __global__ __launch_bounds__(kW * 64, 2) void lamp_decode_kernel(DecodeArgs a) {
                 }
                 const u32x2 o = {cvt_pk_e4m3_in_range<true>(y[2], y[3], cvt_pk_e4m3_in_range<false>(y[0], y[1], 0u)),
                                  cvt_pk_e4m3_in_range<true>(y[6], y[7], cvt_pk_e4m3_in_range<false>(y[4], y[5], 0u))};
-                *reinterpret_cast<u32x2*>(k8l + lds_off<C::kK8Row>(key, col >> 1) + (col & 1) * 8) = o;
+                *reinterpret_cast<u32x2*>(k8l + so + lds_off<C::kK8Row>(key, col >> 1) + (col & 1) * 8) = o;
                 // V tile: as loaded, at the K16 tile's offsets (the P.V reads transpose)
-                *reinterpret_cast<u32x4*>(vl + lds_off<C::kVRow>(key, col)) = rv[r * C::kRun + e];
+                *reinterpret_cast<u32x4*>(vl + so + lds_off<C::kVRow>(key, col)) = rv[r * C::kRun + e];
             }
         }
     };
@@ -277,7 +285,7 @@ __global__ __launch_bounds__(kW * 64, 2) void lamp_decode_kernel(DecodeArgs a) {
                        (__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f};
     constexpr float kNegInf = -__builtin_inff();
 
-    auto tile = [&](const int t) __attribute__((always_inline)) {
+    auto tile = [&](const int t, const int so) __attribute__((always_inline)) {
         // waves without a query head only stage tiles
         if (hv[0]) {
             // ---- (1) 8-bit logits: s[j][kb][i] = key 16kb + 4g + i, query row n16
@@ -286,7 +294,7 @@ __global__ __launch_bounds__(kW * 64, 2) void lamp_decode_kernel(DecodeArgs a) {
             for (int st = 0; st < C::kKS; ++st)
 #pragma unroll
                 for (int kb = 0; kb < 4; ++kb) {
-                    const v8i ka = fp8_operand<D>(k8l, kb * 16 + n16, st, g);
+                    const v8i ka = fp8_operand<D>(k8l + so, kb * 16 + n16, st, g);
 #pragma unroll
                     for (int j = 0; j < kQG; ++j)
                         s[j][kb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
@@ -401,7 +409,7 @@ __global__ __launch_bounds__(kW * 64, 2) void lamp_decode_kernel(DecodeArgs a) {
                 v4f acc16[kQG];
 #pragma unroll
                 for (int ch = 0; ch < C::kDC; ++ch) {
-                    const v8bf ka = *reinterpret_cast<const v8bf*>(k16l + lds_off<C::kK16Row>(c * 16 + n16, ch * 4 + g));
+                    const v8bf ka = *reinterpret_cast<const v8bf*>(k16l + so + lds_off<C::kK16Row>(c * 16 + n16, ch * 4 + g));
 #pragma unroll
                     for (int j = 0; j < kQG; ++j)
                         acc16[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
@@ -439,7 +447,7 @@ __global__ __launch_bounds__(kW * 64, 2) void lamp_decode_kernel(DecodeArgs a) {
                 }
 #pragma unroll
                 for (int db = 0; db < C::kDB; ++db) {
-                    const v8bf va = v_operand_tr<D>(vl, h, db, n16, g);
+                    const v8bf va = v_operand_tr<D>(vl + so, h, db, n16, g);
 #pragma unroll
                     for (int j = 0; j < kQG; ++j)
                         acc_o[j][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb[j], acc_o[j][db], 0, 0, 0);
@@ -450,47 +458,57 @@ __global__ __launch_bounds__(kW * 64, 2) void lamp_decode_kernel(DecodeArgs a) {
             }
 
             // ---- (7) mask byte
-            if (lane == 0) mask_lds[t - t_begin] = (uint8_t)(0x80u | flags[0]);
+            if constexpr (D <= 128) {
+                if (lane == ((t - t_first) & 63)) mask_reg = 0x80u | flags[0];
+            } else {
+                if (lane == 0) mask_lds[t - t_begin] = (uint8_t)(0x80u | flags[0]);
+            }
         }
     };
 
     // Loads run every iteration; past the split's last tile they reload it
     // (from cache), which keeps the compiler from waiting on all loads at
-    // the loop head.  A barrier after the stores, and one after the tile
-    // (every wave has read it before the next one is stored).
+    // the loop head.
     if constexpr (D <= 128) {
+        // Two LDS slots.  The stores of tile t+1 go to the slot tile t does not
+        // read, in the same block as tile t's work, and one barrier per tile
+        // orders both: every wave has read a slot before it is refilled, and
+        // the stores of t+1 are visible before t+1 is read.
+        constexpr int kSlot = C::kLdsBytes;
+        if (mrow)   // tiles before t_first (outside the window) hold no visible key
+            for (int i = t_begin + lane; i < t_first; i += 64) mrow[i] = 0;
         if (t_first <= t_end) {
             load(t_first, rkA, rvA);
-            load(min(t_first + 1, t_end), rkB, rvB);
+            store(rkA, rvA, 0);
+            load(min(t_first + 1, t_end), rkA, rvA);
         }
-        // two tiles per iteration; an odd last tile leaves a spare half (staged, not computed)
-        for (int t = t_first; t <= t_end; t += 2) {
-            store(rkA, rvA);
-            lds_barrier();
+        lds_barrier();
+        for (int t = t_first; t <= t_end; ++t) {
+            const int so = ((t - t_first) & 1) * kSlot;
+            store(rkA, rvA, kSlot - so);
             load(min(t + 2, t_end), rkA, rvA);
-            tile(t);
-            lds_barrier();
-            store(rkB, rvB);
-            lds_barrier();
-            load(min(t + 3, t_end), rkB, rvB);
-            if (t + 1 <= t_end) tile(t + 1);
+            tile(t, so);
+            if (((t - t_first) & 63) == 63 || t == t_end) {
+                const int t0 = t - ((t - t_first) & 63);
+                if (mrow && t0 + lane <= t) mrow[t0 + lane] = (uint8_t)mask_reg;
+                mask_reg = 0;
+            }
             lds_barrier();
         }
     } else {
-        // D = 256: one register set (two would not fit next to the accumulators)
+        // D = 256: one slot, one register set (two would not fit next to the
+        // accumulators); a barrier after the stores, one after the tile
         if (t_first <= t_end) load(t_first, rkA, rvA);
         for (int t = t_first; t <= t_end; ++t) {
-            store(rkA, rvA);
+            store(rkA, rvA, 0);
             lds_barrier();
             load(min(t + 1, t_end), rkA, rvA);
-            tile(t);
+            tile(t, 0);
             lds_barrier();
         }
-    }
-    if (a.mask && hv[0]) {
-        uint8_t* mrow = a.mask + ((size_t)b * a.Hq + hq[0]) * a.nT + t_begin;
-        for (int i = lane; i <= t_end - t_begin; i += 64)
-            mrow[i] = t_begin + i < t_first ? (uint8_t)0 : mask_lds[i];
+        if (mrow)
+            for (int i = lane; i <= t_end - t_begin; i += 64)
+                mrow[t_begin + i] = t_begin + i < t_first ? (uint8_t)0 : mask_lds[i];
     }
 
     // ---- the split's running max, row sum and unnormalised output ----------------------
@@ -560,7 +578,8 @@ hipError_t launch_decode_d(const DecodeShape& sh, const DecodeParams& p, hipStre
         {lamp_decode_kernel<D, 8, 0>, lamp_decode_kernel<D, 8, 1>, lamp_decode_kernel<D, 8, 2>}};
     const bool wide = a.G > 4 || D == 256;
     const Fn fn = table[wide ? 1 : 0][mode];
-    const int lds = DCfg<D, 256>::kLdsBytes + (wide ? 8 : 4) * a.tps_pad;
+    // D <= 128: two tile slots; D = 256: one slot and the mask bytes
+    const int lds = D <= 128 ? 2 * DCfg<D, 256>::kLdsBytes : DCfg<D, 256>::kLdsBytes + 8 * a.tps_pad;
     if (lds > 160 * 1024) return hipErrorInvalidValue;
     hipError_t e = hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
     if (e != hipSuccess) return e;

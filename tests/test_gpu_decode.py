@@ -46,6 +46,10 @@ DECODE = [
     (1, 4, 2, 7, 1300, 128, 1, 200, 0.0, 2 ** -3, 3, "channels", 214),
     # the same with both stages, on drifting keys (per-entry test on edge tiles)
     (1, 8, 2, 5, 1250, 128, 1, 150, 2 ** -8, 2 ** -4, 2, "channels+drift", 215),
+    # one split of 79 tiles: mask bytes of more than 64 tiles per split
+    (1, 4, 2, 16, 5000, 128, 1, 0, 2 ** -8, 2 ** -1, 79, "channels", 216),
+    # a window that starts inside the second 64-tile chunk of a split
+    (1, 4, 4, 3, 9000, 64, 1, 4700, 2 ** -8, 2 ** -1, 141, "channels", 217),
 ]
 
 
