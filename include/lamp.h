@@ -177,11 +177,13 @@ int lamp_debug_attn_dump_logit8(const void* q, const void* k, const void* v, flo
                                 uint8_t* subblock_mask_out, float* logit8_out, uint16_t* p_out);
 
 /* Per-kernel timing with HIP events recorded on the library's stream, for
- * benches.  While enabled (enable = 1), every lamp_attn_fwd call records one
- * event before its quantisation/transpose kernels, one between them and the
- * attention kernel and one after it.  lamp_read_timing waits for those
- * events, returns the summed milliseconds of the two phases and the number of
- * calls, and starts a new accumulation.  Event objects are created on first
+ * benches.  While enabled (enable = 1), every lamp_attn_fwd and
+ * lamp_attn_decode call records one event before its preparation kernels
+ * (quantisation and transpose; for decode the K amax and the scales), one
+ * between them and the attention (decode) kernel and one right after that
+ * kernel (the decode merge follows it, untimed).  lamp_read_timing waits for
+ * those events, returns the summed milliseconds of the two phases and the
+ * number of calls, and starts a new accumulation.  Event objects are created on first
  * use and reused; at most 4096 calls are recorded between two reads. */
 int lamp_set_timing(int enable);
 int lamp_read_timing(double* prep_ms, double* attn_ms, int* n_calls);

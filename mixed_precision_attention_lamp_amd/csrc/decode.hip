@@ -584,11 +584,6 @@ hipError_t launch_decode_d(const DecodeShape& sh, const DecodeParams& p, hipStre
     hipError_t e = hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(fn, dim3(sh.B * sh.Hkv * sh.n_split), dim3(wide ? 512 : 256), lds, st, a);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    const int rows = sh.B * sh.Hq * sh.Sq;
-    hipLaunchKernelGGL(decode_merge_kernel, dim3((rows * (D / 4) + 255) / 256), dim3(256), 0, st, p.part_o,
-                       p.part_ml, p.out, rows, sh.Sq, sh.n_split, D);
     return hipGetLastError();
 }
 
@@ -599,6 +594,13 @@ hipError_t launch_decode(const DecodeShape& sh, const DecodeParams& p, hipStream
     if (sh.D == 128) return launch_decode_d<128>(sh, p, st);
     if (sh.D == 256) return launch_decode_d<256>(sh, p, st);
     return hipErrorInvalidValue;
+}
+
+hipError_t launch_decode_merge(const DecodeShape& sh, const DecodeParams& p, hipStream_t st) {
+    const int rows = sh.B * sh.Hq * sh.Sq;
+    hipLaunchKernelGGL(decode_merge_kernel, dim3((rows * (sh.D / 4) + 255) / 256), dim3(256), 0, st, p.part_o,
+                       p.part_ml, p.out, rows, sh.Sq, sh.n_split, sh.D);
+    return hipGetLastError();
 }
 
 }  // namespace lamp

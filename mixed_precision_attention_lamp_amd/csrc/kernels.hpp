@@ -96,7 +96,10 @@ hipError_t launch_decode_scales(const DecodeShape& sh, const uint16_t* q, const 
 
 // The decode kernel (one workgroup per batch, kv head and split) and the merge
 // of the splits into out.
+// The decode kernel (split results into the workspace), then the merge of
+// the splits into out.
 hipError_t launch_decode(const DecodeShape& sh, const DecodeParams& p, hipStream_t st);
+hipError_t launch_decode_merge(const DecodeShape& sh, const DecodeParams& p, hipStream_t st);
 
 // Compute units of the current device (256 when it cannot be queried).
 int cu_count();

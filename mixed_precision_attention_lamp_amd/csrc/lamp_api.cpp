@@ -405,6 +405,8 @@ int lamp_attn_decode(const void* q, const void* k, const void* v, float* out, in
     e = lamp::launch_decode(sh, p, g_stream);
     if (e != hipSuccess) return hip_fail(e, "decode launch");
     if (ev) (void)hipEventRecord(ev[2], g_stream);
+    e = lamp::launch_decode_merge(sh, p, g_stream);
+    if (e != hipSuccess) return hip_fail(e, "decode merge launch");
     return LAMP_OK;
 }
 
