@@ -104,13 +104,58 @@ def _oracle_unit(unit):
     return unit
 
 
-def cpu_baseline(q, k, v, cfg, delta, tau, budget_s, cores):
-    """Time the oracle on sampled units of the same workload (reported baseline)."""
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _oracle_expectation(unit):
+    """Worker: the parity protocol's oracle-side expectation of one unit
+    (output rows, mask bytes, excusable flags, flip bound)."""
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    import parity
+    return unit, parity.unit_expectation(_CTX, *unit)
+
+
+def parity_units(B, Hq, nT, n=32, seed=77):
+    """Units the bench's parity check compares: the first and last row block
+    of four heads, then random units."""
+    rng = np.random.default_rng(seed)
+    units = set()
+    for h in np.linspace(0, Hq - 1, 4).astype(int):
+        b = int(rng.integers(B))
+        units.update({(b, int(h), 0), (b, int(h), nT - 1)})
+    while len(units) < min(n, B * Hq * nT):
+        units.add((int(rng.integers(B)), int(rng.integers(Hq)), int(rng.integers(nT))))
+    return sorted(units)
+
+
+def single_core_tiny():
+    """Seconds of one core for the whole tiny workload through the oracle."""
+    from inputs import make_config_inputs
+    from oracle import lamp as L
+    q, k, v, cfg = make_config_inputs("tiny")
+    t0 = time.perf_counter()
+    L.lamp_forward(q, k, v, cfg["causal"], cfg["window"], 2.0 ** -8, 2.0 ** -1)
+    return time.perf_counter() - t0
+
+
+def cpu_baseline(q, k, v, cfg, delta, tau, budget_s, cores, with_parity=True):
+    """Time the oracle on sampled units of the same workload (reported
+    baseline), then (untimed) compute the parity protocol's expectation of
+    the units the bench compares with the device output afterwards."""
     global _CTX
     import multiprocessing as mp
     from threadpoolctl import threadpool_limits
     from oracle import lamp as L
     threadpool_limits(1)
+    tiny_s = single_core_tiny()
     _CTX = L.prepare(q, k, v, cfg["causal"], cfg["window"], delta, tau)
     B, Hq, S, D = q.shape
     nT = L.n_tiles(S)
@@ -123,20 +168,55 @@ def cpu_baseline(q, k, v, cfg, delta, tau, budget_s, cores):
     one = max(time.perf_counter() - t0, 1e-3)
     n = max(cores, min(len(units), int(budget_s * cores / one)))
     sample = units[:n]
+    expectations = {}
     t0 = time.perf_counter()
     if cores > 1:
         with mp.get_context("fork").Pool(cores) as pool:
             for _ in pool.imap_unordered(_oracle_unit, sample, chunksize=1):
                 pass
+            wall = time.perf_counter() - t0
+            if with_parity:
+                for u, e in pool.imap_unordered(_oracle_expectation, parity_units(B, Hq, nT), chunksize=1):
+                    expectations[u] = e
     else:
         for u in sample:
             _oracle_unit(u)
-    wall = time.perf_counter() - t0
+        wall = time.perf_counter() - t0
+        if with_parity:
+            for u in parity_units(B, Hq, nT):
+                expectations[u] = _oracle_expectation(u)[1]
     flops = sum(4.0 * D * unit_pairs(r, S, cfg["causal"], cfg["window"]) for (_, _, r) in sample)
     return dict(value=flops / wall / 1e12, unit="TFLOP/s", cores=cores, kind="oracle",
                 sample=f"{len(sample)} random (batch, head, 64-row block) units of the same "
                        f"workload ({flops / 1e9:.2f} GFLOP nominal), {wall:.1f} s wall",
-                wall_s=wall)
+                cpu_model=cpu_model(), cpus_visible=os.cpu_count(),
+                single_core_tiny_workload_s=tiny_s, wall_s=wall), expectations
+
+
+def parity_block(expectations, out, mask):
+    """The oracle leg's check of the device output of the last timed step
+    against the expectations computed before the GPU was touched (the
+    protocol of tests/parity.py; host arrays only)."""
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    import parity
+    judged, n_sub = [], 0
+    S = out.shape[2]
+    for (b, h, r), e in sorted(expectations.items()):
+        rows = slice(r * 64, min(r * 64 + 64, S))
+        judged.append(parity.judge_unit(e, out[b, h, rows], mask[b, h, r], (b, h, r)))
+        n_sub += 4 * len(e["mask"])
+    rep = parity.summarize(judged, n_sub)
+    ok = (rep["finite"] and not rep["unexcused"] and not rep["rows_unexplained"]
+          and rep["mean_abs"] <= parity.MEAN_ABS and rep["max_abs"] <= parity.MAX_ABS_CAP
+          and rep["rows_above"] <= parity.MAX_ROWS_ABOVE * rep["rows_compared"])
+    n_mis = len(rep["excused"]) + len(rep["unexcused"])
+    return {"units": len(expectations), "rows": rep["rows_compared"], "max_abs": rep["max_abs"],
+            "mean_abs": rep["mean_abs"], "rows_above_4e-3": rep["rows_above"],
+            "rows_above_frac": rep["rows_above"] / max(rep["rows_compared"], 1),
+            "rows_unexplained": len(rep["rows_unexplained"]), "mask_subblocks": n_sub,
+            "mask_mismatches": n_mis, "excused": len(rep["excused"]),
+            "within_one_ulp": rep["excused_within_one_ulp"], "unexcused": len(rep["unexcused"]),
+            "pass": bool(ok)}
 
 
 # --------------------------------------------------------------------------
@@ -163,7 +243,7 @@ def decode_subblock_entries(Sq, Skv, causal, window):
     return vis.sum(axis=0).reshape(nT, 4, 16).sum(axis=2)
 
 
-def measure_decode(lamp, torch, tensors, shape, causal, window, delta, tau, tps, steps, warmup):
+def measure_decode(lamp, torch, tensors, shape, causal, window, delta, tau, tps, steps, warmup, settle_ms=0.0):
     """Time `steps` lamp_attn_decode calls after `warmup`; returns the step
     time, the decode kernel time and the amax and scale pass time (HIP
     events on the library's stream; the merge of the splits is in the step
@@ -174,6 +254,7 @@ def measure_decode(lamp, torch, tensors, shape, causal, window, delta, tau, tps,
     def step():
         lamp.lamp_attn_decode(qd, kd, vd, out, causal, window, delta, tau, tps, mask)
 
+    settle(torch, step, settle_ms)
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
@@ -277,7 +358,7 @@ def run_decode(args, cfg, q, k, v):
     out = torch.empty((B, Hq, Sq, D), dtype=torch.float32, device=dev)
     mask = torch.empty((B, Hq, nT), dtype=torch.uint8, device=dev)
     m = measure_decode(lamp, torch, (qd, kd, vd, out, mask), (B, Hq, Hkv, Sq, Skv, D), causal, window,
-                       args.delta, args.tau, tps, args.steps, args.warmup)
+                       args.delta, args.tau, tps, args.steps, args.warmup, settle_ms=args.settle_ms)
     n_split = (nT + tps - 1) // tps
     # algorithmic bytes of the decode kernel: K and V read once (bf16), Q
     # read, the split results and the mask bytes written
@@ -326,8 +407,22 @@ LOGIT8_NOTE = "8-bit logits (e4m3-rounded log2-domain logit)"
 LOGIT8_POINTS = ((2.0 ** -8, 2.0 ** -1), (2.0 ** -8, float("inf")), (2.0 ** -4, 2.0 ** -1))
 
 
+def settle(torch, step, settle_ms):
+    """Run the step until `settle_ms` of wall time have passed, before the
+    warm-up steps: the GPU's clocks take on the order of a hundred launches
+    of this kernel to reach their sustained level, and the timed steps are
+    meant to see that level.  Returns the number of steps run."""
+    n, t0 = 0, time.perf_counter()
+    while (time.perf_counter() - t0) * 1e3 < settle_ms:
+        for _ in range(20):
+            step()
+        n += 20
+        torch.cuda.synchronize()
+    return n
+
+
 def measure(lamp, torch, tensors, shape, causal, window, delta, tau, steps, warmup, plain=False,
-            logit8=False):
+            logit8=False, settle_ms=0.0):
     """Time `steps` calls of lamp_attn_fwd (lamp_attn_fwd_bf16 when plain,
     lamp_attn_fwd_logit8 when logit8) after `warmup` untimed ones; returns the
     step time, the attention kernel
@@ -344,6 +439,7 @@ def measure(lamp, torch, tensors, shape, causal, window, delta, tau, steps, warm
         else:
             lamp.lamp_attn_fwd(qd, kd, vd, out, causal, window, delta, tau, mask)
 
+    settle_steps = settle(torch, step, settle_ms)
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
@@ -367,7 +463,7 @@ def measure(lamp, torch, tensors, shape, causal, window, delta, tau, steps, warm
     f_qk16 = 2.0 * D * stats["flagged_entries"]
     return dict(ms_per_step=total_ms / steps, attn_ms=attn_ms / max(ncalls, 1),
                 prep_ms=prep_ms / max(ncalls, 1), pairs=pairs, f_nom=4.0 * D * pairs,
-                f_qk8=f_qk8, f_pv=f_pv, f_qk16=f_qk16, stats=stats)
+                f_qk8=f_qk8, f_pv=f_pv, f_qk16=f_qk16, stats=stats, settle_steps=settle_steps)
 
 
 def roofline_of(m):
@@ -387,6 +483,7 @@ def run_grid(args, lamp, torch, tensors, shape, causal, window, cfg):
     runs += [(d, t, LOGIT8_NOTE) for d, t in LOGIT8_POINTS]
     for delta, tau, note in runs:
         m = measure(lamp, torch, tensors, shape, causal, window, delta, tau, args.steps, args.warmup,
+                    settle_ms=args.settle_ms / 3,
                     plain=note == PLAIN_NOTE, logit8=note == LOGIT8_NOTE)
         achieved, peak = roofline_of(m)
         print(json.dumps({
@@ -407,6 +504,8 @@ def main():
     ap.add_argument("--tau", type=float, default=2.0 ** -1)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--settle-ms", type=float, default=300.0,
+                    help="run the step this long before the warm-up steps (clock settling)")
     ap.add_argument("--copy-calibrate", action="store_true")
     ap.add_argument("--grid", action="store_true",
                     help="time the (delta, tau) grid and the two endpoints instead of one point")
@@ -431,10 +530,11 @@ def main():
 
     # The CPU baseline runs first, in worker processes forked before this
     # process touches the GPU.
-    cb = None
+    cb, expectations = None, {}
     if not args.no_cpu_baseline and not args.grid:
+        # the machine's CPU share is 16 threads per GPU, whatever the host shows
         cores = max(1, min(len(os.sched_getaffinity(0)), 16))
-        cb = cpu_baseline(q, k, v, cfg, args.delta, args.tau, args.cpu_budget, cores)
+        cb, expectations = cpu_baseline(q, k, v, cfg, args.delta, args.tau, args.cpu_budget, cores)
         cb.pop("wall_s", None)
 
     import torch
@@ -455,12 +555,17 @@ def main():
         run_grid(args, lamp, torch, tensors, shape, causal, window, cfg)
         return
     m = measure(lamp, torch, tensors, shape, causal, window, args.delta, args.tau, args.steps,
-                args.warmup)
+                args.warmup, settle_ms=args.settle_ms)
+    parity = parity_block(expectations, out.cpu().numpy(), mask.cpu().numpy()) if expectations else None
     ms_per_step, attn_ms_avg, prep_ms_avg = m["ms_per_step"], m["attn_ms"], m["prep_ms"]
     stats, f_nom = m["stats"], m["f_nom"]
     achieved, blended_peak = roofline_of(m)
     nq, nk = B * Hq * S * D, B * Hkv * S * D
     quant_bytes = 3.0 * (nq + nk)
+    # algorithmic bytes of the launches before the attention kernel: Q and K
+    # read for their maxima, K read again and its e4m3 codes written, V read
+    # and written transposed
+    prep_bytes = 2.0 * (nq + nk) + 3.0 * nk + 4.0 * nk
     t_mfma = m["f_qk8"] / PEAK_FP8 + (m["f_pv"] + m["f_qk16"]) / PEAK_BF16
     t_roof = t_mfma + quant_bytes / PEAK_HBM
     traffic = None
@@ -488,9 +593,13 @@ def main():
                      "unit": "TFLOP/s", "frac": achieved / blended_peak, "traffic": traffic},
         "blended_roofline_frac": t_roof / (ms_per_step * 1e-3),
         "kernel_ms": {"attention": attn_ms_avg, "quantise_and_transpose": prep_ms_avg},
+        "prep_hbm": {"bytes": prep_bytes, "GB/s": prep_bytes / (prep_ms_avg * 1e-3) / 1e9,
+                     "frac": prep_bytes / (prep_ms_avg * 1e-3) / PEAK_HBM},
+        "settle_steps": m["settle_steps"],
         "recompute": {"r_sb": stats["r_sb"], "r_e": stats["r_e"], "hist_0_to_4": stats["hist"],
                       "tiles_0_1_2plus": stats["pages_buckets"]},
     }
+    res["parity"] = parity
     res["cpu_baseline"] = cb
     print(json.dumps(res), flush=True)
 

@@ -28,16 +28,20 @@
  *   - Arguments are validated before any HIP call; on a validation error
  *     nothing is launched and nothing is written.  The return value is LAMP_OK
  *     or a negative error code; lamp_last_error() gives a message.
- *   - The library owns one device workspace per device (K8, a transposed copy
- *     of V, scales, decode split results); it only grows, and
- *     lamp_release_workspace() frees it.  Every call's kernels use it, so calls
- *     on one device must not overlap in time: issue them on one stream, or
- *     synchronise before switching streams.
+ *   - The library owns one device workspace per (device, stream) pair (K8, a
+ *     transposed copy of V, scales, decode split results), allocated on the
+ *     first call on that stream; it only grows (the old buffer is freed after
+ *     that stream drains), and lamp_release_workspace() frees all of them.
+ *     Calls on different streams use different workspaces and may overlap in
+ *     time; calls on one stream run in order.  At most 64 (device, stream)
+ *     pairs hold a workspace at a time (LAMP_ERR_UNSUPPORTED beyond that).
+ *     LAMP_WORKSPACE_LIMIT_BYTES (environment, bytes) caps one workspace:
+ *     a call that needs more returns LAMP_ERR_NOMEM and launches nothing.
  *   - Inputs must be finite, and every Q and K head whose largest magnitude
  *     is not 0 has it at least 2^-119, so that the inverse scale 448/amax is
- *     finite in fp32 (then no scaled value rounds beyond +-448).  Not
- *     thread-safe for concurrent calls sharing a device; the stream and the
- *     last error are per host thread.
+ *     finite in fp32 (then no scaled value rounds beyond +-448).  The stream
+ *     and the last error are per host thread; host threads may call
+ *     concurrently on distinct streams.
  */
 #ifndef LAMP_H
 #define LAMP_H
@@ -141,9 +145,16 @@ int lamp_attn_fwd_bf16(const void* q, const void* k, const void* v, float* out,
 int lamp_subblock_stats(const uint8_t* subblock_mask, int B, int Hq, int S,
                         int causal, int window, int64_t* stats_out);
 
-/* The quantisation step on its own (per-head amax scales, e4m3 codes), for tests.
- * q8 [B,Hq,S,D] and k8 [B,Hkv,S,D] receive e4m3fn byte codes; q_scale [B*Hq] and
- * k_scale [B*Hkv] receive fl32(amax/448) (1 for an all-zero head).  Device pointers. */
+/* The quantisation step on its own, for tests: Q and K brought to the 8-bit
+ * format in which the key-query products are formed ("LampAttention", abstract:
+ * 8-bit formats for the products).  Per (batch, head) the largest magnitude
+ * amax of the bf16 slab gives the scale fl32(amax/448) and the inverse scale
+ * fl32(448/amax) (both 1 for an all-zero head); each element x becomes the
+ * e4m3fn code of fl32(x * inverse scale), nearest even.
+ *   q [B,Hq,S,D], k [B,Hkv,S,D] bf16 device tensors as for lamp_attn_fwd.
+ *   q8 [B,Hq,S,D], k8 [B,Hkv,S,D]: uint8 device outputs (e4m3fn codes, 16-byte
+ *   aligned); q_scale [B*Hq], k_scale [B*Hkv]: fp32 device outputs (the scales).
+ * Sizes and errors as lamp_attn_fwd; uses the workspace of the current stream. */
 int lamp_quantize_qk(const void* q, const void* k, int B, int Hq, int Hkv, int S, int D,
                      uint8_t* q8, uint8_t* k8, float* q_scale, float* k_scale);
 
@@ -155,6 +166,18 @@ int lamp_quantize_qk(const void* q, const void* k, int B, int Hq, int Hkv, int S
  * All device pointers (any may be null), n elements. */
 int lamp_debug_convert(const float* x, int64_t n, uint8_t* e4m3, uint16_t* e4m3_bf16,
                        uint16_t* bf16, float* exp2);
+
+/* The instruction that forms the 8-bit key-query products of lamp_attn_fwd
+ * ("LampAttention", abstract: products in 8-bit formats), on given operands,
+ * for tests of its accumulation: for each of n_blocks blocks,
+ *   out[blk][i][j] = sum_{d<128} a[blk][i][d] * b[blk][j][d]
+ * as the gfx950 FP8 matrix instruction of the attention kernel computes it
+ * (e4m3fn operands, fp32 result; the hardware keeps a limited number of bits
+ * below the largest product, so this is not the exactly rounded sum).
+ *   a, b  uint8 device arrays [n_blocks, 16, 128] of e4m3fn codes (no NaN codes);
+ *   out   fp32 device array [n_blocks, 16, 16].
+ * 0 <= n_blocks <= 2^20; pointers 16-byte aligned. */
+int lamp_debug_fp8_dot(const uint8_t* a, const uint8_t* b, float* out, int n_blocks);
 
 /* lamp_attn_fwd plus a dump of its per-entry intermediates, for tests on small
  * shapes (S <= 2048).  For every visible (query i, key j) of head (b, hq):
@@ -194,7 +217,7 @@ int lamp_set_stream(void* hip_stream);
 /* Message of the last non-OK return on this host thread ("" if none). */
 const char* lamp_last_error(void);
 
-/* Free the device workspace (synchronises the device first). */
+/* Free every workspace (synchronises each device that holds one first). */
 void lamp_release_workspace(void);
 
 /* Library version: major * 10000 + minor * 100 + patch. */

@@ -899,7 +899,31 @@ hipError_t launch_d(const Shape& sh, const AttnParams& p, hipStream_t st) {
     return hipGetLastError();
 }
 
+// Test hook: the 8-bit Q.K^T instruction of the attention kernel on given
+// operand blocks.  One wave per block: a [16 rows][128] and b [16 rows][128]
+// e4m3 codes, out [16][16] fp32 = a . b^T, with the operand arrangement of
+// qk() (lane group g holds depth 32g .. 32g+31 of row n16 of each operand).
+__global__ __launch_bounds__(64) void debug_fp8_dot_kernel(const uint8_t* __restrict__ a,
+                                                           const uint8_t* __restrict__ b, float* out,
+                                                           int n) {
+    const int blk = blockIdx.x;
+    if (blk >= n) return;
+    const int lane = threadIdx.x, n16 = lane & 15, g = lane >> 4;
+    const v8i ka = fp8_operand_global<128>(a + ((size_t)blk * 16 + n16) * 128, 0, g);
+    const v8i qb = fp8_operand_global<128>(b + ((size_t)blk * 16 + n16) * 128, 0, g);
+    const v4f s = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ka, qb, v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0,
+                                                                    0, 0, 0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) out[((size_t)blk * 16 + 4 * g + i) * 16 + n16] = s[i];
+}
+
 }  // namespace
+
+hipError_t launch_debug_fp8_dot(const uint8_t* a, const uint8_t* b, float* out, int n, hipStream_t st) {
+    if (n <= 0) return hipSuccess;
+    hipLaunchKernelGGL(debug_fp8_dot_kernel, dim3((unsigned)n), dim3(64), 0, st, a, b, out, n);
+    return hipGetLastError();
+}
 
 hipError_t launch_attention(const Shape& sh, const AttnParams& p, hipStream_t st) {
     if (sh.D == 64) return launch_d<64>(sh, p, st);

@@ -108,6 +108,10 @@ int cu_count();
 hipError_t launch_subblock_stats(const uint8_t* mask, int B, int Hq, int S, int causal,
                                  int window, int64_t* stats, hipStream_t st);
 
+// n blocks of a [16][128] . b [16][128]^T (e4m3 codes) -> out [16][16] fp32 on
+// the attention kernel's 8-bit Q.K^T instruction.
+hipError_t launch_debug_fp8_dot(const uint8_t* a, const uint8_t* b, float* out, int n, hipStream_t st);
+
 hipError_t launch_debug_convert(const float* x, int64_t n, uint8_t* e4m3, uint16_t* e4m3_bf16,
                                 uint16_t* bf16, float* exp2, hipStream_t st);
 

@@ -21,18 +21,39 @@ constexpr int kMaxDevices = 64;
 thread_local hipStream_t g_stream = nullptr;
 thread_local std::string g_error;
 
+// One workspace per (device, stream): kernels of calls on different streams
+// never share scratch memory, so such calls may overlap in time.
 struct Workspace {
+    int dev = -1;
+    hipStream_t stream = nullptr;
     void* ptr = nullptr;
     size_t bytes = 0;
 };
+constexpr int kMaxWorkspaces = 64;
 std::mutex g_ws_mutex;
-Workspace g_ws[kMaxDevices];
+Workspace g_ws[kMaxWorkspaces];
 
 // Event timing of lamp_attn_fwd phases (lamp_set_timing / lamp_read_timing).
 constexpr int kMaxTimed = 4096;
 thread_local bool g_timing = false;
 thread_local int g_n_timed = 0;
 thread_local hipEvent_t g_events[kMaxTimed][3];
+
+// The next free slot of three events, or null when timing is off or every
+// slot is taken.  The slot counts as used only after timing_commit, which a
+// call reaches once all of its launches have been enqueued: a call that fails
+// part way leaves no half-recorded slot behind.
+hipEvent_t* timing_slot() {
+    if (!g_timing || g_n_timed >= kMaxTimed) return nullptr;
+    hipEvent_t* ev = g_events[g_n_timed];
+    for (int i = 0; i < 3; ++i)
+        if (!ev[i] && hipEventCreate(&ev[i]) != hipSuccess) return nullptr;
+    return ev;
+}
+
+void timing_commit(hipEvent_t* ev) {
+    if (hipEventRecord(ev[2], g_stream) == hipSuccess) ++g_n_timed;
+}
 
 int fail(int code, const char* fmt, ...) {
     char buf[512];
@@ -58,9 +79,10 @@ size_t workspace_limit() {
     return (size_t)std::strtoull(s, nullptr, 10);
 }
 
-// Returns LAMP_OK and a device pointer to at least `bytes` of workspace on the
-// current device.  Grows only; the old buffer is freed after a device-wide
-// synchronisation, since kernels on any stream may still read it.
+// Returns LAMP_OK and a device pointer to at least `bytes` of workspace for
+// the current device and the calling thread's stream.  Grows only; the old
+// buffer is freed after that stream has drained, since only kernels on it
+// read that buffer.
 int get_workspace(size_t bytes, void** out) {
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
@@ -69,11 +91,20 @@ int get_workspace(size_t bytes, void** out) {
     if (bytes > workspace_limit())
         return fail(LAMP_ERR_NOMEM, "workspace of %zu bytes exceeds LAMP_WORKSPACE_LIMIT_BYTES", bytes);
     std::lock_guard<std::mutex> lock(g_ws_mutex);
-    Workspace& ws = g_ws[dev];
+    Workspace* slot = nullptr;
+    for (auto& w : g_ws)
+        if (w.dev == dev && w.stream == g_stream) { slot = &w; break; }
+    if (!slot)
+        for (auto& w : g_ws)
+            if (w.dev < 0) { slot = &w; w.dev = dev; w.stream = g_stream; break; }
+    if (!slot)
+        return fail(LAMP_ERR_UNSUPPORTED, "more than %d (device, stream) pairs hold a workspace; "
+                    "call lamp_release_workspace", kMaxWorkspaces);
+    Workspace& ws = *slot;
     if (ws.bytes < bytes) {
         if (ws.ptr) {
-            e = hipDeviceSynchronize();
-            if (e != hipSuccess) return hip_fail(e, "hipDeviceSynchronize");
+            e = hipStreamSynchronize(g_stream);
+            if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
             (void)hipFree(ws.ptr);
             ws.ptr = nullptr;
             ws.bytes = 0;
@@ -242,13 +273,7 @@ static int attn_fwd_impl(const void* q, const void* k, const void* v, float* out
     auto* k8 = base + L.k8;
     auto* vt = reinterpret_cast<uint16_t*>(base + L.vt);
 
-    hipEvent_t* ev = nullptr;
-    if (g_timing && g_n_timed < kMaxTimed) {
-        ev = g_events[g_n_timed];
-        for (int i = 0; i < 3 && ev; ++i)
-            if (!ev[i] && hipEventCreate(&ev[i]) != hipSuccess) ev = nullptr;
-        if (ev) ++g_n_timed;
-    }
+    hipEvent_t* ev = timing_slot();
     if (ev) (void)hipEventRecord(ev[0], g_stream);
     auto* q_inv = reinterpret_cast<float*>(base + L.q_inv);
     // amax partial maxima and the V transpose, then scales and K8 (the
@@ -276,7 +301,7 @@ static int attn_fwd_impl(const void* q, const void* k, const void* v, float* out
     p.logit8 = logit8;
     e = lamp::launch_attention(sh, p, g_stream);
     if (e != hipSuccess) return hip_fail(e, "attention launch");
-    if (ev) (void)hipEventRecord(ev[2], g_stream);
+    if (ev) timing_commit(ev);
     return LAMP_OK;
 }
 
@@ -387,13 +412,7 @@ int lamp_attn_decode(const void* q, const void* k, const void* v, float* out, in
     p.causal = causal;
     p.window = window;
 
-    hipEvent_t* ev = nullptr;
-    if (g_timing && g_n_timed < kMaxTimed) {
-        ev = g_events[g_n_timed];
-        for (int i = 0; i < 3 && ev; ++i)
-            if (!ev[i] && hipEventCreate(&ev[i]) != hipSuccess) ev = nullptr;
-        if (ev) ++g_n_timed;
-    }
+    hipEvent_t* ev = timing_slot();
     if (ev) (void)hipEventRecord(ev[0], g_stream);
     hipError_t e = lamp::launch_decode_scales(sh, p.q16, p.k16, reinterpret_cast<uint32_t*>(base + o_partial),
                                               reinterpret_cast<float*>(base + o_qs),
@@ -404,7 +423,7 @@ int lamp_attn_decode(const void* q, const void* k, const void* v, float* out, in
     if (ev) (void)hipEventRecord(ev[1], g_stream);
     e = lamp::launch_decode(sh, p, g_stream);
     if (e != hipSuccess) return hip_fail(e, "decode launch");
-    if (ev) (void)hipEventRecord(ev[2], g_stream);
+    if (ev) timing_commit(ev);
     e = lamp::launch_decode_merge(sh, p, g_stream);
     if (e != hipSuccess) return hip_fail(e, "decode merge launch");
     return LAMP_OK;
@@ -419,7 +438,11 @@ int lamp_set_timing(int enable) {
 int lamp_read_timing(double* prep_ms, double* attn_ms, int* n_calls) {
     if (!prep_ms || !attn_ms || !n_calls) return fail(LAMP_ERR_INVALID, "outputs must be non-null");
     double a = 0.0, b = 0.0;
-    for (int i = 0; i < g_n_timed; ++i) {
+    const int n = g_n_timed;
+    // the slots are released whatever happens below, so that one failed read
+    // does not make every later one fail too
+    g_n_timed = 0;
+    for (int i = 0; i < n; ++i) {
         hipEvent_t* ev = g_events[i];
         hipError_t e = hipEventSynchronize(ev[2]);
         if (e != hipSuccess) return hip_fail(e, "hipEventSynchronize");
@@ -433,8 +456,7 @@ int lamp_read_timing(double* prep_ms, double* attn_ms, int* n_calls) {
     }
     *prep_ms = a;
     *attn_ms = b;
-    *n_calls = g_n_timed;
-    g_n_timed = 0;
+    *n_calls = n;
     return LAMP_OK;
 }
 
@@ -480,6 +502,18 @@ int lamp_debug_convert(const float* x, int64_t n, uint8_t* e4m3, uint16_t* e4m3_
     return LAMP_OK;
 }
 
+int lamp_debug_fp8_dot(const uint8_t* a, const uint8_t* b, float* out, int n_blocks) {
+    if (n_blocks < 0 || n_blocks > (1 << 20))
+        return fail(LAMP_ERR_INVALID, "n_blocks must be in [0, 2^20] (got %d)", n_blocks);
+    if (n_blocks == 0) return LAMP_OK;
+    if (!a || !b || !out) return fail(LAMP_ERR_INVALID, "a, b and out must be non-null");
+    if (!aligned16(a) || !aligned16(b) || !aligned16(out))
+        return fail(LAMP_ERR_INVALID, "a, b and out must be 16-byte aligned");
+    hipError_t e = lamp::launch_debug_fp8_dot(a, b, out, n_blocks, g_stream);
+    if (e != hipSuccess) return hip_fail(e, "fp8 dot launch");
+    return LAMP_OK;
+}
+
 int lamp_set_stream(void* hip_stream) {
     g_stream = static_cast<hipStream_t>(hip_stream);
     return LAMP_OK;
@@ -490,17 +524,18 @@ const char* lamp_last_error(void) { return g_error.c_str(); }
 void lamp_release_workspace(void) {
     std::lock_guard<std::mutex> lock(g_ws_mutex);
     bool any = false;
-    for (auto& ws : g_ws) any |= ws.ptr != nullptr;
+    for (auto& ws : g_ws) any |= ws.dev >= 0;
     if (!any) return;
-    (void)hipDeviceSynchronize();
     int cur = 0;
     (void)hipGetDevice(&cur);
-    for (int d = 0; d < kMaxDevices; ++d) {
-        if (!g_ws[d].ptr) continue;
-        (void)hipSetDevice(d);
-        (void)hipFree(g_ws[d].ptr);
-        g_ws[d].ptr = nullptr;
-        g_ws[d].bytes = 0;
+    for (auto& ws : g_ws) {
+        if (ws.dev < 0) continue;
+        if (ws.ptr) {
+            (void)hipSetDevice(ws.dev);
+            (void)hipDeviceSynchronize();
+            (void)hipFree(ws.ptr);
+        }
+        ws = Workspace{};
     }
     (void)hipSetDevice(cur);
 }

@@ -479,19 +479,6 @@ def decode_forward(q_bits, k_bits, v_bits, causal=True, window=0, delta=2.0 ** -
     return out, mask
 
 
-def unit_fragility(ctx, b, hq, r, k=1):
-    """For one unit: {t: 4-bit set of sub-blocks whose flag is within k ulps}."""
-    trace = []
-    run_unit(ctx, b, hq, r, trace=trace)
-    res = {}
-    for rec in trace:
-        if rec.get("final"):
-            continue
-        fr = fragile_flags(rec["e"], rec["s2"], rec["vis"], ctx["delta"], rec["T2"], k)
-        res[rec["t"]] = sum(int(f) << c for c, f in enumerate(fr))
-    return res
-
-
 # --------------------------------------------------------------------------
 # Counters reported with every run (tables 1-6 "16-bit sub-blocks per tile")
 # --------------------------------------------------------------------------

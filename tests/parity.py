@@ -1,32 +1,39 @@
 """Parity protocol between the HIP path and the CPU oracle (test helper).
 
 The oracle sums the 8-bit key-query products exactly and rounds once to fp32.
-The gfx950 FP8 matrix cores do not: their internal accumulation keeps about
-11 bits below the largest product of each instruction (measured: error up to
-2^-10.9 max_d |q8_d k8_d| over random e4m3 codes; the bf16 matrix cores stay
-within 2^-20).  The device exp2 is a few fp32 ulps from the correctly
-rounded value.  Both are legitimate differences, so the protocol works with
-explicit windows around every statistic the method rounds or compares:
+The gfx950 FP8 matrix instructions do not: they keep a limited number of bits
+below the largest product of each instruction.  Measured on the device over
+262144 dot products of 128 uniformly random e4m3 codes the error reached
+2^-10.94 max_d |q8_d k8_d|, and 2^-11.12 over 524288 dot products of
+activation-like codes (Gaussian rows with log-normal channel scales and
+outlier channels, the workloads' recipe); test_fp8_accumulation_error keeps
+measuring both.  The bf16 matrix instructions stay within 2^-20 of the
+largest product.  The device exp2 is within 2 fp32 ulps of the correctly
+rounded value (test_device_exp2_error).  Both are legitimate differences, so
+the protocol works with explicit windows around every statistic the method
+rounds or compares:
 
-* 8-bit logit:  |d acc8| <= EPS_ACC8 * max_d |q8_d k8_d|  (checked on the
-  device itself by test_fp8_accumulation_bound), so
-  |d s2| <= c8 * that + 1 ulp, and the running max moves by at most the
-  largest such window of its row;
+* 8-bit logit:  |d acc8| <= EPS_ACC8 * max_d |q8_d k8_d|  (EPS_ACC8 = 2^-11,
+  the activation-like bound with a 9 % margin; the dump tests check it on
+  every visible entry they see), so |d s2| <= c8 * that + 1 ulp;
+* running max: the largest 8-bit logit window among the entries of its row
+  seen so far (the running max is one of them);
 * 16-bit logit: |d acc16| <= EPS_ACC16 * max_d |q_d k_d|;
 * exponentials: the argument moves by the logit window plus the max window,
   and exp2 itself by EXP2_ULPS fp32 ulps.
 
 Mask: bit-exact, except for sub-blocks whose flag the oracle itself flips
 when every statistic moves within its window ("excused").  The number of
-mismatches, and how many of them lie within one fp32 ulp of a threshold, is
-reported.  Outputs: mean |dO| <= 5e-4; a row with |dO| > 4e-3 must be
-explained by the weights that can legitimately differ -- those whose
-exponential lies within its window of an e4m3 (bf16) rounding midpoint (one
-such flip moves a weight by a whole 8-bit step, 1/16), and those of an
-excused sub-block, which the device took in the other precision -- i.e.
-|dO| <= 4e-3 + the first-order effect of changing all of them.  The oracle
-never takes anything from the device: an excused flag enters only as this
-bound.
+mismatches, how many of them are excused, and how many lie within one fp32
+ulp of a threshold are reported.  Outputs: mean |dO| <= 5e-4 and max |dO| <=
+MAX_ABS_CAP everywhere; a row with |dO| > 4e-3 must be explained by the
+weights that can legitimately differ -- those whose exponential lies within
+its window of an e4m3 (bf16) rounding midpoint (one such flip moves a weight
+by a whole 8-bit step) and those of an excused sub-block, which the device
+took in the other precision -- i.e. |dO| <= 4e-3 + the first-order effect of
+changing all of them; and at most MAX_ROWS_ABOVE of the compared rows may be
+above 4e-3.  The oracle never takes anything from the device: an excused
+flag enters only as this bound.
 """
 import sys
 
@@ -38,30 +45,40 @@ from oracle.formats import round_bf16, round_e4m3
 
 MAX_ABS = 4e-3
 MEAN_ABS = 5e-4
-EPS_ACC8 = 2.0 ** -9.5      # FP8 matrix-core accumulation, relative to the largest product
+MAX_ABS_CAP = 0.1           # no output may differ by more, explained or not
+MAX_ROWS_ABOVE = 0.08       # at most this fraction of compared rows above MAX_ABS
+EPS_ACC8 = 2.0 ** -11       # FP8 matrix-core accumulation, relative to the largest product
 EPS_ACC16 = 2.0 ** -18      # bf16 matrix-core accumulation, relative to the largest product
-EXP2_ULPS = 4               # device exp2 (measured <= 2)
+EXP2_ULPS = 2               # device exp2 (measured <= 2)
 
 
-def tile_windows(ctx, b, h, r, rec):
-    """Windows (ds2, dx, dx16), each [rows, cols], of one traced tile."""
+def unit_windows(ctx, b, h, r, trace):
+    """{t: (ds2, dx, dx16)}, each [rows, cols], for the traced tiles of one unit
+    (or of one decode split: a trace restarts the running max).  ds2 bounds
+    the 8-bit logit, dx the argument of the 8-bit exponential and dx16 that
+    of the 16-bit one; the running max window is the largest 8-bit logit
+    window of its row over every tile seen so far."""
     G = ctx["G"]
-    rows = np.arange(r * 64, r * 64 + rec["vis"].shape[0])
-    cols = rec["cols"]
-    q8 = ctx["q8"][b, h, rows]
-    k8 = ctx["k8"][b, h // G, cols]
-    maxp8 = np.max(np.abs(q8[:, None, :] * k8[None, :, :]), axis=2)
-    q16 = ctx["q16"][b, h, rows]
-    k16 = ctx["k16"][b, h // G, cols]
-    maxp16 = np.max(np.abs(q16[:, None, :] * k16[None, :, :]), axis=2)
     c8, c16 = L.logit_constants(ctx["D"], ctx["sq"][b, h], ctx["sk"][b, h // G])
-    s2 = np.where(rec["vis"], rec["s2"], 0.0)
-    ulp_s2 = np.spacing(np.abs(s2).astype(np.float32)).astype(np.float64)
-    ds2 = c8 * EPS_ACC8 * maxp8 + ulp_s2
-    dm = np.where(rec["vis"], ds2, 0.0).max(axis=1, keepdims=True)   # row max window (this tile)
-    dx = ds2 + dm
-    dx16 = c16 * EPS_ACC16 * maxp16 + dm
-    return ds2, dx, dx16
+    res, dm = {}, None
+    for rec in trace:
+        if rec.get("final"):
+            continue
+        rows = np.arange(r * 64, r * 64 + rec["vis"].shape[0])
+        cols = rec["cols"]
+        q8 = ctx["q8"][b, h, rows]
+        k8 = ctx["k8"][b, h // G, cols]
+        maxp8 = np.max(np.abs(q8[:, None, :] * k8[None, :, :]), axis=2)
+        q16 = ctx["q16"][b, h, rows]
+        k16 = ctx["k16"][b, h // G, cols]
+        maxp16 = np.max(np.abs(q16[:, None, :] * k16[None, :, :]), axis=2)
+        s2 = np.where(rec["vis"], rec["s2"], 0.0)
+        ulp_s2 = np.spacing(np.abs(s2).astype(np.float32)).astype(np.float64)
+        ds2 = c8 * EPS_ACC8 * maxp8 + ulp_s2
+        tile_dm = np.where(rec["vis"], ds2, 0.0).max(axis=1)
+        dm = tile_dm if dm is None else np.maximum(dm, tile_dm)
+        res[rec["t"]] = (ds2, ds2 + dm[:, None], c16 * EPS_ACC16 * maxp16 + dm[:, None])
+    return res
 
 
 def _e_bounds(e, dx):
@@ -71,14 +88,19 @@ def _e_bounds(e, dx):
     return np.maximum(lo, 0.0), hi
 
 
-def fragile_mask_bits(ctx, b, h, r, rec, one_ulp=False):
-    """4-bit set of sub-blocks whose flag can flip within the windows (or within
-    one fp32 ulp of each statistic when one_ulp)."""
+def fragile_mask_bits(ctx, b, h, r, rec, win=None, one_ulp=False):
+    """4-bit set of sub-blocks whose flag can flip within the windows ``win``
+    (this tile's entry of unit_windows; computed from the unit when None), or
+    within one fp32 ulp of each statistic when one_ulp."""
     vis, e, s2 = rec["vis"], rec["e"], rec["s2"]
     if one_ulp:
         fr = L.fragile_flags(e, s2, vis, ctx["delta"], rec["T2"], 1)
         return sum(int(f) << c for c, f in enumerate(fr))
-    ds2, dx, _ = tile_windows(ctx, b, h, r, rec)
+    if win is None:
+        trace = []
+        L.run_unit(ctx, b, h, r, trace=trace)
+        win = unit_windows(ctx, b, h, r, [x for x in trace if x.get("final") or x["t"] <= rec["t"]])[rec["t"]]
+    ds2, dx, _ = win
     e_lo, e_hi = _e_bounds(e, dx)
     a = np.abs(np.where(vis, s2, 0.0))
     res = []
@@ -88,11 +110,11 @@ def fragile_mask_bits(ctx, b, h, r, rec, one_ulp=False):
     return sum(int(lo != hi) << c for c, (lo, hi) in enumerate(zip(*res)))
 
 
-def fragile_alternatives(ctx, b, h, r, rec):
+def fragile_alternatives(ctx, b, h, r, rec, win):
     """|p_alt - p| for every weight whose exponential can round to the other
     neighbour within its window (0 elsewhere)."""
     vis, p, e, e16 = rec["vis"], rec["p"], rec["e"], rec["e16"]
-    _, dx, dx16 = tile_windows(ctx, b, h, r, rec)
+    _, dx, dx16 = win
     rec16 = ~np.isnan(e16)
     alt = np.zeros_like(p)
     lo, hi = _e_bounds(e, dx)
@@ -131,28 +153,65 @@ def flag_alternatives(ctx, b, h, r, rec, bits):
     return alt
 
 
-def flip_bound(ctx, b, h, r, flag_bits=None):
-    """Per (row, column) bound on |dO| from weights that can round the other
-    way and from the sub-blocks of ``flag_bits`` ({t: 4-bit set}) taken in the
-    other precision.
+def unit_expectation(ctx, b, h, r, flag_bits=None):
+    """Everything the protocol needs of one unit, from the oracle alone.
 
-    Returns (bound [rows, D], n_fragile) for unit (b, h, r)."""
+    Returns dict(out [rows, D], mask {t: byte}, wide {t: 4-bit set excusable
+    within the windows}, tight {t: 4-bit set within one fp32 ulp}, bound
+    [rows, D], n_fragile).  ``bound`` is the first-order effect on each output
+    of every weight that can round the other way, plus, for the sub-blocks of
+    ``flag_bits`` ({t: 4-bit set}; every excusable sub-block when None), of
+    taking the sub-block in the other precision."""
     trace = []
-    out, _ = L.run_unit(ctx, b, h, r, trace=trace)
+    out, mask = L.run_unit(ctx, b, h, r, trace=trace)
     fin = trace[-1]
+    wins = unit_windows(ctx, b, h, r, trace)
     vv = ctx["v"][b, h // ctx["G"]]
     bound = np.zeros_like(out)
-    n_fragile = 0
+    wide, tight, n_fragile = {}, {}, 0
     for rec in trace[:-1]:
-        alt = fragile_alternatives(ctx, b, h, r, rec)
+        t = rec["t"]
+        wide[t] = fragile_mask_bits(ctx, b, h, r, rec, wins[t])
+        tight[t] = fragile_mask_bits(ctx, b, h, r, rec, one_ulp=True)
+        alt = fragile_alternatives(ctx, b, h, r, rec, wins[t])
         n_fragile += int((alt > 0).sum())
-        if flag_bits:
-            alt = alt + flag_alternatives(ctx, b, h, r, rec, flag_bits.get(rec["t"], 0))
+        bits = wide[t] if flag_bits is None else flag_bits.get(t, 0)
+        alt = alt + flag_alternatives(ctx, b, h, r, rec, bits)
         scale = np.exp2(rec["m_new"] - fin["m"]) / fin["ell"]
-        w = alt * scale[:, None]
         vj = vv[rec["cols"]]
-        bound += np.einsum("ij,ijd->id", w, np.abs(vj[None, :, :] - out[:, None, :]))
-    return 1.1 * bound, n_fragile
+        bound += np.einsum("ij,ijd->id", alt * scale[:, None], np.abs(vj[None, :, :] - out[:, None, :]))
+    return dict(out=out, mask=mask, wide=wide, tight=tight, bound=1.1 * bound, n_fragile=n_fragile)
+
+
+def judge_unit(exp, out_dev, mask_dev, unit):
+    """Classify one unit's device result against its expectation.
+
+    ``out_dev`` [rows, D] and ``mask_dev`` [nT] are the device's rows of the
+    unit.  Returns dict(excused [(unit, t, dev, oracle)], unexcused [...],
+    within_one_ulp n, flipped {t: bits}, diff [rows, D], rows_above [i],
+    rows_unexplained [(unit, row, col, |dO|, bound)])."""
+    b, h, r = unit
+    want = np.zeros(mask_dev.shape[0], dtype=np.uint8)
+    for t, byte in exp["mask"].items():
+        want[t] = byte
+    excused, unexcused, flipped, n_one = [], [], {}, 0
+    for t in np.nonzero(mask_dev != want)[0]:
+        t = int(t)
+        x = int(mask_dev[t]) ^ int(want[t])
+        ok = (x & 0x80) == 0 and (x & ~exp["wide"].get(t, 0) & 0x0F) == 0
+        n_one += int((x & 0x80) == 0 and (x & ~exp["tight"].get(t, 0) & 0x0F) == 0)
+        (excused if ok else unexcused).append((b, h, r, t, int(mask_dev[t]), int(want[t])))
+        if ok:
+            flipped[t] = x & 0x0F
+    diff = np.abs(out_dev.astype(np.float64) - exp["out"].astype(np.float64))
+    above = np.nonzero((diff > MAX_ABS).any(axis=1))[0]
+    unexplained = []
+    for i in above:
+        if not np.all(diff[i] <= MAX_ABS + exp["bound"][i]):
+            j = int(np.argmax(diff[i] - exp["bound"][i]))
+            unexplained.append((b, h, r * 64 + int(i), j, float(diff[i, j]), float(exp["bound"][i, j])))
+    return dict(excused=excused, unexcused=unexcused, within_one_ulp=n_one, flipped=flipped, diff=diff,
+                rows_above=above, rows_unexplained=unexplained)
 
 
 def to_device(bits):
@@ -172,6 +231,31 @@ def say(msg):
     sys.stdout.flush()
 
 
+def summarize(judged, n_sub):
+    """Totals of judge_unit results: the parity figures reported everywhere."""
+    d = np.concatenate([j["diff"].reshape(-1) for j in judged]) if judged else np.zeros(1)
+    rows = sum(j["diff"].shape[0] for j in judged)
+    above = sum(len(j["rows_above"]) for j in judged)
+    unexpl = [u for j in judged for u in j["rows_unexplained"]]
+    return dict(max_abs=float(d.max()), mean_abs=float(d.mean()),
+                excused=[e for j in judged for e in j["excused"]],
+                unexcused=[e for j in judged for e in j["unexcused"]],
+                excused_within_one_ulp=sum(j["within_one_ulp"] for j in judged),
+                n_subblocks=n_sub, rows_compared=rows, rows_above=above,
+                rows_explained=above - len(unexpl), rows_unexplained=unexpl,
+                finite=bool(np.isfinite(d).all()))
+
+
+def report_line(tag, label, rep):
+    n_mis = len(rep["excused"]) + len(rep["unexcused"])
+    return (f"[{tag}] {label} max|dO|={rep['max_abs']:.3e} mean|dO|={rep['mean_abs']:.3e} "
+            f"mask mismatches {n_mis} of {rep['n_subblocks']} sub-blocks (excused {len(rep['excused'])}, "
+            f"within 1 ulp {rep['excused_within_one_ulp']}; unexcused {len(rep['unexcused'])}); "
+            f"rows above {MAX_ABS:g}: {rep['rows_above']} of {rep['rows_compared']} "
+            f"({rep['rows_above'] / max(rep['rows_compared'], 1):.2%}; explained by the flip bound "
+            f"{rep['rows_explained']}, unexplained {len(rep['rows_unexplained'])})")
+
+
 def compare(q, k, v, causal, window, delta, tau, units=None, gpu=None, label=""):
     """Run both sides and apply the protocol; returns a report dict (asserts nothing)."""
     B, Hq, S, D = q.shape
@@ -180,58 +264,20 @@ def compare(q, k, v, causal, window, delta, tau, units=None, gpu=None, label="")
     say(f"[parity] {label} B={B} Hq={Hq} Hkv={k.shape[1]} S={S} D={D} causal={causal} "
         f"window={window} delta={delta} tau={tau} units={len(units)}")
     out_g, mask_g = gpu if gpu is not None else run_gpu(q, k, v, causal, window, delta, tau)
-    out_o, mask_o = L.lamp_forward(q, k, v, causal, window, delta, tau, units=units)
     ctx = L.prepare(q, k, v, causal, window, delta, tau)
-    unexcused, excused, flipped = [], [], {}
-    n_one_ulp = 0
-    for (b, h, r) in units:
-        diff = np.nonzero(mask_g[b, h, r] != mask_o[b, h, r])[0]
-        if diff.size == 0:
-            continue
-        trace = []
-        L.run_unit(ctx, b, h, r, trace=trace)
-        recs = {rec["t"]: rec for rec in trace[:-1]}
-        for t in diff:
-            x = int(mask_g[b, h, r, t]) ^ int(mask_o[b, h, r, t])
-            rec = recs.get(int(t))
-            wide = fragile_mask_bits(ctx, b, h, r, rec) if rec is not None else 0
-            tight = fragile_mask_bits(ctx, b, h, r, rec, one_ulp=True) if rec is not None else 0
-            ok = (x & 0x80) == 0 and (x & ~wide & 0x0F) == 0
-            n_one_ulp += int((x & 0x80) == 0 and (x & ~tight & 0x0F) == 0)
-            (excused if ok else unexcused).append((b, h, r, int(t), int(mask_g[b, h, r, t]),
-                                                   int(mask_o[b, h, r, t])))
-            if ok:
-                flipped.setdefault((b, h, r), {})[int(t)] = x & 0x0F
-    rows_mask = np.zeros((B, Hq, S), dtype=bool)
-    for (b, h, r) in units:
-        rows_mask[b, h, r * 64:min(r * 64 + 64, S)] = True
-    diff = np.abs(out_g.astype(np.float64) - out_o.astype(np.float64))
-    d = diff[rows_mask]
-    # rows above the bound must be explained by weights near a rounding midpoint
-    explained, unexplained = 0, []
+    judged, n_sub = [], 0
     for (b, h, r) in units:
         rows = slice(r * 64, min(r * 64 + 64, S))
-        blk = diff[b, h, rows]
-        if not (blk > MAX_ABS).any():
-            continue
-        bnd, _ = flip_bound(ctx, b, h, r, flipped.get((b, h, r)))
-        for i in np.nonzero((blk > MAX_ABS).any(axis=1))[0]:
-            if np.all(blk[i] <= MAX_ABS + bnd[i]):
-                explained += 1
-            else:
-                j = int(np.argmax(blk[i] - bnd[i]))
-                unexplained.append((b, h, r * 64 + int(i), j, float(blk[i, j]), float(bnd[i, j])))
-    n_sub = sum(int(((mask_o[b, h, r] & 0x80) != 0).sum()) * 4 for (b, h, r) in units)
-    rep = dict(max_abs=float(d.max()), mean_abs=float(d.mean()), excused=excused,
-               unexcused=unexcused, excused_within_one_ulp=n_one_ulp, n_units=len(units),
-               n_subblocks=n_sub, rows_explained=explained, rows_unexplained=unexplained,
-               rows_compared=int(rows_mask.sum()),
-               finite=bool(np.isfinite(out_g[rows_mask]).all()))
-    say(f"[parity] {label} max|dO|={rep['max_abs']:.3e} mean|dO|={rep['mean_abs']:.3e} "
-        f"mask mismatches {len(excused) + len(unexcused)} of {n_sub} sub-blocks (excused "
-        f"{len(excused)}, of which within 1 ulp {n_one_ulp}; unexcused {len(unexcused)}); "
-        f"rows above {MAX_ABS:g}: {explained + len(unexplained)} of {rep['rows_compared']} "
-        f"(explained by the flip bound {explained}, unexplained {len(unexplained)})")
+        exp = unit_expectation(ctx, b, h, r, flag_bits={})
+        n_sub += 4 * len(exp["mask"])
+        j = judge_unit(exp, out_g[b, h, rows], mask_g[b, h, r], (b, h, r))
+        if j["flipped"] and j["rows_unexplained"]:
+            # bound the device's excused flags in the other precision
+            exp = unit_expectation(ctx, b, h, r, flag_bits=j["flipped"])
+            j = judge_unit(exp, out_g[b, h, rows], mask_g[b, h, r], (b, h, r))
+        judged.append(j)
+    rep = summarize(judged, n_sub)
+    say(report_line("parity", label, rep))
     return rep
 
 
@@ -324,6 +370,8 @@ def assert_parity(rep):
     assert not rep["unexcused"], f"unexcused mask mismatches: {rep['unexcused'][:10]}"
     assert not rep["rows_unexplained"], f"rows above {MAX_ABS}: {rep['rows_unexplained'][:10]}"
     assert rep["mean_abs"] <= MEAN_ABS, rep["mean_abs"]
+    assert rep["max_abs"] <= MAX_ABS_CAP, rep["max_abs"]
+    assert rep["rows_above"] <= MAX_ROWS_ABOVE * rep["rows_compared"], (rep["rows_above"], rep["rows_compared"])
 
 
 # --------------------------------------------------------------------------
@@ -470,7 +518,7 @@ def compare_logit8(q, k, v, causal, window, delta, tau, units=None, label="", gp
     return rep
 
 
-def assert_parity_logit8(rep, max_skipped=0.1):
+def assert_parity_logit8(rep, max_skipped=0.03):
     assert rep["finite"], "non-finite outputs"
     assert not rep["unexcused"], f"unexcused mask mismatches: {rep['unexcused'][:10]}"
     assert not rep["rows_unexplained"], f"rows above {MAX_ABS}: {rep['rows_unexplained'][:10]}"
@@ -510,8 +558,9 @@ def decode_flip_bound(ctx, b, h, traces, out, flag_bits=None):
                  for tr in traces)
         bound = np.zeros_like(out)
         for trace in traces:
+            wins = unit_windows(ctx, b, h, 0, trace)
             for rec in trace[:-1]:
-                alt = fragile_alternatives(ctx, b, h, 0, rec)
+                alt = fragile_alternatives(ctx, b, h, 0, rec, wins[rec["t"]])
                 if flag_bits:
                     alt = alt + flag_alternatives(ctx, b, h, 0, rec, flag_bits.get(rec["t"], 0))
                 scale = np.where(np.isneginf(rec["m_new"]), 0.0, np.exp2(rec["m_new"] - M)) / Lt
@@ -551,12 +600,15 @@ def compare_decode(q, k, v, causal, window, delta, tau, tps, heads=None, label="
             want[t] = byte
         n_sub += int(((want & 0x80) != 0).sum()) * 4
         recs = {rec["t"]: rec for tr in traces for rec in tr[:-1]}
+        wins = {}
+        for tr in traces:
+            wins.update(unit_windows(ctx, b, h, 0, tr))
         diff_t = np.nonzero(mask_g[b, h] != want)[0]
         flipped = {}
         for t in diff_t:
             x = int(mask_g[b, h, t]) ^ int(want[t])
             rec = recs.get(int(t))
-            wide = fragile_mask_bits(ctx, b, h, 0, rec) if rec is not None else 0
+            wide = fragile_mask_bits(ctx, b, h, 0, rec, wins[int(t)]) if rec is not None else 0
             if (x & 0x80) == 0 and (x & ~wide & 0x0F) == 0:
                 n_excused += 1
                 flipped[int(t)] = x & 0x0F
