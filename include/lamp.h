@@ -79,6 +79,25 @@ int lamp_attn_fwd(const void* q, const void* k, const void* v, float* out,
                   int causal, int window, float delta, float tau,
                   uint8_t* subblock_mask_out);
 
+/* lamp_attn_fwd for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same kernels and results, with the workspace in a fixed device array of
+ * 64 MiB (67108864 bytes) per device instead of the per-stream workspace.
+ * Nothing is allocated or freed by the call (no hipMalloc, hipFree or
+ * allocating library routine); the array is part of the library's code object
+ * and each device holds its copy until the process ends.  The workspace needs
+ * about 3 * B * Hkv * ceil(S/64) * 64 * D bytes (K8 and the transposed V) plus
+ * per-head scales; a call needing more than 64 MiB returns
+ * LAMP_ERR_UNSUPPORTED and launches nothing.  Every call on a device shares
+ * that device's array: calls that overlap in time on one device (different
+ * streams, or host threads) race on it and must be serialised by the caller.
+ * No timing events are recorded.  Arguments, layout, sizes and other errors
+ * as lamp_attn_fwd. */
+int lamp_attn_fwd_noalloc(const void* q, const void* k, const void* v, float* out,
+                          int B, int Hq, int Hkv, int S, int D,
+                          int causal, int window, float delta, float tau,
+                          uint8_t* subblock_mask_out);
+
 /* The forward pass under a literal reading of the 8-bit accumulation of
  * key-query products ("LampAttention", abstract): the log2-domain logit
  * c * acc (c = log2(e)/sqrt(D) times the Q and K scales) is itself rounded to

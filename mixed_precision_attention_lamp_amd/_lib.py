@@ -41,6 +41,8 @@ def load():
     vp, i32, f32, i64 = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_int64
     lib.lamp_attn_fwd.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, f32, f32, vp]
     lib.lamp_attn_fwd.restype = i32
+    lib.lamp_attn_fwd_noalloc.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, f32, f32, vp]
+    lib.lamp_attn_fwd_noalloc.restype = i32
     lib.lamp_attn_fwd_logit8.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, f32, f32, vp]
     lib.lamp_attn_fwd_logit8.restype = i32
     lib.lamp_attn_fwd_bf16.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, vp]
@@ -204,6 +206,19 @@ def lamp_attn_fwd(q, k, v, out, causal=1, window=0, delta=2.0 ** -8, tau=2.0 ** 
     _check(lib.lamp_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, Hq, Hkv, S, D,
                              int(causal), int(window), float(delta), float(tau),
                              _ptr(subblock_mask_out)))
+
+
+def lamp_attn_fwd_noalloc(q, k, v, out, causal=1, window=0, delta=2.0 ** -8, tau=2.0 ** -1,
+                          subblock_mask_out=None):
+    """lamp_attn_fwd on the library's fixed scratch array (allocates nothing);
+    arguments as lamp_attn_fwd."""
+    lib = load()
+    B, Hq, Hkv, S, D = _attn_shapes(q, k, v)
+    _check_fwd_outputs(q, k, v, out, subblock_mask_out, B, Hq, S, D)
+    _sync_stream(lib)
+    _check(lib.lamp_attn_fwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, Hq, Hkv, S, D,
+                                     int(causal), int(window), float(delta), float(tau),
+                                     _ptr(subblock_mask_out)))
 
 
 def lamp_attn_fwd_logit8(q, k, v, out, causal=1, window=0, delta=2.0 ** -8, tau=2.0 ** -1,

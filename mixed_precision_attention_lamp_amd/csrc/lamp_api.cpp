@@ -241,10 +241,48 @@ int cu_count() {
 }  // namespace lamp
 
 // plain = 1: plain bf16 FlashAttention (delta and tau unused).
+// Workspace of lamp_attn_fwd_noalloc: a fixed device array, one copy per
+// device, held until the process ends.  Host code never passes `scratch`
+// itself to a kernel or a copy (in host code the name is a host-side stand-in,
+// not a device address); it uses the address hipGetSymbolAddress returns for
+// the current device.
+constexpr size_t kScratchBytes = (size_t)64 << 20;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+namespace {
+
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices] = {nullptr};
+
+// The current device's address of `scratch`, looked up on the first call on
+// that device (with that device current).
+int scratch_address(void** out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    if (dev < 0 || dev >= kMaxDevices) return fail(LAMP_ERR_UNSUPPORTED, "device index %d", dev);
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p) {
+            (void)hipGetLastError();
+            return fail(LAMP_ERR_HIP, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+        }
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return LAMP_OK;
+}
+
+}  // namespace
+
+// use_scratch = 1: the workspace is the device's fixed scratch array (nothing
+// is allocated; sizes beyond it are rejected), and no timing events are used.
 static int attn_fwd_impl(const void* q, const void* k, const void* v, float* out, int B, int Hq, int Hkv,
                          int S, int D, int causal, int window, float delta, float tau,
                          uint8_t* subblock_mask_out, float* dump_s, uint16_t* dump_p, int plain,
-                         int logit8) {
+                         int logit8, int use_scratch = 0) {
     if (!q || !k || !v || !out) return fail(LAMP_ERR_INVALID, "q, k, v and out must be non-null");
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
         return fail(LAMP_ERR_INVALID, "q, k, v and out must be 16-byte aligned");
@@ -260,7 +298,16 @@ static int attn_fwd_impl(const void* q, const void* k, const void* v, float* out
     const lamp::Shape sh = make_shape(B, Hq, Hkv, S, D);
     const Layout L = workspace_layout(sh);
     void* ws = nullptr;
-    rc = get_workspace(L.total, &ws);
+    if (use_scratch) {
+        if (L.total > kScratchBytes)
+            return fail(LAMP_ERR_UNSUPPORTED,
+                        "lamp_attn_fwd_noalloc: this call needs %zu bytes of workspace, more than the "
+                        "fixed %zu-byte scratch array (B*Hkv*ceil(S/64)*64*D*3 bytes plus scales)",
+                        L.total, kScratchBytes);
+        rc = scratch_address(&ws);
+    } else {
+        rc = get_workspace(L.total, &ws);
+    }
     if (rc != LAMP_OK) return rc;
     uint8_t* base = static_cast<uint8_t*>(ws);
 
@@ -273,7 +320,7 @@ static int attn_fwd_impl(const void* q, const void* k, const void* v, float* out
     auto* k8 = base + L.k8;
     auto* vt = reinterpret_cast<uint16_t*>(base + L.vt);
 
-    hipEvent_t* ev = timing_slot();
+    hipEvent_t* ev = use_scratch ? nullptr : timing_slot();
     if (ev) (void)hipEventRecord(ev[0], g_stream);
     auto* q_inv = reinterpret_cast<float*>(base + L.q_inv);
     // amax partial maxima and the V transpose, then scales and K8 (the
@@ -312,6 +359,13 @@ int lamp_attn_fwd(const void* q, const void* k, const void* v, float* out, int B
                   uint8_t* subblock_mask_out) {
     return attn_fwd_impl(q, k, v, out, B, Hq, Hkv, S, D, causal, window, delta, tau, subblock_mask_out,
                          nullptr, nullptr, 0, 0);
+}
+
+int lamp_attn_fwd_noalloc(const void* q, const void* k, const void* v, float* out, int B, int Hq, int Hkv,
+                          int S, int D, int causal, int window, float delta, float tau,
+                          uint8_t* subblock_mask_out) {
+    return attn_fwd_impl(q, k, v, out, B, Hq, Hkv, S, D, causal, window, delta, tau, subblock_mask_out,
+                         nullptr, nullptr, 0, 0, 1);
 }
 
 int lamp_attn_fwd_logit8(const void* q, const void* k, const void* v, float* out, int B, int Hq, int Hkv,
