@@ -36,8 +36,17 @@ COPY_BYTES = 1 << 30       # size of the calibration copy
 # by the same counter's reading for a plain copy of COPY_BYTES (see
 # profiles/attn_qwen3_8b_hbm_traffic.md).  Valid only for the kernel source
 # whose hash is recorded; any change to it makes the figure null.
-TRAFFIC = {"kernel_hash": "83dce971bb47ae85", "workload": "qwen3-8b", "delta": 2.0 ** -8, "tau": 2.0 ** -1,
-           "bytes_per_launch": 143867356.3}
+TRAFFIC = {"kernel_hash": "abc4631f3051ed19", "workload": "qwen3-8b", "delta": 2.0 ** -8, "tau": 2.0 ** -1,
+           "bytes_per_launch": 152330761.1}
+
+
+# Vector-issue ceiling of the attention kernel on the qwen3-8b workload, from
+# the instruction counters of profiles/attn_qwen3_8b_sq_counters.md: vector
+# cycles per SIMD per launch (full-rate instructions 4 cycles, v_exp_f32 and
+# v_cvt_pk_fp8_f32 8, matrix products 4 of issue), i.e. the launch time if the
+# vector units were never idle.  Valid only for the recorded kernel source.
+VALU_CEILING = {"kernel_hash": "abc4631f3051ed19", "workload": "qwen3-8b", "delta": 2.0 ** -8,
+                "tau": 2.0 ** -1, "cycles_per_simd": 220406.0, "clock_hz": 2.4e9}
 
 
 # The same for the decode kernel on the qwen3-8b-decode workload
@@ -568,6 +577,12 @@ def main():
     prep_bytes = 2.0 * (nq + nk) + 3.0 * nk + 4.0 * nk
     t_mfma = m["f_qk8"] / PEAK_FP8 + (m["f_pv"] + m["f_qk16"]) / PEAK_BF16
     t_roof = t_mfma + quant_bytes / PEAK_HBM
+    valu_ceiling = None
+    if (VALU_CEILING["kernel_hash"] == kernel_source_hash() and VALU_CEILING["workload"] == args.workload
+            and VALU_CEILING["delta"] == args.delta and VALU_CEILING["tau"] == args.tau):
+        t_valu = VALU_CEILING["cycles_per_simd"] / VALU_CEILING["clock_hz"]
+        valu_ceiling = {"bound": "valu", "ceiling_ms": t_valu * 1e3, "frac": t_valu / (attn_ms_avg * 1e-3),
+                        "source": "instruction counters, profiles/attn_qwen3_8b_sq_counters.md"}
     traffic = None
     if (TRAFFIC is not None and TRAFFIC["kernel_hash"] == kernel_source_hash()
             and TRAFFIC["workload"] == args.workload and TRAFFIC["delta"] == args.delta
@@ -591,6 +606,7 @@ def main():
                    "delta": args.delta, "tau": args.tau},
         "roofline": {"bound": "mfma", "achieved": achieved / 1e12, "peak": blended_peak / 1e12,
                      "unit": "TFLOP/s", "frac": achieved / blended_peak, "traffic": traffic},
+        "valu_ceiling": valu_ceiling,
         "blended_roofline_frac": t_roof / (ms_per_step * 1e-3),
         "kernel_ms": {"attention": attn_ms_avg, "quantise_and_transpose": prep_ms_avg},
         "prep_hbm": {"bytes": prep_bytes, "GB/s": prep_bytes / (prep_ms_avg * 1e-3) / 1e9,

@@ -181,6 +181,20 @@ __global__ __launch_bounds__(kThreads, 1) void lamp_attn_kernel(AttnArgs a) {
     const int t_begin = tile_lo(r_first, a.window);
     const int t_end = tile_hi(r_last, a.nT, a.causal);
     const int row0 = r * kTileRows + wib * kWaveRows;   // first query row of this wave
+    // The tiles this wave's row block visits, [tv_lo, tv_hi], and those all of
+    // whose entries are visible, [tf_lo, tf_hi] (empty when lo > hi), as
+    // wave-uniform bounds: the loop's per-tile decisions are scalar compares.
+    const int r_u = __builtin_amdgcn_readfirstlane(r);
+    const bool active_u = r_u < a.nT;
+    const int tv_lo = active_u ? tile_lo(r_u, a.window) : 1;
+    const int tv_hi = active_u ? tile_hi(r_u, a.nT, a.causal) : 0;
+    int tf_lo = 1, tf_hi = 0;
+    if (active_u && r_u * kTileRows + kTileRows <= a.S) {
+        tf_hi = a.S / kTileKeys - 1;
+        if (a.causal) tf_hi = min(tf_hi, r_u - 1);
+        const int num = r_u * kTileRows + kTileRows - a.window;
+        tf_lo = a.window > 0 && num > 0 ? (num + kTileKeys - 1) / kTileKeys : 0;
+    }
 
     uint8_t* q8_lds = lds + C::kQ8Off + wave * C::kQ8Bytes;
 
@@ -331,9 +345,8 @@ __global__ __launch_bounds__(kThreads, 1) void lamp_attn_kernel(AttnArgs a) {
         for (int db = 0; db < C::kDB; ++db) acc_o[qg][db] = v4f{0.f, 0.f, 0.f, 0.f};
     }
 
-    auto work = [&](int t) __attribute__((always_inline)) {
-        return active && t >= t_begin && t <= t_end && tile_visited(r, t, a.S, a.causal, a.window);
-    };
+    auto work = [&](int t) __attribute__((always_inline)) { return t >= tv_lo && t <= tv_hi; };
+    auto full_tile = [&](int t) __attribute__((always_inline)) { return t >= tf_lo && t <= tf_hi; };
 
     // ---- matrix-core phases ---------------------------------------------------------
     // Q.K^T of tile t: s[qg][kb][i] = 8-bit accumulator of key 16kb + 4g + i, query 16qg + n16
@@ -456,8 +469,9 @@ __global__ __launch_bounds__(kThreads, 1) void lamp_attn_kernel(AttnArgs a) {
     float smin[kTest == 2 ? kQG : 1][4];    // and minima, when the first stage is off
     uint32_t vis[kQG];                  // masked tiles: bit kb*4+i = entry visible
 
-    // (2)-(3): running max and 8-bit exponentials of tile t, straight-line code.
-    auto softmax = [&](const v4f (&s)[kQG][4], u32x2 (&P)[kQG][4], int t, auto masked_tag) __attribute__((always_inline)) {
+    // (2): visibility, sub-block maxima (and minima) and the running max of
+    // tile t, straight-line code.
+    auto stats = [&](const v4f (&s)[kQG][4], int t, auto masked_tag) __attribute__((always_inline)) {
         constexpr bool kMasked = decltype(masked_tag)::value;
         constexpr float kNegInf = -__builtin_inff();
         if constexpr (kMasked) {
@@ -503,7 +517,23 @@ __global__ __launch_bounds__(kThreads, 1) void lamp_attn_kernel(AttnArgs a) {
             m_use[qg] = mn == kNegInf ? 0.0f : mn;
             m_run[qg] = mn;
         }
-        // 8-bit exponentials against the running max
+        if constexpr (kDump) {
+#pragma unroll
+            for (int qg = 0; qg < kQG; ++qg) {
+                const int qi = row0 + qg * 16 + n16;
+#pragma unroll
+                for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int kj = t * kTileKeys + kb * 16 + g * 4 + i;
+                        if (qi < a.S && kj < a.S) a.dump_s[(q_head * a.S + qi) * a.S + kj] = s[qg][kb][i];
+                    }
+            }
+        }
+    };
+    // (3): 8-bit exponentials of tile t against the running max.
+    auto exps8 = [&](const v4f (&s)[kQG][4], u32x2 (&P)[kQG][4], auto masked_tag) __attribute__((always_inline)) {
+        constexpr bool kMasked = decltype(masked_tag)::value;
 #pragma unroll
         for (int qg = 0; qg < kQG; ++qg)
 #pragma unroll
@@ -525,19 +555,10 @@ __global__ __launch_bounds__(kThreads, 1) void lamp_attn_kernel(AttnArgs a) {
                     P[qg][kb] = u32x2{e4m3x2_to_bf16x2<false>(w), e4m3x2_to_bf16x2<true>(w)};
                 }
             }
-        if constexpr (kDump) {
-#pragma unroll
-            for (int qg = 0; qg < kQG; ++qg) {
-                const int qi = row0 + qg * 16 + n16;
-#pragma unroll
-                for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const int kj = t * kTileKeys + kb * 16 + g * 4 + i;
-                        if (qi < a.S && kj < a.S) a.dump_s[(q_head * a.S + qi) * a.S + kj] = s[qg][kb][i];
-                    }
-            }
-        }
+    };
+    auto softmax = [&](const v4f (&s)[kQG][4], u32x2 (&P)[kQG][4], int t, auto masked_tag) __attribute__((always_inline)) {
+        stats(s, t, masked_tag);
+        exps8(s, P, masked_tag);
     };
 
     // (4): the look-ahead test on the accumulators of tile t; returns the wave's
@@ -553,15 +574,22 @@ __global__ __launch_bounds__(kThreads, 1) void lamp_attn_kernel(AttnArgs a) {
         uint64_t hit[4] = {0, 0, 0, 0};
         if constexpr (kTest == 1) {
             bool slow = false;
+            float thr[kQG];
 #pragma unroll
             for (int qg = 0; qg < kQG; ++qg) {
                 const float a1 = (a.x_delta + m_use[qg]) * inv_c8;
-                const float thr = __builtin_fmaxf(a1, a2);
+                thr[qg] = __builtin_fmaxf(a1, a2);
                 slow |= a1 <= -a2;
-#pragma unroll
-                for (int kb = 0; kb < 4; ++kb) hit[kb] |= wave_ballot(smax[qg][kb] >= thr);
             }
-            if (wave_ballot(slow) != 0) {
+            if (wave_ballot(slow) == 0) {
+#pragma unroll
+                for (int kb = 0; kb < 4; ++kb) {
+                    uint64_t h = 0;
+#pragma unroll
+                    for (int qg = 0; qg < kQG; ++qg) h |= wave_ballot(smax[qg][kb] >= thr[qg]);
+                    hit[kb] = h;
+                }
+            } else {
                 if constexpr (kDense) {
                     // an entry is sensitive iff max(x_delta - x, a2 - |acc|) <= 0
                     // (each difference is exact in sign); the lane's minimum
@@ -619,32 +647,39 @@ __global__ __launch_bounds__(kThreads, 1) void lamp_attn_kernel(AttnArgs a) {
     // the wave walks its set bits behind scalar branches, running the bf16
     // logits of each flagged sub-block on the matrix cores and rounding its
     // exponentials to bf16 into the compile-time-indexed register tile P.
-    auto recompute = [&](u32x2 (&P)[kQG][4], uint32_t flags, auto masked_tag, int t) __attribute__((always_inline)) {
-        constexpr bool kMasked = decltype(masked_tag)::value;
+    // The bf16 logits of flagged sub-block c (the matrix-core half of (5))
+    auto recompute_mfma = [&](v4f (&acc16)[kQG], int c, int t) __attribute__((always_inline)) {
         const uint8_t* k16l = lds + C::kK16Off + (C::kPP ? (t & 1) * C::kK16Bytes : 0);
+#pragma unroll
+        for (int ch = 0; ch < C::kDC; ++ch) {
+            const v8bf ka = *reinterpret_cast<const v8bf*>(k16l + lds_off<C::kK16Row>(c * 16 + n16, ch * 4 + g));
+#pragma unroll
+            for (int qg = 0; qg < kQG; ++qg)
+                acc16[qg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                    ka, qb[ch][qg], ch == 0 ? v4f{0.f, 0.f, 0.f, 0.f} : acc16[qg], 0, 0, 0);
+        }
+    };
+    // ... and their exponentials rounded to bf16, spliced into P
+    auto recompute_exp = [&](u32x2 (&P)[kQG][4], const v4f (&acc16)[kQG], int c, auto masked_tag) __attribute__((always_inline)) {
+        constexpr bool kMasked = decltype(masked_tag)::value;
+#pragma unroll
+        for (int qg = 0; qg < kQG; ++qg) {
+            float e[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                e[i] = fast_exp2(__builtin_fmaf(acc16[qg][i], c16, -m_use[qg]));
+                if constexpr (kMasked) e[i] = ((vis[qg] >> (c * 4 + i)) & 1u) ? e[i] : 0.0f;
+            }
+            P[qg][c] = u32x2{f32x2_to_bf16x2(e[0], e[1]), f32x2_to_bf16x2(e[2], e[3])};
+        }
+    };
+    auto recompute = [&](u32x2 (&P)[kQG][4], uint32_t flags, auto masked_tag, int t) __attribute__((always_inline)) {
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
             if (!((flags >> c) & 1u)) continue;
             v4f acc16[kQG];
-#pragma unroll
-            for (int ch = 0; ch < C::kDC; ++ch) {
-                const v8bf ka = *reinterpret_cast<const v8bf*>(k16l + lds_off<C::kK16Row>(c * 16 + n16, ch * 4 + g));
-#pragma unroll
-                for (int qg = 0; qg < kQG; ++qg) {
-                    acc16[qg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                        ka, qb[ch][qg], ch == 0 ? v4f{0.f, 0.f, 0.f, 0.f} : acc16[qg], 0, 0, 0);
-                }
-            }
-#pragma unroll
-            for (int qg = 0; qg < kQG; ++qg) {
-                float e[4];
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    e[i] = fast_exp2(__builtin_fmaf(acc16[qg][i], c16, -m_use[qg]));
-                    if constexpr (kMasked) e[i] = ((vis[qg] >> (c * 4 + i)) & 1u) ? e[i] : 0.0f;
-                }
-                P[qg][c] = u32x2{f32x2_to_bf16x2(e[0], e[1]), f32x2_to_bf16x2(e[2], e[3])};
-            }
+            recompute_mfma(acc16, c, t);
+            recompute_exp(P, acc16, c, masked_tag);
         }
     };
 
@@ -697,6 +732,8 @@ __global__ __launch_bounds__(kThreads, 1) void lamp_attn_kernel(AttnArgs a) {
         // never touch a slot read in it.  In the plain bf16 mode the Q.K^T tiles
         // are K16 tiles, staged like K8, and there is no test or recompute.
         const int grp = wave >> 2;
+        constexpr auto kFull = std::integral_constant<bool, false>{};
+        constexpr auto kPart = std::integral_constant<bool, true>{};
         load_k8(t_begin);
         store_k8(t_begin);
         load_k8(t_begin + 1);
@@ -712,7 +749,7 @@ __global__ __launch_bounds__(kThreads, 1) void lamp_attn_kernel(AttnArgs a) {
         lds_barrier();
         for (int t = t_begin; t <= t_end; ++t) {
             const bool w_cur = work(t), w_next = work(t + 1);
-            const bool full = tile_full(r, t, a.S, a.causal, a.window);
+            const bool full = full_tile(t);
             // ---- V(t)
             load_k8(t + 2);
             if constexpr (!kPlain) load_k16(t + 1);
@@ -720,12 +757,10 @@ __global__ __launch_bounds__(kThreads, 1) void lamp_attn_kernel(AttnArgs a) {
             uint32_t flags = 0;
             if (w_cur) {
                 round_logits(S);
-                if (full) softmax(S, P, t, std::integral_constant<bool, false>{});
-                else softmax(S, P, t, std::integral_constant<bool, true>{});
+                if (full) softmax(S, P, t, kFull);
+                else softmax(S, P, t, kPart);
                 rescale();
-                if constexpr (!kPlain)
-                    flags = full ? test(S, std::integral_constant<bool, false>{})
-                                 : test(S, std::integral_constant<bool, true>{});
+                if constexpr (!kPlain) flags = full ? test(S, kFull) : test(S, kPart);
             }
             if (lane == 0) flag_lds[wave] = flags;
             lds_barrier();
@@ -733,7 +768,7 @@ __global__ __launch_bounds__(kThreads, 1) void lamp_attn_kernel(AttnArgs a) {
             // goes first and the vector work of the other wave fills around it
             __builtin_amdgcn_s_setprio(1);
             flags = 0;
-    #pragma unroll
+#pragma unroll
             for (int w = 0; w < C::kWavesPerBlock; ++w) flags |= flag_lds[blk * C::kWavesPerBlock + w];
             flags = __builtin_amdgcn_readfirstlane(flags);
             // the loads of V(t) have arrived; storing them first frees their registers
@@ -744,8 +779,8 @@ __global__ __launch_bounds__(kThreads, 1) void lamp_attn_kernel(AttnArgs a) {
                 if constexpr (kPlain) {
                     flags = 0xFu;   // every sub-block in 16-bit
                 } else if (flags != 0) {
-                    if (full) recompute(P, flags, std::integral_constant<bool, false>{}, t);
-                    else recompute(P, flags, std::integral_constant<bool, true>{}, t);
+                    if (full) recompute(P, flags, kFull, t);
+                    else recompute(P, flags, kPart, t);
                 }
                 dump_p(P, t);
                 pv(P, t);
@@ -776,7 +811,7 @@ __global__ __launch_bounds__(kThreads, 1) void lamp_attn_kernel(AttnArgs a) {
             // barrier below orders these stores before the recompute of tile t
             if (t > t_begin) store_k16(0);
             const bool w_prev = work(t - 1), w_cur = work(t), w_next = work(t + 1);
-            const bool full = tile_full(r, t, a.S, a.causal, a.window);
+            const bool full = full_tile(t);
             // P.V of tile t-1 is issued first (it reads P before the exponentials
             // of tile t overwrite it) and runs on the matrix cores under the
             // vector work of tile t
