@@ -18,17 +18,21 @@
 //   7. a mask byte per tile records the flags ("16-bit sub-blocks per tile",
 //      tables 1-6).
 //
-// Schedule: the loop over KV tiles is software-pipelined.  In the iteration of
-// tile t a wave first issues the P.V products of tile t-1, which run on the
-// matrix cores under the vector work of tile t (max, exponentials, 8-bit
-// rounding); after the sub-block test and the 16-bit recompute of tile t it
-// issues the Q.K^T products of tile t+1, which run under the rescale, the LDS
-// stores and the barrier.  Tiles are staged through registers into unpadded LDS
-// layouts whose 16-byte chunks are XOR-swizzled by row (conflict-free operand
-// reads); K8 runs two tiles ahead of the vector work (two LDS slots), K16 one
-// and V^T zero (one slot each, ordered by the two barriers of a tile).  Each
-// wave quantises its Q rows into LDS in the prologue (the arithmetic of the
-// quantisation pass) and keeps its Q16 operand in registers.
+// Schedule (D = 64, 128): two waves per SIMD run the same sequence of vector
+// phases (max, exponentials, rescale, test) and matrix phases (recompute, P.V,
+// the next tile's Q.K^T) one phase apart, so that each SIMD's matrix cores
+// work under the other wave's vector work; the K8, K16 and V^T tiles are
+// copied from global memory straight into LDS (buffer loads with an LDS
+// destination, no registers) two tiles ahead, into three slots per array.
+// D = 256 (no room for a second set of slots): every wave runs one
+// software-pipelined loop; the P.V products of tile t-1 run under the vector
+// work of tile t, and the Q.K^T products of tile t+1 under the rescale,
+// the LDS stores and the barrier; tiles are staged through registers (K8 two
+// tiles ahead in two slots, K16 and V^T in one slot each).  LDS layouts are
+// unpadded, their 16-byte chunks XOR-swizzled by row (conflict-free operand
+// reads).  Each wave quantises its Q rows into LDS in the prologue (the
+// arithmetic of the quantisation pass) and keeps its Q16 operand (and, for
+// D <= 128, its Q8 operand) in registers.
 //
 // Work decomposition: a workgroup of eight waves shares staged K/V tiles.  A
 // wave owns 32 query rows (16 for D = 256), so that the fp32 output
@@ -98,15 +102,18 @@ struct Cfg {
     static constexpr int kK16Bytes = kTileKeys * kK16Row;
     static constexpr int kVtBytes = D * kVtRow;
     static constexpr int kQ8Bytes = kWaveRows * kK8Row;        // per wave
-    // ping-pong schedule (two K16 and V^T slots) where the slots fit in LDS
+    // ping-pong schedule where its slots fit in LDS: three slots of each
+    // staged array, filled by direct global-to-LDS copies; otherwise two Q.K^T
+    // slots and one K16 and V^T slot, staged through registers
     static constexpr bool kPP = D <= 128;
-    static constexpr int kSlots16 = kPP ? 2 : 1;
+    static constexpr int kSlots16 = kPP ? 3 : 1;
+    static constexpr int kSlotsQK = kPP ? 3 : 2;
     // The tiles Q.K^T reads: K8, or K16 in the plain bf16 mode (which then
     // needs no separate K16 slots and no Q8 rows).
     static constexpr int kQKRow = kPlain ? kK16Row : kK8Row;
     static constexpr int kQKBytes = kTileKeys * kQKRow;
-    static constexpr int kK8Off = 0;                            // two slots
-    static constexpr int kK16Off = 2 * kQKBytes;
+    static constexpr int kK8Off = 0;
+    static constexpr int kK16Off = kSlotsQK * kQKBytes;
     static constexpr int kVtOff = kK16Off + (kPlain ? 0 : kSlots16 * kK16Bytes);
     static constexpr int kQ8Off = kVtOff + kSlots16 * kVtBytes;
     static constexpr int kLdsBytes = kQ8Off + (kPlain ? 0 : kWaves * kQ8Bytes);
@@ -274,6 +281,73 @@ __global__ __launch_bounds__(kThreads, 1) void lamp_attn_kernel(AttnArgs a) {
 #pragma unroll
         for (int i = 0; i < kVtCh; ++i) *reinterpret_cast<u32x4*>(base + (tid + i * kThreads) * 16) = st_vt[i];
     };
+    // Ping-pong schedule: direct global-to-LDS copies, no registers.  Copy i
+    // of wave w moves chunks i*kThreads + 64w .. +63 of a tile, lane l the
+    // chunk i*kThreads + 64w + l: the chunk-to-thread map of the staged loads.
+    // Each array of the (batch, kv head) is one buffer: a lane's byte offset
+    // (row and swizzled chunk) is fixed, the tile's is a scalar, and reads past
+    // the buffer's end (keys past the last) return zeros.  A copy's LDS
+    // destination is one wave-uniform address; lane l's 16 bytes land 16 l
+    // bytes above it.
+    const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+    constexpr int kBufWord3 = 0x00020000;    // raw 32-bit-format buffer
+    const __amdgpu_buffer_rsrc_t rs_qk = __builtin_amdgcn_make_buffer_rsrc(
+        kPlain ? (void*)k16_head : (void*)(a.k8 + kv_head * a.S_pad * D), (short)0,
+        kPlain ? a.S * C::kK16Row : a.S_pad * D, kBufWord3);
+    const __amdgpu_buffer_rsrc_t rs_k16 =
+        __builtin_amdgcn_make_buffer_rsrc((void*)k16_head, (short)0, a.S * C::kK16Row, kBufWord3);
+    const __amdgpu_buffer_rsrc_t rs_vt = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(a.vt + kv_head * a.nT * (size_t)D * kTileKeys), (short)0, a.nT * C::kVtBytes, kBufWord3);
+    auto chunk_off = [&](int i, auto row_bytes) __attribute__((always_inline)) -> unsigned {
+        constexpr int kRow = decltype(row_bytes)::value;
+        const unsigned p = (tid + i * kThreads) * 16;
+        const unsigned row = p / kRow, slot16 = (p % kRow) >> 4;
+        return row * kRow + ((slot16 ^ swz<kRow / 16>(row)) << 4);
+    };
+    auto dma = [&](__amdgpu_buffer_rsrc_t rs, unsigned voff, int soff, uint8_t* dst) __attribute__((always_inline)) {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)dst, 16, voff, soff, 0, 0);
+    };
+    auto dma_qk_i = [&](int t, int slot, int i) __attribute__((always_inline)) {
+        const int first = i * kThreads + wave_u * 64;
+        if (first * 16 >= C::kQKBytes) return;    // D = 64: half the waves
+        dma(rs_qk, chunk_off(i, std::integral_constant<int, C::kQKRow>{}), t * C::kQKBytes,
+            lds + C::kK8Off + slot * C::kQKBytes + first * 16);
+    };
+    auto dma_k16_i = [&](int t, int slot, int i) __attribute__((always_inline)) {
+        dma(rs_k16, chunk_off(i, std::integral_constant<int, C::kK16Row>{}), t * C::kK16Bytes,
+            lds + C::kK16Off + slot * C::kK16Bytes + (i * kThreads + wave_u * 64) * 16);
+    };
+    auto dma_vt_i = [&](int t, int slot, int i) __attribute__((always_inline)) {
+        dma(rs_vt, chunk_off(i, std::integral_constant<int, C::kVtRow>{}), t * C::kVtBytes,
+            lds + C::kVtOff + slot * C::kVtBytes + (i * kThreads + wave_u * 64) * 16);
+    };
+    auto dma_qk = [&](int t, int slot) __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < kK8ChMin; ++i) dma_qk_i(t, slot, i);
+    };
+    auto dma_k16 = [&](int t, int slot) __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < kK16Ch; ++i) dma_k16_i(t, slot, i);
+    };
+    auto dma_vt = [&](int t, int slot) __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < kVtCh; ++i) dma_vt_i(t, slot, i);
+    };
+    // The copies one matrix phase issues, one per call: K16 and V^T of tile
+    // t16 into slot s16, then K8 of tile t8 into slot s8.  Tiles past the end
+    // copy the last one again: its destination slot is not read any more, and
+    // the copies of a phase stay a fixed, branch-free sequence.
+    constexpr int kDmaK16 = kPlain ? 0 : kK16Ch;
+    constexpr int kDmaSteps = kDmaK16 + kVtCh + kK8ChMin;
+    auto dma_step = [&](int k, int t16, int s16, int t8, int s8) __attribute__((always_inline)) {
+        if (k < kDmaK16) {
+            if constexpr (!kPlain) dma_k16_i(min(t16, t_end), s16, k);
+        } else if (k < kDmaK16 + kVtCh) {
+            dma_vt_i(min(t16, t_end), s16, k - kDmaK16);
+        } else if (k < kDmaSteps) {
+            dma_qk_i(min(t8, t_end), s8, k - kDmaK16 - kVtCh);
+        }
+    };
 
     // ---- prologue: this wave's Q16 operand into registers, Q8 rows into its LDS ----
     float m_run[kQG], c8 = 0.0f, inv_c8 = 0.0f, a2 = 0.0f, c8_log = 0.0f;
@@ -345,15 +419,22 @@ __global__ __launch_bounds__(kThreads, 1) void lamp_attn_kernel(AttnArgs a) {
         for (int db = 0; db < C::kDB; ++db) acc_o[qg][db] = v4f{0.f, 0.f, 0.f, 0.f};
     }
 
+    // the ping-pong schedule keeps this wave's 8-bit Q operand in registers
+    constexpr bool kQ8Reg = C::kPP && !kPlain && C::kKS == 1;
+    v8i q8r[kQG];
+    if constexpr (kQ8Reg) {
+#pragma unroll
+        for (int qg = 0; qg < kQG; ++qg) q8r[qg] = fp8_operand<D>(q8_lds, qg * 16 + n16, 0, g);
+    }
     auto work = [&](int t) __attribute__((always_inline)) { return t >= tv_lo && t <= tv_hi; };
     auto full_tile = [&](int t) __attribute__((always_inline)) { return t >= tf_lo && t <= tf_hi; };
 
     // ---- matrix-core phases ---------------------------------------------------------
     // Q.K^T of tile t: s[qg][kb][i] = 8-bit accumulator of key 16kb + 4g + i, query 16qg + n16
-    auto qk = [&](v4f (&s)[kQG][4], int t) __attribute__((always_inline)) {
+    auto qk = [&](v4f (&s)[kQG][4], int slot) __attribute__((always_inline)) {
         if constexpr (kPlain) {
             // bf16 logits of all four sub-blocks (the recompute's products)
-            const uint8_t* kl = lds + C::kK8Off + (t & 1) * C::kQKBytes;
+            const uint8_t* kl = lds + C::kK8Off + slot * C::kQKBytes;
 #pragma unroll
             for (int c = 0; c < 4; ++c)
 #pragma unroll
@@ -366,12 +447,13 @@ __global__ __launch_bounds__(kThreads, 1) void lamp_attn_kernel(AttnArgs a) {
                 }
             return;
         }
-        const uint8_t* k8l = lds + C::kK8Off + (t & 1) * C::kQKBytes;
+        const uint8_t* k8l = lds + C::kK8Off + slot * C::kQKBytes;
 #pragma unroll
         for (int st = 0; st < C::kKS; ++st) {
             v8i qf[kQG];
 #pragma unroll
-            for (int qg = 0; qg < kQG; ++qg) qf[qg] = fp8_operand<D>(q8_lds, qg * 16 + n16, st, g);
+            for (int qg = 0; qg < kQG; ++qg)
+                qf[qg] = kQ8Reg ? q8r[qg] : fp8_operand<D>(q8_lds, qg * 16 + n16, st, g);
 #pragma unroll
             for (int kb = 0; kb < 4; ++kb) {
                 const v8i ka = fp8_operand<D>(k8l, kb * 16 + n16, st, g);
@@ -389,9 +471,11 @@ __global__ __launch_bounds__(kThreads, 1) void lamp_attn_kernel(AttnArgs a) {
     // half's operands are read up front, and each read of the second half
     // reuses the registers of the first-half operand whose products were just
     // issued; the schedule is pinned (the scheduler would sink every read next
-    // to its use).
-    auto pv = [&](const u32x2 (&P)[kQG][4], int t) __attribute__((always_inline)) {
-        const uint8_t* vtl = lds + C::kVtOff + (C::kPP ? (t & 1) * C::kVtBytes : 0);
+    // to its use).  The phase's copies into LDS (copy(k), k = 0, 1, ...) are
+    // issued one after every second output block, between matrix products,
+    // so that the memory unit takes them one at a time.
+    auto pv = [&](const u32x2 (&P)[kQG][4], int slot, auto copy) __attribute__((always_inline)) {
+        const uint8_t* vtl = lds + C::kVtOff + slot * C::kVtBytes;
         if constexpr (C::kPP) {
             v8bf va[C::kDB];
 #pragma unroll
@@ -415,6 +499,10 @@ __global__ __launch_bounds__(kThreads, 1) void lamp_attn_kernel(AttnArgs a) {
                     if (h == 0) {
                         va[db] = *reinterpret_cast<const v8bf*>(vtl + lds_off<C::kVtRow>(db * 16 + n16, 4 + g));
                         __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                    }
+                    if ((db & 1) && h * (C::kDB / 2) + db / 2 < kDmaSteps) {
+                        copy(h * (C::kDB / 2) + db / 2);
+                        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
                     }
                 }
 #pragma unroll
@@ -648,8 +736,8 @@ __global__ __launch_bounds__(kThreads, 1) void lamp_attn_kernel(AttnArgs a) {
     // logits of each flagged sub-block on the matrix cores and rounding its
     // exponentials to bf16 into the compile-time-indexed register tile P.
     // The bf16 logits of flagged sub-block c (the matrix-core half of (5))
-    auto recompute_mfma = [&](v4f (&acc16)[kQG], int c, int t) __attribute__((always_inline)) {
-        const uint8_t* k16l = lds + C::kK16Off + (C::kPP ? (t & 1) * C::kK16Bytes : 0);
+    auto recompute_mfma = [&](v4f (&acc16)[kQG], int c, int slot) __attribute__((always_inline)) {
+        const uint8_t* k16l = lds + C::kK16Off + slot * C::kK16Bytes;
 #pragma unroll
         for (int ch = 0; ch < C::kDC; ++ch) {
             const v8bf ka = *reinterpret_cast<const v8bf*>(k16l + lds_off<C::kK16Row>(c * 16 + n16, ch * 4 + g));
@@ -673,12 +761,12 @@ __global__ __launch_bounds__(kThreads, 1) void lamp_attn_kernel(AttnArgs a) {
             P[qg][c] = u32x2{f32x2_to_bf16x2(e[0], e[1]), f32x2_to_bf16x2(e[2], e[3])};
         }
     };
-    auto recompute = [&](u32x2 (&P)[kQG][4], uint32_t flags, auto masked_tag, int t) __attribute__((always_inline)) {
+    auto recompute = [&](u32x2 (&P)[kQG][4], uint32_t flags, auto masked_tag, int slot) __attribute__((always_inline)) {
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
             if (!((flags >> c) & 1u)) continue;
             v4f acc16[kQG];
-            recompute_mfma(acc16, c, t);
+            recompute_mfma(acc16, c, slot);
             recompute_exp(P, acc16, c, masked_tag);
         }
     };
@@ -723,37 +811,49 @@ __global__ __launch_bounds__(kThreads, 1) void lamp_attn_kernel(AttnArgs a) {
         // wave is in a vector phase while the other is in a matrix phase:
         //   V(t): running max, exponentials, rescale and test of tile t, flags
         //         out;
-        //   M(t): 16-bit recompute and P.V of tile t, Q.K^T of tile t+1,
-        //         and the LDS stores of K8(t+2), K16(t+1) and V^T(t+1) (loaded in
-        //         V(t)).
-        // A workgroup barrier ends every phase.  The two groups read the K16 and
-        // V^T tiles of t and the K8 tile of t+1 in two consecutive phases, M(t) of
-        // each; two slots of each array then suffice, and the stores of a phase
-        // never touch a slot read in it.  In the plain bf16 mode the Q.K^T tiles
-        // are K16 tiles, staged like K8, and there is no test or recompute.
+        //   M(t): 16-bit recompute and P.V of tile t, Q.K^T of tile t+1, and
+        //         the copies of K16(t+2), V^T(t+2) and K8(t+3) into LDS, issued
+        //         between the P.V products.
+        // A workgroup barrier ends every phase.  Tile u lives in slot u % 3 of
+        // each array.  Both groups read the K16 and V^T tiles of t and the K8
+        // tile of t+1 in M(t), two consecutive phases; the copies a group issues
+        // in M(t) overwrite tiles t-1 (K16, V^T) and t (K8), which both groups
+        // finished reading in M(t-1), and they are complete (each wave waits
+        // for its own before issuing the next ones, in M(t+1)) before the first
+        // reader, the first group's M(t+2).  In the plain bf16 mode
+        // the Q.K^T tiles are K16 tiles, staged like K8, and there is no test or
+        // recompute.
         const int grp = wave >> 2;
         constexpr auto kFull = std::integral_constant<bool, false>{};
         constexpr auto kPart = std::integral_constant<bool, true>{};
-        load_k8(t_begin);
-        store_k8(t_begin);
-        load_k8(t_begin + 1);
-        if constexpr (!kPlain) load_k16(t_begin);
-        load_vt(t_begin);
+        auto wait_copies = []() __attribute__((always_inline)) {
+            __asm__ __volatile__("s_waitcnt vmcnt(0)" ::: "memory");
+        };
+        int s_cur = t_begin % 3;                 // slot of tile t
+        const int s_b1 = s_cur == 2 ? 0 : s_cur + 1;
+        const int s_b2 = s_b1 == 2 ? 0 : s_b1 + 1;
+        // the tiles the first two matrix phases read, and K8 of the third
+        dma_qk(t_begin, s_cur);
+        if (t_begin + 1 <= t_end) dma_qk(t_begin + 1, s_b1);
+        if (t_begin + 2 <= t_end) dma_qk(t_begin + 2, s_b2);
+        if constexpr (!kPlain) dma_k16(t_begin, s_cur);
+        dma_vt(t_begin, s_cur);
+        if (t_begin + 1 <= t_end) {
+            if constexpr (!kPlain) dma_k16(t_begin + 1, s_b1);
+            dma_vt(t_begin + 1, s_b1);
+        }
+        wait_copies();
         lds_barrier();
         if (grp == 1) lds_barrier();
-        // M(t_begin - 1): the first Q.K^T and the stores for tile t_begin
-        if (work(t_begin)) qk(S, t_begin);
-        store_k8(t_begin + 1);
-        if constexpr (!kPlain) store_k16(t_begin & 1);
-        store_vt(t_begin & 1);
+        // M(t_begin - 1): the first Q.K^T
+        if (work(t_begin)) qk(S, s_cur);
         lds_barrier();
         for (int t = t_begin; t <= t_end; ++t) {
             const bool w_cur = work(t), w_next = work(t + 1);
             const bool full = full_tile(t);
+            const int s_n1 = s_cur == 2 ? 0 : s_cur + 1;   // slot of t+1
+            const int s_n2 = s_n1 == 2 ? 0 : s_n1 + 1;     // slot of t+2 (and t-1)
             // ---- V(t)
-            load_k8(t + 2);
-            if constexpr (!kPlain) load_k16(t + 1);
-            load_vt(t + 1);
             uint32_t flags = 0;
             if (w_cur) {
                 round_logits(S);
@@ -771,25 +871,26 @@ __global__ __launch_bounds__(kThreads, 1) void lamp_attn_kernel(AttnArgs a) {
 #pragma unroll
             for (int w = 0; w < C::kWavesPerBlock; ++w) flags |= flag_lds[blk * C::kWavesPerBlock + w];
             flags = __builtin_amdgcn_readfirstlane(flags);
-            // the loads of V(t) have arrived; storing them first frees their registers
-            store_k8(t + 2);
-            if constexpr (!kPlain) store_k16((t + 1) & 1);
-            store_vt((t + 1) & 1);
             if (w_cur) {
                 if constexpr (kPlain) {
                     flags = 0xFu;   // every sub-block in 16-bit
                 } else if (flags != 0) {
-                    if (full) recompute(P, flags, kFull, t);
-                    else recompute(P, flags, kPart, t);
+                    if (full) recompute(P, flags, kFull, s_cur);
+                    else recompute(P, flags, kPart, s_cur);
                 }
                 dump_p(P, t);
-                pv(P, t);
-                if (a.mask && wib == 0 && lane == 0)
-                    a.mask[(q_head * a.nT + r) * a.nT + t] = (uint8_t)(0x80u | flags);
             }
-            if (w_next) qk(S, t + 1);
+            if (w_cur) pv(P, s_cur, [](int) {});
+            if (w_next) qk(S, s_n1);
+            // copies for later tiles, after this wave's previous ones have landed
+            wait_copies();
+#pragma unroll
+            for (int k = 0; k < kDmaSteps; ++k) dma_step(k, t + 2, s_n2, t + 3, s_cur);
+            if (w_cur && a.mask && wib == 0 && lane == 0)
+                a.mask[(q_head * a.nT + r) * a.nT + t] = (uint8_t)(0x80u | flags);
             __builtin_amdgcn_s_setprio(0);
             lds_barrier();
+            s_cur = s_n1;
         }
         if (grp == 0) lds_barrier();
     } else {
@@ -801,7 +902,7 @@ __global__ __launch_bounds__(kThreads, 1) void lamp_attn_kernel(AttnArgs a) {
         load_k8(t_begin + 1);
         store_k8(t_begin + 1);
         lds_barrier();
-        if (work(t_begin)) qk(S, t_begin);
+        if (work(t_begin)) qk(S, t_begin & 1);
         lds_barrier();   // every wave has read K8(t_begin) before its slot is refilled
 
         // ---- the pipelined loop ---------------------------------------------------------
@@ -815,7 +916,7 @@ __global__ __launch_bounds__(kThreads, 1) void lamp_attn_kernel(AttnArgs a) {
             // P.V of tile t-1 is issued first (it reads P before the exponentials
             // of tile t overwrite it) and runs on the matrix cores under the
             // vector work of tile t
-            if (w_prev) pv(P, t - 1);
+            if (w_prev) pv(P, 0, [](int) {});
             if (w_cur) {
                 round_logits(S);
                 if (full) softmax(S, P, t, std::integral_constant<bool, false>{});
@@ -838,11 +939,11 @@ __global__ __launch_bounds__(kThreads, 1) void lamp_attn_kernel(AttnArgs a) {
             for (int w = 0; w < C::kWavesPerBlock; ++w) flags |= flag_lds[blk * C::kWavesPerBlock + w];
             flags = __builtin_amdgcn_readfirstlane(flags);
             if (w_cur && flags != 0) {
-                if (full) recompute(P, flags, std::integral_constant<bool, false>{}, t);
-                else recompute(P, flags, std::integral_constant<bool, true>{}, t);
+                if (full) recompute(P, flags, std::integral_constant<bool, false>{}, 0);
+                else recompute(P, flags, std::integral_constant<bool, true>{}, 0);
             }
             // Q.K^T of tile t+1 runs on the matrix cores under what follows
-            if (w_next) qk(S, t + 1);
+            if (w_next) qk(S, (t + 1) & 1);
             if (w_cur) {
                 dump_p(P, t);
                 rescale();
@@ -858,7 +959,7 @@ __global__ __launch_bounds__(kThreads, 1) void lamp_attn_kernel(AttnArgs a) {
             lds_barrier();
         }
         // P.V of the last tile
-        if (work(t_end)) pv(P, t_end);
+        if (work(t_end)) pv(P, 0, [](int) {});
     }
 
     // ---- epilogue: out = O / l ------------------------------------------------------

@@ -112,19 +112,27 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(
     const int out_len = rows_out * D;
     const int begin = chunk * kChunk;
     const int end = min(begin + kChunk, out_len);
-    for (int i = begin + threadIdx.x * 8; i < end; i += kThreads * 8) {
-        u32x2 o = {0u, 0u};
-        if (i < in_len) {
-            const u32x4 w = *reinterpret_cast<const u32x4*>(src + i);
-            float x[8];
+    // every load of the block's chunk is issued before the first conversion
+    constexpr int kPer = kChunk / (kThreads * 8);
+    u32x4 w[kPer];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                x[2 * j] = bf16_bits_to_float(w[j] & 0xFFFFu) * inv;
-                x[2 * j + 1] = bf16_bits_to_float(w[j] >> 16) * inv;
-            }
-            o[0] = cvt_pk_e4m3<true>(x[2], x[3], cvt_pk_e4m3<false>(x[0], x[1], 0u));
-            o[1] = cvt_pk_e4m3<true>(x[6], x[7], cvt_pk_e4m3<false>(x[4], x[5], 0u));
+    for (int j = 0; j < kPer; ++j) {
+        const int i = begin + (j * kThreads + (int)threadIdx.x) * 8;
+        w[j] = i < in_len && i < end ? *reinterpret_cast<const u32x4*>(src + i) : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+        const int i = begin + (j * kThreads + (int)threadIdx.x) * 8;
+        if (i >= end) break;
+        float x[8];
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+            x[2 * h] = bf16_bits_to_float(w[j][h] & 0xFFFFu) * inv;
+            x[2 * h + 1] = bf16_bits_to_float(w[j][h] >> 16) * inv;
         }
+        u32x2 o;
+        o[0] = cvt_pk_e4m3<true>(x[2], x[3], cvt_pk_e4m3<false>(x[0], x[1], 0u));
+        o[1] = cvt_pk_e4m3<true>(x[6], x[7], cvt_pk_e4m3<false>(x[4], x[5], 0u));
         *reinterpret_cast<u32x2*>(dst + i) = o;
     }
 }
