@@ -36,8 +36,8 @@ COPY_BYTES = 1 << 30       # size of the calibration copy
 # by the same counter's reading for a plain copy of COPY_BYTES (see
 # profiles/attn_qwen3_8b_hbm_traffic.md).  Valid only for the kernel source
 # whose hash is recorded; any change to it makes the figure null.
-TRAFFIC = {"kernel_hash": "abc4631f3051ed19", "workload": "qwen3-8b", "delta": 2.0 ** -8, "tau": 2.0 ** -1,
-           "bytes_per_launch": 152330761.1}
+TRAFFIC = {"kernel_hash": "cf40d647f84067a2", "workload": "qwen3-8b", "delta": 2.0 ** -8, "tau": 2.0 ** -1,
+           "bytes_per_launch": 137899189.2}
 
 
 # Vector-issue ceiling of the attention kernel on the qwen3-8b workload, from
@@ -45,8 +45,8 @@ TRAFFIC = {"kernel_hash": "abc4631f3051ed19", "workload": "qwen3-8b", "delta": 2
 # cycles per SIMD per launch (full-rate instructions 4 cycles, v_exp_f32 and
 # v_cvt_pk_fp8_f32 8, matrix products 4 of issue), i.e. the launch time if the
 # vector units were never idle.  Valid only for the recorded kernel source.
-VALU_CEILING = {"kernel_hash": "abc4631f3051ed19", "workload": "qwen3-8b", "delta": 2.0 ** -8,
-                "tau": 2.0 ** -1, "cycles_per_simd": 220406.0, "clock_hz": 2.4e9}
+VALU_CEILING = {"kernel_hash": "cf40d647f84067a2", "workload": "qwen3-8b", "delta": 2.0 ** -8,
+                "tau": 2.0 ** -1, "cycles_per_simd": 211896.3, "clock_hz": 2.4e9}
 
 
 # The same for the decode kernel on the qwen3-8b-decode workload
