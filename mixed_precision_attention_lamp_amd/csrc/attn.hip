@@ -811,9 +811,9 @@ __global__ __launch_bounds__(kThreads, 1) void lamp_attn_kernel(AttnArgs a) {
         // wave is in a vector phase while the other is in a matrix phase:
         //   V(t): running max, exponentials, rescale and test of tile t, flags
         //         out;
-        //   M(t): 16-bit recompute and P.V of tile t, Q.K^T of tile t+1, and
-        //         the copies of K16(t+2), V^T(t+2) and K8(t+3) into LDS, issued
-        //         between the P.V products.
+        //   M(t): Q.K^T of tile t+1 (the logits of t are dead), 16-bit
+        //         recompute and P.V of tile t, and the copies of K16(t+2),
+        //         V^T(t+2) and K8(t+3) into LDS.
         // A workgroup barrier ends every phase.  Tile u lives in slot u % 3 of
         // each array.  Both groups read the K16 and V^T tiles of t and the K8
         // tile of t+1 in M(t), two consecutive phases; the copies a group issues
@@ -871,6 +871,7 @@ __global__ __launch_bounds__(kThreads, 1) void lamp_attn_kernel(AttnArgs a) {
 #pragma unroll
             for (int w = 0; w < C::kWavesPerBlock; ++w) flags |= flag_lds[blk * C::kWavesPerBlock + w];
             flags = __builtin_amdgcn_readfirstlane(flags);
+            if (w_next) qk(S, s_n1);
             if (w_cur) {
                 if constexpr (kPlain) {
                     flags = 0xFu;   // every sub-block in 16-bit
@@ -881,7 +882,6 @@ __global__ __launch_bounds__(kThreads, 1) void lamp_attn_kernel(AttnArgs a) {
                 dump_p(P, t);
             }
             if (w_cur) pv(P, s_cur, [](int) {});
-            if (w_next) qk(S, s_n1);
             // copies for later tiles, after this wave's previous ones have landed
             wait_copies();
 #pragma unroll
