@@ -101,22 +101,20 @@ struct Cfg {
     static constexpr int kK8Bytes = kTileKeys * kK8Row;
     static constexpr int kK16Bytes = kTileKeys * kK16Row;
     static constexpr int kVtBytes = D * kVtRow;
-    static constexpr int kQ8Bytes = kWaveRows * kK8Row;        // per wave
-    // ping-pong schedule where its slots fit in LDS: three slots of each
-    // staged array, filled by direct global-to-LDS copies; otherwise two Q.K^T
-    // slots and one K16 and V^T slot, staged through registers
+    // Every staged array is filled by direct global-to-LDS copies: three
+    // slots each under the ping-pong schedule (D <= 128), two each otherwise
+    // (D = 256: 160 KB, all of a CU's LDS)
     static constexpr bool kPP = D <= 128;
-    static constexpr int kSlots16 = kPP ? 3 : 1;
+    static constexpr int kSlots16 = kPP ? 3 : 2;
     static constexpr int kSlotsQK = kPP ? 3 : 2;
     // The tiles Q.K^T reads: K8, or K16 in the plain bf16 mode (which then
-    // needs no separate K16 slots and no Q8 rows).
+    // needs no separate K16 slots).
     static constexpr int kQKRow = kPlain ? kK16Row : kK8Row;
     static constexpr int kQKBytes = kTileKeys * kQKRow;
     static constexpr int kK8Off = 0;
     static constexpr int kK16Off = kSlotsQK * kQKBytes;
     static constexpr int kVtOff = kK16Off + (kPlain ? 0 : kSlots16 * kK16Bytes);
-    static constexpr int kQ8Off = kVtOff + kSlots16 * kVtBytes;
-    static constexpr int kLdsBytes = kQ8Off + (kPlain ? 0 : kWaves * kQ8Bytes);
+    static constexpr int kLdsBytes = kVtOff + kSlots16 * kVtBytes;
     static constexpr int kDB = D / 16;        // 16-wide output column blocks
     static constexpr int kDC = D / 32;        // 32-deep bf16 matrix-core steps
 };
@@ -139,7 +137,6 @@ __global__ __launch_bounds__(kThreads, 1) void lamp_attn_kernel(AttnArgs a) {
     constexpr int kQG = C::kQG;
     constexpr int kWaveRows = C::kWaveRows;
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-    __shared__ uint32_t flag_lds[kWaves];    // 4-bit flag sets exchanged by the waves of a block
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6;
@@ -203,88 +200,19 @@ __global__ __launch_bounds__(kThreads, 1) void lamp_attn_kernel(AttnArgs a) {
         tf_lo = a.window > 0 && num > 0 ? (num + kTileKeys - 1) / kTileKeys : 0;
     }
 
-    uint8_t* q8_lds = lds + C::kQ8Off + wave * C::kQ8Bytes;
 
-    // ---- staging: register loads at the start of an iteration, LDS stores at its end
-    // Thread tid owns the 16-byte chunks tid + kThreads*i of a tile, i.e. LDS
-    // bytes [16 c, 16 c + 16) of the swizzled layout, and loads the global chunk
-    // that belongs there.  Loads and stores run every iteration: a tile past
-    // the last one reloads the last one (its stores fill slots that no later
-    // phase reads), which keeps every load consumed by a store on every path
-    // and so keeps the compiler from waiting on loads at the loop head.
+    // ---- staging: K8, K16 and V^T tiles are copied from global memory straight
+    // into swizzled LDS layouts.  Thread tid owns the 16-byte chunks
+    // c = tid + kThreads*i of a tile, i.e. LDS bytes [16 c, 16 c + 16), and
+    // copies the global chunk that belongs there.
     constexpr int kK8Ch = C::kQKBytes / 16 / kThreads;     // chunks per thread and tile
     constexpr int kK16Ch = C::kK16Bytes / 16 / kThreads;
     constexpr int kVtCh = C::kVtBytes / 16 / kThreads;
     static_assert(kK16Ch >= 1 && kVtCh >= 1, "tile smaller than one chunk per thread");
     constexpr int kK8ChMin = kK8Ch > 0 ? kK8Ch : 1;
-    u32x4 st_k8[kK8ChMin], st_k16[kK16Ch], st_vt[kVtCh];
-    // Global addresses are a wave-uniform tile base plus an unsigned 32-bit
-    // per-thread byte offset (scalar base + vector offset addressing).
     const uint8_t* k16_head = reinterpret_cast<const uint8_t*>(a.k16 + kv_head * a.S * D);
-    auto load_k8 = [&](int t) __attribute__((always_inline)) {
-        constexpr int kNC = C::kQKRow / 16;
-        if constexpr (kPlain) {
-            // K16 rows; keys past the end reload the last key (masked out)
-#pragma unroll
-            for (int i = 0; i < kK8ChMin; ++i) {
-                const unsigned p = (tid + i * kThreads) * 16;
-                const unsigned row = p / C::kQKRow, slot = (p % C::kQKRow) >> 4;
-                const unsigned key = min(min(t, t_end) * kTileKeys + (int)row, a.S - 1);
-                st_k8[i] = *reinterpret_cast<const u32x4*>(k16_head + (key * C::kQKRow + ((slot ^ swz<kNC>(row)) << 4)));
-            }
-        } else {
-            const uint8_t* src = a.k8 + (kv_head * a.S_pad + (size_t)min(t, t_end) * kTileKeys) * D;
-#pragma unroll
-            for (int i = 0; i < kK8ChMin; ++i) {
-                const unsigned p = min((tid + i * kThreads) * 16, C::kQKBytes - 16);
-                const unsigned row = p / C::kQKRow, slot = (p % C::kQKRow) >> 4;
-                st_k8[i] = *reinterpret_cast<const u32x4*>(src + (row * C::kQKRow + ((slot ^ swz<kNC>(row)) << 4)));
-            }
-        }
-    };
-    auto store_k8 = [&](int t) __attribute__((always_inline)) {
-        uint8_t* base = lds + C::kK8Off + (t & 1) * C::kQKBytes;
-#pragma unroll
-        for (int i = 0; i < kK8ChMin; ++i) {
-            const int p = (tid + i * kThreads) * 16;
-            if (p < C::kQKBytes) *reinterpret_cast<u32x4*>(base + p) = st_k8[i];
-        }
-    };
-    auto load_k16 = [&](int t) __attribute__((always_inline)) {
-        constexpr int kNC = C::kK16Row / 16;
-#pragma unroll
-        for (int i = 0; i < kK16Ch; ++i) {
-            const unsigned p = (tid + i * kThreads) * 16;
-            const unsigned row = p / C::kK16Row, slot = (p % C::kK16Row) >> 4;
-            // keys past the end reload the last key: they are masked out
-            const unsigned key = min(t * kTileKeys + (int)row, a.S - 1);
-            st_k16[i] = *reinterpret_cast<const u32x4*>(k16_head + (key * C::kK16Row + ((slot ^ swz<kNC>(row)) << 4)));
-        }
-    };
-    auto store_k16 = [&](int slot) __attribute__((always_inline)) {
-        uint8_t* base = lds + C::kK16Off + slot * C::kK16Bytes;
-#pragma unroll
-        for (int i = 0; i < kK16Ch; ++i) *reinterpret_cast<u32x4*>(base + (tid + i * kThreads) * 16) = st_k16[i];
-    };
-    auto load_vt = [&](int t) __attribute__((always_inline)) {
-        const uint8_t* src = reinterpret_cast<const uint8_t*>(a.vt + (kv_head * a.nT + min(t, t_end)) * (size_t)D * kTileKeys);
-        constexpr int kNC = C::kVtRow / 16;
-#pragma unroll
-        for (int i = 0; i < kVtCh; ++i) {
-            const unsigned p = (tid + i * kThreads) * 16;
-            const unsigned row = p / C::kVtRow, slot = (p % C::kVtRow) >> 4;
-            st_vt[i] = *reinterpret_cast<const u32x4*>(src + (row * C::kVtRow + ((slot ^ swz<kNC>(row)) << 4)));
-        }
-    };
-    auto store_vt = [&](int slot) __attribute__((always_inline)) {
-        uint8_t* base = lds + C::kVtOff + slot * C::kVtBytes;
-#pragma unroll
-        for (int i = 0; i < kVtCh; ++i) *reinterpret_cast<u32x4*>(base + (tid + i * kThreads) * 16) = st_vt[i];
-    };
-    // Ping-pong schedule: direct global-to-LDS copies, no registers.  Copy i
-    // of wave w moves chunks i*kThreads + 64w .. +63 of a tile, lane l the
-    // chunk i*kThreads + 64w + l: the chunk-to-thread map of the staged loads.
-    // Each array of the (batch, kv head) is one buffer: a lane's byte offset
+    // Copy i of wave w moves chunks i*kThreads + 64w .. +63 of a tile, lane l
+    // the chunk i*kThreads + 64w + l.  Each array of the (batch, kv head) is one buffer: a lane's byte offset
     // (row and swizzled chunk) is fixed, the tile's is a scalar, and reads past
     // the buffer's end (keys past the last) return zeros.  A copy's LDS
     // destination is one wave-uniform address; lane l's 16 bytes land 16 l
@@ -360,34 +288,36 @@ __global__ __launch_bounds__(kThreads, 1) void lamp_attn_kernel(AttnArgs a) {
 #pragma unroll
         for (int ch = 0; ch < C::kDC; ++ch) qb[ch][qg] = *reinterpret_cast<const v8bf*>(qrow + ch * 32 + g * 8);
     }
+    // Q8 = E4M3(fl32(q * inv)) of this wave's rows (the arithmetic of the
+    // quantisation pass), straight into the 8-bit operand registers: lane
+    // (n16, g) holds depth 32g .. 32g+31 of 128-deep step st of row 16qg + n16
+    // (D = 64: lane groups 2, 3 hold zeros); rows past the end are zero.
+    v8i q8r[C::kKS][kQG];
     if constexpr (!kPlain) {
-        // Q8 = E4M3(fl32(q * inv)) for this wave's rows, the arithmetic of the
-        // quantisation pass; rows past the end are zero
-        constexpr int kNC = C::kK8Row / 16;
         const float inv = active ? a.q_inv[q_head] : 1.0f;
 #pragma unroll
-        for (int i = 0; i < C::kQ8Bytes / 1024; ++i) {
-            const int p = i * 1024 + lane * 16;
-            const int row = p / C::kK8Row, slot = (p % C::kK8Row) >> 4;
-            const int gq = row0 + row;
-            u32x4 o = {0u, 0u, 0u, 0u};
-            if (gq < a.S) {
-                const uint16_t* src = a.q16 + (q_head * a.S + gq) * D + ((slot ^ swz<kNC>(row)) << 4);
+        for (int st = 0; st < C::kKS; ++st)
 #pragma unroll
-                for (int h = 0; h < 2; ++h) {
-                    const u32x4 w = *reinterpret_cast<const u32x4*>(src + 8 * h);
-                    float x[8];
+            for (int qg = 0; qg < kQG; ++qg) {
+                v8i x8 = {0, 0, 0, 0, 0, 0, 0, 0};
+                const int gq = row0 + qg * 16 + n16;
+                if (gq < a.S && (D >= 128 || g * 32 < D)) {
+                    const uint16_t* src = a.q16 + (q_head * a.S + gq) * D + (D >= 128 ? st * 128 + 32 * g : 32 * g);
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        x[2 * j] = bf16_bits_to_float(w[j] & 0xFFFFu) * inv;
-                        x[2 * j + 1] = bf16_bits_to_float(w[j] >> 16) * inv;
+                    for (int h = 0; h < 4; ++h) {
+                        const u32x4 w = *reinterpret_cast<const u32x4*>(src + 8 * h);
+                        float x[8];
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) {
+                            x[2 * j] = bf16_bits_to_float(w[j] & 0xFFFFu) * inv;
+                            x[2 * j + 1] = bf16_bits_to_float(w[j] >> 16) * inv;
+                        }
+                        x8[2 * h] = (int)cvt_pk_e4m3<true>(x[2], x[3], cvt_pk_e4m3<false>(x[0], x[1], 0u));
+                        x8[2 * h + 1] = (int)cvt_pk_e4m3<true>(x[6], x[7], cvt_pk_e4m3<false>(x[4], x[5], 0u));
                     }
-                    o[2 * h] = cvt_pk_e4m3<true>(x[2], x[3], cvt_pk_e4m3<false>(x[0], x[1], 0u));
-                    o[2 * h + 1] = cvt_pk_e4m3<true>(x[6], x[7], cvt_pk_e4m3<false>(x[4], x[5], 0u));
                 }
+                q8r[st][qg] = x8;
             }
-            *reinterpret_cast<u32x4*>(q8_lds + p) = o;
-        }
     }
 #pragma unroll
     for (int qg = 0; qg < kQG; ++qg) m_run[qg] = -__builtin_inff();
@@ -419,13 +349,6 @@ __global__ __launch_bounds__(kThreads, 1) void lamp_attn_kernel(AttnArgs a) {
         for (int db = 0; db < C::kDB; ++db) acc_o[qg][db] = v4f{0.f, 0.f, 0.f, 0.f};
     }
 
-    // the ping-pong schedule keeps this wave's 8-bit Q operand in registers
-    constexpr bool kQ8Reg = C::kPP && !kPlain && C::kKS == 1;
-    v8i q8r[kQG];
-    if constexpr (kQ8Reg) {
-#pragma unroll
-        for (int qg = 0; qg < kQG; ++qg) q8r[qg] = fp8_operand<D>(q8_lds, qg * 16 + n16, 0, g);
-    }
     auto work = [&](int t) __attribute__((always_inline)) { return t >= tv_lo && t <= tv_hi; };
     auto full_tile = [&](int t) __attribute__((always_inline)) { return t >= tf_lo && t <= tf_hi; };
 
@@ -450,17 +373,13 @@ __global__ __launch_bounds__(kThreads, 1) void lamp_attn_kernel(AttnArgs a) {
         const uint8_t* k8l = lds + C::kK8Off + slot * C::kQKBytes;
 #pragma unroll
         for (int st = 0; st < C::kKS; ++st) {
-            v8i qf[kQG];
-#pragma unroll
-            for (int qg = 0; qg < kQG; ++qg)
-                qf[qg] = kQ8Reg ? q8r[qg] : fp8_operand<D>(q8_lds, qg * 16 + n16, st, g);
 #pragma unroll
             for (int kb = 0; kb < 4; ++kb) {
                 const v8i ka = fp8_operand<D>(k8l, kb * 16 + n16, st, g);
 #pragma unroll
                 for (int qg = 0; qg < kQG; ++qg)
                     s[qg][kb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                        ka, qf[qg], st == 0 ? v4f{0.f, 0.f, 0.f, 0.f} : s[qg][kb], 0, 0, 0, 0, 0, 0);
+                        ka, q8r[st][qg], st == 0 ? v4f{0.f, 0.f, 0.f, 0.f} : s[qg][kb], 0, 0, 0, 0, 0, 0);
             }
         }
     };
@@ -804,6 +723,12 @@ __global__ __launch_bounds__(kThreads, 1) void lamp_attn_kernel(AttnArgs a) {
 
     v4f S[kQG][4];
     u32x2 P[kQG][4];
+    constexpr auto kFull = std::integral_constant<bool, false>{};
+    constexpr auto kPart = std::integral_constant<bool, true>{};
+    // waits for this wave's outstanding copies into LDS (and global stores)
+    auto wait_copies = []() __attribute__((always_inline)) {
+        __asm__ __volatile__("s_waitcnt vmcnt(0)" ::: "memory");
+    };
     if constexpr (C::kPP) {
         // ---- ping-pong schedule ---------------------------------------------------------
         // Waves 0-3 (one per SIMD) and waves 4-7 run the same sequence of phases,
@@ -823,12 +748,8 @@ __global__ __launch_bounds__(kThreads, 1) void lamp_attn_kernel(AttnArgs a) {
         // reader, the first group's M(t+2).  In the plain bf16 mode
         // the Q.K^T tiles are K16 tiles, staged like K8, and there is no test or
         // recompute.
+        __shared__ uint32_t flag_lds[kWaves];    // 4-bit flag sets exchanged by the waves of a block
         const int grp = wave >> 2;
-        constexpr auto kFull = std::integral_constant<bool, false>{};
-        constexpr auto kPart = std::integral_constant<bool, true>{};
-        auto wait_copies = []() __attribute__((always_inline)) {
-            __asm__ __volatile__("s_waitcnt vmcnt(0)" ::: "memory");
-        };
         int s_cur = t_begin % 3;                 // slot of tile t
         const int s_b1 = s_cur == 2 ? 0 : s_cur + 1;
         const int s_b2 = s_b1 == 2 ? 0 : s_b1 + 1;
@@ -894,56 +815,62 @@ __global__ __launch_bounds__(kThreads, 1) void lamp_attn_kernel(AttnArgs a) {
         }
         if (grp == 0) lds_barrier();
     } else {
-        // ---- prologue staging and the first tile's Q.K^T ------------------------------
-        load_k8(t_begin);
-        load_k16(t_begin);
-        store_k8(t_begin);
-        store_k16(0);
-        load_k8(t_begin + 1);
-        store_k8(t_begin + 1);
+        // ---- one software-pipelined loop (D = 256) ----------------------------------------
+        // Iteration t: copies of K8(t+1) and K16(t+1) into slot (t+1) & 1 and of
+        // V^T(t) into slot t & 1; P.V of tile t-1 (its products run under the
+        // vector work of tile t); max, exponentials and test of tile t; flag
+        // barrier; recompute of tile t; Q.K^T of tile t+1; rescale; barrier.
+        // The copies overwrite K8(t-1), K16(t-1) and V^T(t-2), whose last
+        // readers (Q.K^T in iteration t-2, the recompute and P.V in iteration
+        // t-1) are behind the previous barrier.  Each wave waits for its K8 copy
+        // before the flag barrier (Q.K^T of t+1 follows it) and for the rest
+        // before the closing barrier.  The 4-bit flag sets go through the first
+        // bytes of K8 slot t & 1: K8(t) has been read, and K8(t+2) is copied
+        // there only after the closing barrier.
+        constexpr int kAfterK8 = kK16Ch + kVtCh;    // copies issued after a tile's K8 copies
+        static_assert(kAfterK8 < 16, "vmcnt immediate");
+        dma_qk(t_begin, t_begin & 1);
+        dma_k16(t_begin, t_begin & 1);
+        wait_copies();
         lds_barrier();
         if (work(t_begin)) qk(S, t_begin & 1);
-        lds_barrier();   // every wave has read K8(t_begin) before its slot is refilled
-
-        // ---- the pipelined loop ---------------------------------------------------------
+        lds_barrier();   // every wave has read K8(t_begin): its slot takes the flags
         for (int t = t_begin; t <= t_end; ++t) {
-            // K16 of tile t (loaded in the previous iteration) into its single slot:
-            // every wave has finished the recompute of tile t-1, and the flag
-            // barrier below orders these stores before the recompute of tile t
-            if (t > t_begin) store_k16(0);
+            const int sc = t & 1, sn = sc ^ 1;
+            if (t + 1 <= t_end) {
+                dma_qk(t + 1, sn);
+                dma_k16(t + 1, sn);
+            }
+            dma_vt(t, sc);
             const bool w_prev = work(t - 1), w_cur = work(t), w_next = work(t + 1);
             const bool full = full_tile(t);
             // P.V of tile t-1 is issued first (it reads P before the exponentials
-            // of tile t overwrite it) and runs on the matrix cores under the
-            // vector work of tile t
-            if (w_prev) pv(P, 0, [](int) {});
+            // of tile t overwrite it)
+            if (w_prev) pv(P, sn, [](int) {});
+            uint32_t flags = 0u;
             if (w_cur) {
                 round_logits(S);
-                if (full) softmax(S, P, t, std::integral_constant<bool, false>{});
-                else softmax(S, P, t, std::integral_constant<bool, true>{});
+                if (full) softmax(S, P, t, kFull);
+                else softmax(S, P, t, kPart);
+                flags = full ? test(S, kFull) : test(S, kPart);
             }
-            // loads for later tiles, stored to LDS before the barrier that ends this
-            // iteration
-            load_k8(t + 2);
-            load_k16(t + 1);
-            load_vt(t);
-            uint32_t flags = 0u;
-            if (w_cur)
-                flags = full ? test(S, std::integral_constant<bool, false>{})
-                             : test(S, std::integral_constant<bool, true>{});
             // the waves of a 64-row block OR their flags
-            if (lane == 0) flag_lds[wave] = flags;
+            uint32_t* flag_slot = reinterpret_cast<uint32_t*>(lds + C::kK8Off + sc * C::kQKBytes);
+            if (lane == 0) flag_slot[wave] = flags;
+            // this wave's K8(t+1) copies have landed (at most kAfterK8 newer
+            // copies outstanding; an iteration without them waits for nothing)
+            __asm__ __volatile__("s_waitcnt vmcnt(%0)" ::"n"(kAfterK8) : "memory");
             lds_barrier();
             flags = 0;
-    #pragma unroll
-            for (int w = 0; w < C::kWavesPerBlock; ++w) flags |= flag_lds[blk * C::kWavesPerBlock + w];
+#pragma unroll
+            for (int w = 0; w < C::kWavesPerBlock; ++w) flags |= flag_slot[blk * C::kWavesPerBlock + w];
             flags = __builtin_amdgcn_readfirstlane(flags);
             if (w_cur && flags != 0) {
-                if (full) recompute(P, flags, std::integral_constant<bool, false>{}, 0);
-                else recompute(P, flags, std::integral_constant<bool, true>{}, 0);
+                if (full) recompute(P, flags, kFull, sc);
+                else recompute(P, flags, kPart, sc);
             }
             // Q.K^T of tile t+1 runs on the matrix cores under what follows
-            if (w_next) qk(S, (t + 1) & 1);
+            if (w_next) qk(S, sn);
             if (w_cur) {
                 dump_p(P, t);
                 rescale();
@@ -951,15 +878,11 @@ __global__ __launch_bounds__(kThreads, 1) void lamp_attn_kernel(AttnArgs a) {
                 if (a.mask && wib == 0 && lane == 0)
                     a.mask[(q_head * a.nT + r) * a.nT + t] = (uint8_t)(0x80u | flags);
             }
-            // K8 of tile t+2 into the slot Q.K^T of tile t used; V^T of tile t into
-            // its single slot (every wave passed the flag barrier, so the P.V of
-            // tile t-1 has read it)
-            store_k8(t + 2);
-            store_vt(0);
+            wait_copies();
             lds_barrier();
         }
         // P.V of the last tile
-        if (work(t_end)) pv(P, 0, [](int) {});
+        if (work(t_end)) pv(P, t_end & 1, [](int) {});
     }
 
     // ---- epilogue: out = O / l ------------------------------------------------------
