@@ -31,22 +31,41 @@ PEAK_BF16 = 2.5e15         # MI355X dense bf16 matrix FLOP/s
 PEAK_HBM = 8.0e12          # MI355X HBM3E bytes/s
 COPY_BYTES = 1 << 30       # size of the calibration copy
 
-# HBM traffic of the attention kernel on the qwen3-8b workload from two
-# rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE; KiB per dispatch), each scaled
-# by the same counter's reading for a plain copy of COPY_BYTES (see
-# profiles/attn_qwen3_8b_hbm_traffic.md).  Valid only for the kernel source
-# whose hash is recorded; any change to it makes the figure null.
-TRAFFIC = {"kernel_hash": "cf40d647f84067a2", "workload": "qwen3-8b", "delta": 2.0 ** -8, "tau": 2.0 ** -1,
-           "bytes_per_launch": 137899189.2}
+# HBM traffic of the attention kernel per workload, from two rocprofv3 --pmc
+# runs (FETCH_SIZE, WRITE_SIZE; KiB per dispatch), each scaled by the same
+# counter's reading for a plain copy of COPY_BYTES (profiles/
+# attn_qwen3_8b_hbm_traffic.md, attn_gemma3_12b_counters.md).  Valid only for
+# the kernel source whose hash is recorded; any change to it makes the figure
+# null.
+TRAFFIC = [
+    {"kernel_hash": "a2cd920749cc33ec", "workload": "qwen3-8b", "delta": 2.0 ** -8, "tau": 2.0 ** -1,
+     "bytes_per_launch": 131232940.1},
+    {"kernel_hash": "a2cd920749cc33ec", "workload": "gemma3-12b", "delta": 2.0 ** -8, "tau": 2.0 ** -1,
+     "bytes_per_launch": 1185432941.0},
+]
 
 
-# Vector-issue ceiling of the attention kernel on the qwen3-8b workload, from
-# the instruction counters of profiles/attn_qwen3_8b_sq_counters.md: vector
-# cycles per SIMD per launch (full-rate instructions 4 cycles, v_exp_f32 and
-# v_cvt_pk_fp8_f32 8, matrix products 4 of issue), i.e. the launch time if the
-# vector units were never idle.  Valid only for the recorded kernel source.
-VALU_CEILING = {"kernel_hash": "cf40d647f84067a2", "workload": "qwen3-8b", "delta": 2.0 ** -8,
-                "tau": 2.0 ** -1, "cycles_per_simd": 211896.3, "clock_hz": 2.4e9}
+# Vector-issue ceiling of the attention kernel per workload, from the
+# instruction counters (profiles/attn_qwen3_8b_sq_counters.md,
+# attn_gemma3_12b_counters.md): vector cycles per SIMD per launch (full-rate
+# instructions 4 cycles, v_exp_f32 and v_cvt_pk_fp8_f32 8, matrix products 4
+# of issue), i.e. the launch time if the vector units were never idle.  Valid
+# only for the recorded kernel source.
+VALU_CEILING = [
+    {"kernel_hash": "a2cd920749cc33ec", "workload": "qwen3-8b", "delta": 2.0 ** -8, "tau": 2.0 ** -1,
+     "cycles_per_simd": 211120.3, "clock_hz": 2.4e9, "source": "profiles/attn_qwen3_8b_sq_counters.md"},
+    {"kernel_hash": "a2cd920749cc33ec", "workload": "gemma3-12b", "delta": 2.0 ** -8, "tau": 2.0 ** -1,
+     "cycles_per_simd": 575520.3, "clock_hz": 2.4e9, "source": "profiles/attn_gemma3_12b_counters.md"},
+]
+
+
+def _record(records, args, kernel_hash):
+    """The record of `records` measured on this kernel source and workload point."""
+    for r in records:
+        if (r["kernel_hash"] == kernel_hash and r["workload"] == args.workload
+                and r["delta"] == args.delta and r["tau"] == args.tau):
+            return r
+    return None
 
 
 # The same for the decode kernel on the qwen3-8b-decode workload
@@ -578,16 +597,13 @@ def main():
     t_mfma = m["f_qk8"] / PEAK_FP8 + (m["f_pv"] + m["f_qk16"]) / PEAK_BF16
     t_roof = t_mfma + quant_bytes / PEAK_HBM
     valu_ceiling = None
-    if (VALU_CEILING["kernel_hash"] == kernel_source_hash() and VALU_CEILING["workload"] == args.workload
-            and VALU_CEILING["delta"] == args.delta and VALU_CEILING["tau"] == args.tau):
-        t_valu = VALU_CEILING["cycles_per_simd"] / VALU_CEILING["clock_hz"]
+    vrec = _record(VALU_CEILING, args, kernel_source_hash())
+    if vrec is not None:
+        t_valu = vrec["cycles_per_simd"] / vrec["clock_hz"]
         valu_ceiling = {"bound": "valu", "ceiling_ms": t_valu * 1e3, "frac": t_valu / (attn_ms_avg * 1e-3),
-                        "source": "instruction counters, profiles/attn_qwen3_8b_sq_counters.md"}
-    traffic = None
-    if (TRAFFIC is not None and TRAFFIC["kernel_hash"] == kernel_source_hash()
-            and TRAFFIC["workload"] == args.workload and TRAFFIC["delta"] == args.delta
-            and TRAFFIC["tau"] == args.tau):
-        traffic = TRAFFIC["bytes_per_launch"]
+                        "source": "instruction counters, " + vrec["source"]}
+    trec = _record(TRAFFIC, args, kernel_source_hash())
+    traffic = trec["bytes_per_launch"] if trec is not None else None
     res = {
         "metric": METRIC,
         "value": f_nom / (ms_per_step * 1e-3) / 1e12,
