@@ -7,6 +7,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <initializer_list>
 #include <mutex>
 #include <string>
 
@@ -122,16 +123,28 @@ int get_workspace(size_t bytes, void** out) {
     return LAMP_OK;
 }
 
+// Whether the product of positive factors (each below 2^32) reaches `limit`
+// (at most 2^31): the running product is checked after every factor, so it
+// never overflows.
+bool product_reaches(std::initializer_list<int64_t> factors, int64_t limit) {
+    int64_t p = 1;
+    for (int64_t f : factors) {
+        p *= f;
+        if (p >= limit) return true;
+    }
+    return false;
+}
+
 int check_sizes(int B, int Hq, int Hkv, int S, int D) {
     if (B < 1 || Hq < 1 || Hkv < 1 || S < 1 || D < 1)
         return fail(LAMP_ERR_INVALID, "sizes must be >= 1 (B=%d Hq=%d Hkv=%d S=%d D=%d)", B, Hq, Hkv, S, D);
     if (Hq % Hkv != 0) return fail(LAMP_ERR_INVALID, "Hq (%d) must be a multiple of Hkv (%d)", Hq, Hkv);
     if (D != 64 && D != 128 && D != 256)
         return fail(LAMP_ERR_UNSUPPORTED, "head dimension D=%d (supported: 64, 128, 256)", D);
-    const int64_t nT = (S + 63) / 64;
-    const int64_t elems = (int64_t)B * Hq * nT * 64 * D;
-    if (elems >= ((int64_t)1 << 31))
-        return fail(LAMP_ERR_UNSUPPORTED, "B*Hq*S*D = %lld exceeds 2^31", (long long)elems);
+    const int64_t nT = ((int64_t)S + 63) / 64;   // 64-bit: S may be INT_MAX
+    if (product_reaches({B, Hq, nT * 64, D}, (int64_t)1 << 31))
+        return fail(LAMP_ERR_UNSUPPORTED, "B*Hq*S*D (S padded to 64) reaches 2^31 (B=%d Hq=%d S=%d D=%d)",
+                    B, Hq, S, D);
     return LAMP_OK;
 }
 
@@ -210,8 +223,9 @@ int check_decode(int B, int Hq, int Hkv, int Sq, int Skv, int D) {
         return fail(LAMP_ERR_UNSUPPORTED, "head dimension D=%d (supported: 64, 128, 256)", D);
     if (Sq > 16) return fail(LAMP_ERR_UNSUPPORTED, "decode needs Sq <= 16 (got %d)", Sq);
     if (Hq / Hkv > 8) return fail(LAMP_ERR_UNSUPPORTED, "decode needs Hq/Hkv <= 8 (got %d)", Hq / Hkv);
-    const int64_t nT = (Skv + 63) / 64;
-    if ((int64_t)B * Hkv * nT * 64 * D >= ((int64_t)1 << 31) || (int64_t)B * Hq * Sq * D * nT >= ((int64_t)1 << 31))
+    const int64_t nT = ((int64_t)Skv + 63) / 64;   // 64-bit: Skv may be INT_MAX
+    if (product_reaches({B, Hkv, nT * 64, D}, (int64_t)1 << 31) ||
+        product_reaches({B, Hq, Sq, D, nT}, (int64_t)1 << 31))
         return fail(LAMP_ERR_UNSUPPORTED, "decode sizes exceed 2^31 elements");
     return LAMP_OK;
 }
@@ -518,6 +532,9 @@ int lamp_subblock_stats(const uint8_t* subblock_mask, int B, int Hq, int S, int 
                         int64_t* stats_out) {
     if (!subblock_mask || !stats_out) return fail(LAMP_ERR_INVALID, "mask and stats_out must be non-null");
     if (B < 1 || Hq < 1 || S < 1) return fail(LAMP_ERR_INVALID, "sizes must be >= 1");
+    const int64_t nT = ((int64_t)S + 63) / 64;
+    if (product_reaches({B, Hq, nT, nT}, (int64_t)1 << 31))
+        return fail(LAMP_ERR_UNSUPPORTED, "a mask of B*Hq*nT*nT bytes reaches 2^31 (B=%d Hq=%d S=%d)", B, Hq, S);
     if (causal != 0 && causal != 1) return fail(LAMP_ERR_INVALID, "causal must be 0 or 1");
     if (window < 0 || (window > 0 && !causal)) return fail(LAMP_ERR_INVALID, "bad window");
     if ((reinterpret_cast<uintptr_t>(stats_out) & 7u) != 0) return fail(LAMP_ERR_INVALID, "stats_out must be 8-byte aligned");
