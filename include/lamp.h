@@ -159,7 +159,8 @@ int lamp_attn_fwd_bf16(const void* q, const void* k, const void* v, float* out,
  *   [0..4] tiles with 0..4 sub-blocks in 16-bit (visited tiles only),
  *   [5] visited tiles, [6] visited sub-blocks (holding a visible entry),
  *   [7] sub-blocks in 16-bit, [8] visible entries, [9] visible entries in
- *   16-bit sub-blocks.  Overwritten, not accumulated. */
+ *   16-bit sub-blocks.  Overwritten, not accumulated.  A mask of 2^31 bytes
+ * or more (B * Hq * ceil(S/64)^2) is LAMP_ERR_UNSUPPORTED. */
 #define LAMP_STATS_LEN 10
 int lamp_subblock_stats(const uint8_t* subblock_mask, int B, int Hq, int S,
                         int causal, int window, int64_t* stats_out);
