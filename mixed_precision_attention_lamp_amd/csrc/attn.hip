@@ -488,11 +488,7 @@ __global__ __launch_bounds__(kThreads, 1) void lamp_attn_kernel(AttnArgs a) {
                 const int qi = row0 + qg * 16 + n16;
 #pragma unroll
                 for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const int kj = t * kTileKeys + kb * 16 + g * 4 + i;
-                        vis[qg] |= (pair_visible(qi, kj, a.S, a.causal, a.window) ? 1u : 0u) << (kb * 4 + i);
-                    }
+                    vis[qg] |= visible4(qi, t * kTileKeys + kb * 16 + g * 4, a.S, a.causal, a.window) << (kb * 4);
             }
         }
         // running max in the log2 domain: rounding is monotone, so the max of

@@ -59,6 +59,18 @@ __device__ __forceinline__ bool pair_visible(int i, int j, int S, int causal, in
     return i < S && j < S && (!causal || j <= i) && (window <= 0 || i - j < window);
 }
 
+// pair_visible(i, j0 + e, ...) for e = 0..3 as bits 0..3: the visible keys of
+// a run of four are one contiguous range [lo, hi) of e (clamped counts from
+// the end of the sequence, the causal bound and the window), so the mask is
+// a difference of two low-bit masks.
+__device__ __forceinline__ uint32_t visible4(int i, int j0, int S, int causal, int window) {
+    int hi = min(max(S - j0, 0), 4);
+    if (causal) hi = min(hi, max(i - j0 + 1, 0));
+    const int lo = window > 0 ? min(max(i - window - j0 + 1, 0), 4) : 0;
+    const uint32_t m = ((1u << hi) - 1u) & ~((1u << lo) - 1u);
+    return i < S ? m : 0u;
+}
+
 // Smallest fp32 a >= 0 with fl32(a * c8) >= t2: then |s| >= t2 for the
 // log2-domain logit s = fl32(acc * c8) exactly when |acc| >= a (rounding is
 // monotone).  0 when every logit passes, +inf when none can.
