@@ -38,10 +38,10 @@ COPY_BYTES = 1 << 30       # size of the calibration copy
 # the kernel source whose hash is recorded; any change to it makes the figure
 # null.
 TRAFFIC = [
-    {"kernel_hash": "a2cd920749cc33ec", "workload": "qwen3-8b", "delta": 2.0 ** -8, "tau": 2.0 ** -1,
-     "bytes_per_launch": 131232940.1},
-    {"kernel_hash": "a2cd920749cc33ec", "workload": "gemma3-12b", "delta": 2.0 ** -8, "tau": 2.0 ** -1,
-     "bytes_per_launch": 1185432941.0},
+    {"kernel_hash": "be1fbab06caff0dc", "workload": "qwen3-8b", "delta": 2.0 ** -8, "tau": 2.0 ** -1,
+     "bytes_per_launch": 130217078.4},
+    {"kernel_hash": "be1fbab06caff0dc", "workload": "gemma3-12b", "delta": 2.0 ** -8, "tau": 2.0 ** -1,
+     "bytes_per_launch": 419012325.0},
 ]
 
 
@@ -52,10 +52,10 @@ TRAFFIC = [
 # of issue), i.e. the launch time if the vector units were never idle.  Valid
 # only for the recorded kernel source.
 VALU_CEILING = [
-    {"kernel_hash": "a2cd920749cc33ec", "workload": "qwen3-8b", "delta": 2.0 ** -8, "tau": 2.0 ** -1,
-     "cycles_per_simd": 211120.3, "clock_hz": 2.4e9, "source": "profiles/attn_qwen3_8b_sq_counters.md"},
-    {"kernel_hash": "a2cd920749cc33ec", "workload": "gemma3-12b", "delta": 2.0 ** -8, "tau": 2.0 ** -1,
-     "cycles_per_simd": 575520.3, "clock_hz": 2.4e9, "source": "profiles/attn_gemma3_12b_counters.md"},
+    {"kernel_hash": "be1fbab06caff0dc", "workload": "qwen3-8b", "delta": 2.0 ** -8, "tau": 2.0 ** -1,
+     "cycles_per_simd": 208704.3, "clock_hz": 2.4e9, "source": "profiles/attn_qwen3_8b_sq_counters.md"},
+    {"kernel_hash": "be1fbab06caff0dc", "workload": "gemma3-12b", "delta": 2.0 ** -8, "tau": 2.0 ** -1,
+     "cycles_per_simd": 569344.3, "clock_hz": 2.4e9, "source": "profiles/attn_gemma3_12b_counters.md"},
 ]
 
 

@@ -150,16 +150,18 @@ __global__ __launch_bounds__(kThreads, 1) void lamp_attn_kernel(AttnArgs a) {
     // Workgroups are dispatched in index order, round-robin over the XCDs.
     // Index order is longest (causal) rows first; consecutive indices are
     // consecutive units, so with 8 units per level each XCD keeps to one unit
-    // and its K/V tiles stay in that XCD's L2.  Unpaired launches offset the
-    // units by the level's parity, so that each XCD alternates between two
-    // units: units differ in how much they recompute, and two share the
-    // load while each K/V tile is fetched into two L2s only.
+    // and its K/V tiles stay in that XCD's L2.  Unpaired launches with D <= 128
+    // offset the units by the level's parity, so that each XCD alternates
+    // between two units: units differ in how much they recompute, and two
+    // share the load while each K/V tile is fetched into two L2s only.  At
+    // D = 256 a unit's tiles outgrow an XCD's L2 by themselves, and one unit
+    // per XCD measured faster.
     const int wg = blockIdx.x;
     const int n_hg = a.G / a.heads_per_wg;
     const int n_lv = a.paired ? (a.n_rg + 1) / 2 : a.n_rg;
     const int n_u = a.n_wg / n_lv;
     const int level = wg / n_u;
-    int u = (wg % n_u + (a.paired ? 0 : (level & 1))) % n_u;
+    int u = (wg % n_u + (a.paired || D == 256 ? 0 : (level & 1))) % n_u;
     const int hg = u % n_hg;
     u /= n_hg;
     const int hk = u % a.Hkv;
