@@ -24,15 +24,15 @@
 // work under the other wave's vector work; the K8, K16 and V^T tiles are
 // copied from global memory straight into LDS (buffer loads with an LDS
 // destination, no registers) two tiles ahead, into three slots per array.
-// D = 256 (no room for a second set of slots): every wave runs one
-// software-pipelined loop; the P.V products of tile t-1 run under the vector
-// work of tile t, and the Q.K^T products of tile t+1 under the rescale,
-// the LDS stores and the barrier; tiles are staged through registers (K8 two
-// tiles ahead in two slots, K16 and V^T in one slot each).  LDS layouts are
-// unpadded, their 16-byte chunks XOR-swizzled by row (conflict-free operand
-// reads).  Each wave quantises its Q rows into LDS in the prologue (the
-// arithmetic of the quantisation pass) and keeps its Q16 operand (and, for
-// D <= 128, its Q8 operand) in registers.
+// D = 256 (no room for the ping-pong's slots): every wave runs one
+// software-pipelined loop over two slots per array; the P.V products of tile
+// t-1 run ahead of the vector work of tile t, with the copies of later tiles
+// issued between them, and the Q.K^T products of tile t+1 under the rescale,
+// the LDS stores and the barrier.  LDS layouts are unpadded, their 16-byte
+// chunks XOR-swizzled by row (conflict-free operand reads).  Each wave
+// quantises its Q rows in the prologue (the arithmetic of the quantisation
+// pass) straight into its Q8 operand registers, and keeps its Q16 operand in
+// registers too.
 //
 // Work decomposition: a workgroup of eight waves shares staged K/V tiles.  A
 // wave owns 32 query rows (16 for D = 256), so that the fp32 output
@@ -447,6 +447,8 @@ __global__ __launch_bounds__(kThreads, 1) void lamp_attn_kernel(AttnArgs a) {
 #pragma unroll
                 for (int qg = 0; qg < kQG; ++qg)
                     acc_o[qg][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb[qg], acc_o[qg][db], 0, 0, 0);
+                // one copy after every fourth output block
+                if ((db & 3) == 3) copy((h * C::kDB + db) >> 2);
             }
 #pragma unroll
             for (int qg = 0; qg < kQG; ++qg)
@@ -814,37 +816,50 @@ __global__ __launch_bounds__(kThreads, 1) void lamp_attn_kernel(AttnArgs a) {
         if (grp == 0) lds_barrier();
     } else {
         // ---- one software-pipelined loop (D = 256) ----------------------------------------
-        // Iteration t: copies of K8(t+1) and K16(t+1) into slot (t+1) & 1 and of
-        // V^T(t) into slot t & 1; P.V of tile t-1 (its products run under the
-        // vector work of tile t); max, exponentials and test of tile t; flag
-        // barrier; recompute of tile t; Q.K^T of tile t+1; rescale; barrier.
+        // Iteration t: copies of K8(t+1) into slot (t+1) & 1; P.V of tile t-1,
+        // with the copies of K16(t+1) into slot (t+1) & 1 and of V^T(t) into
+        // slot t & 1 issued between its products (one after every fourth output
+        // block: issued together at the top, they held every wave at the
+        // address unit); max, exponentials and test of tile t; flag barrier;
+        // recompute of tile t; Q.K^T of tile t+1; rescale; barrier.
         // The copies overwrite K8(t-1), K16(t-1) and V^T(t-2), whose last
         // readers (Q.K^T in iteration t-2, the recompute and P.V in iteration
         // t-1) are behind the previous barrier.  Each wave waits for its K8 copy
         // before the flag barrier (Q.K^T of t+1 follows it) and for the rest
         // before the closing barrier.  The 4-bit flag sets go through the first
         // bytes of K8 slot t & 1: K8(t) has been read, and K8(t+2) is copied
-        // there only after the closing barrier.
+        // there only after the closing barrier.  Waves 0-3 issue at a raised
+        // priority, so that the wave sharing their SIMD falls behind and runs
+        // its matrix products under their vector work rather than beside them.
         constexpr int kAfterK8 = kK16Ch + kVtCh;    // copies issued after a tile's K8 copies
         static_assert(kAfterK8 < 16, "vmcnt immediate");
+        static_assert(kAfterK8 == C::kDB / 2, "one copy per four output blocks of P.V");
         dma_qk(t_begin, t_begin & 1);
         dma_k16(t_begin, t_begin & 1);
         wait_copies();
         lds_barrier();
         if (work(t_begin)) qk(S, t_begin & 1);
         lds_barrier();   // every wave has read K8(t_begin): its slot takes the flags
+        if (wave_u < C::kWavesPerBlock) __builtin_amdgcn_s_setprio(3);
         for (int t = t_begin; t <= t_end; ++t) {
             const int sc = t & 1, sn = sc ^ 1;
-            if (t + 1 <= t_end) {
-                dma_qk(t + 1, sn);
-                dma_k16(t + 1, sn);
-            }
-            dma_vt(t, sc);
+            if (t + 1 <= t_end) dma_qk(t + 1, sn);
             const bool w_prev = work(t - 1), w_cur = work(t), w_next = work(t + 1);
             const bool full = full_tile(t);
-            // P.V of tile t-1 is issued first (it reads P before the exponentials
-            // of tile t overwrite it)
-            if (w_prev) pv(P, sn, [](int) {});
+            auto copy = [&](int k) __attribute__((always_inline)) {
+                if (k < kK16Ch) {
+                    if (t + 1 <= t_end) dma_k16_i(t + 1, sn, k);
+                } else if (k < kAfterK8) {
+                    dma_vt_i(t, sc, k - kK16Ch);
+                }
+            };
+            // P.V of tile t-1 reads P before the exponentials of tile t overwrite it
+            if (w_prev) {
+                pv(P, sn, copy);
+            } else {
+#pragma unroll
+                for (int k = 0; k < kAfterK8; ++k) copy(k);
+            }
             uint32_t flags = 0u;
             if (w_cur) {
                 round_logits(S);
@@ -879,6 +894,7 @@ __global__ __launch_bounds__(kThreads, 1) void lamp_attn_kernel(AttnArgs a) {
             wait_copies();
             lds_barrier();
         }
+        __builtin_amdgcn_s_setprio(0);
         // P.V of the last tile
         if (work(t_end)) pv(P, t_end & 1, [](int) {});
     }
