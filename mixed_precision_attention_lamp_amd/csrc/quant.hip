@@ -92,6 +92,21 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(
     const uint16_t* src = (is_q ? q : k) + (size_t)hs * S * D;
     uint8_t* dst = (is_q ? q8 : k8) + (size_t)hs * rows_out * D;
 
+    const bool codes = !(is_q && q8 == nullptr);
+    const int in_len = S * D;
+    const int out_len = rows_out * D;
+    const int begin = chunk * kChunk;
+    const int end = min(begin + kChunk, out_len);
+    // every load of the block's chunk is issued first: they do not depend on
+    // the scale, and their latency runs under the reduction of the maxima
+    constexpr int kPer = kChunk / (kThreads * 8);
+    u32x4 w[kPer];
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+        const int i = begin + (j * kThreads + (int)threadIdx.x) * 8;
+        w[j] = codes && i < in_len && i < end ? *reinterpret_cast<const u32x4*>(src + i) : u32x4{0u, 0u, 0u, 0u};
+    }
+
     uint32_t m = 0;
     for (int i = threadIdx.x; i < nch; i += kThreads) m = max(m, partial[(size_t)slab * nch + i]);
     m = block_max_u32(m, red);
@@ -106,20 +121,7 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(
         (is_q ? q_scale : k_scale)[hs] = scale;
         if (is_q && q_inv) q_inv[hs] = inv;
     }
-    if (is_q && q8 == nullptr) return;
-
-    const int in_len = S * D;
-    const int out_len = rows_out * D;
-    const int begin = chunk * kChunk;
-    const int end = min(begin + kChunk, out_len);
-    // every load of the block's chunk is issued before the first conversion
-    constexpr int kPer = kChunk / (kThreads * 8);
-    u32x4 w[kPer];
-#pragma unroll
-    for (int j = 0; j < kPer; ++j) {
-        const int i = begin + (j * kThreads + (int)threadIdx.x) * 8;
-        w[j] = i < in_len && i < end ? *reinterpret_cast<const u32x4*>(src + i) : u32x4{0u, 0u, 0u, 0u};
-    }
+    if (!codes) return;
 #pragma unroll
     for (int j = 0; j < kPer; ++j) {
         const int i = begin + (j * kThreads + (int)threadIdx.x) * 8;
