@@ -73,7 +73,9 @@ enum {
  *             Byte (b, hq, r, t): bit 7 = tile (query rows 64r.., keys 64t..) visited,
  *             bit c (0..3) = sub-block c (keys 64t+16c .. 64t+16c+15) recomputed in
  *             16-bit; 0 for tiles that hold no visible entry.
- * Sizes: B, Hq, Hkv, S >= 1; Hq % Hkv == 0; D in {64, 128, 256}; B*Hq*S*D < 2^31. */
+ * Sizes: B, Hq, Hkv, S >= 1; Hq % Hkv == 0; D in {64, 128, 256}; per head
+ * S_pad*D < 2^30 (S_pad = 64 nT); B*(Hq+2*Hkv)*nT < 2^29 (launch grids).  The
+ * tensors themselves may exceed 2^31 elements. */
 int lamp_attn_fwd(const void* q, const void* k, const void* v, float* out,
                   int B, int Hq, int Hkv, int S, int D,
                   int causal, int window, float delta, float tau,
@@ -174,7 +176,8 @@ int lamp_subblock_stats(const uint8_t* subblock_mask, int B, int Hq, int S,
  *   q [B,Hq,S,D], k [B,Hkv,S,D] bf16 device tensors as for lamp_attn_fwd.
  *   q8 [B,Hq,S,D], k8 [B,Hkv,S,D]: uint8 device outputs (e4m3fn codes, 16-byte
  *   aligned); q_scale [B*Hq], k_scale [B*Hkv]: fp32 device outputs (the scales).
- * Sizes and errors as lamp_attn_fwd; uses the workspace of the current stream. */
+ * Sizes and errors as lamp_attn_fwd, and B*(Hq+Hkv) <= 65535; uses the
+ * workspace of the current stream. */
 int lamp_quantize_qk(const void* q, const void* k, int B, int Hq, int Hkv, int S, int D,
                      uint8_t* q8, uint8_t* k8, float* q_scale, float* k_scale);
 

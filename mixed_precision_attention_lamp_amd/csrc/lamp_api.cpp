@@ -142,9 +142,14 @@ int check_sizes(int B, int Hq, int Hkv, int S, int D) {
     if (D != 64 && D != 128 && D != 256)
         return fail(LAMP_ERR_UNSUPPORTED, "head dimension D=%d (supported: 64, 128, 256)", D);
     const int64_t nT = ((int64_t)S + 63) / 64;   // 64-bit: S may be INT_MAX
-    if (product_reaches({B, Hq, nT * 64, D}, (int64_t)1 << 31))
-        return fail(LAMP_ERR_UNSUPPORTED, "B*Hq*S*D (S padded to 64) reaches 2^31 (B=%d Hq=%d S=%d D=%d)",
-                    B, Hq, S, D);
+    // Addresses across heads are 64-bit everywhere; within one (batch, head)
+    // slab the kernels use 32-bit offsets and buffer sizes of S_pad * 2D bytes,
+    // and the launches have at most B (Hq + 2 Hkv) nT (D / 64) workgroups.
+    if (product_reaches({nT * 64, D}, (int64_t)1 << 30))
+        return fail(LAMP_ERR_UNSUPPORTED, "S*D (S padded to 64) reaches 2^30 per head (S=%d D=%d)", S, D);
+    if (product_reaches({B, (int64_t)Hq + 2 * (int64_t)Hkv, nT}, (int64_t)1 << 29))
+        return fail(LAMP_ERR_UNSUPPORTED, "B*(Hq+2*Hkv)*ceil(S/64) reaches 2^29 (B=%d Hq=%d Hkv=%d S=%d)",
+                    B, Hq, Hkv, S);
     return LAMP_OK;
 }
 
@@ -551,6 +556,10 @@ int lamp_quantize_qk(const void* q, const void* k, int B, int Hq, int Hkv, int S
         return fail(LAMP_ERR_INVALID, "q, k, q8 and k8 must be 16-byte aligned");
     int rc = check_sizes(B, Hq, Hkv, S, D);
     if (rc != LAMP_OK) return rc;
+    // the maxima pass of this entry point runs one grid row per (batch, head)
+    if ((int64_t)B * ((int64_t)Hq + Hkv) > 65535)
+        return fail(LAMP_ERR_UNSUPPORTED, "lamp_quantize_qk needs B*(Hq+Hkv) <= 65535 (B=%d Hq=%d Hkv=%d)", B, Hq,
+                    Hkv);
     const lamp::Shape sh = make_shape(B, Hq, Hkv, S, D);
     const Layout L = workspace_layout(sh);
     void* ws = nullptr;

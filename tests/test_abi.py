@@ -60,7 +60,8 @@ def _fwd(lib, **kw):
     (dict(window=16, causal=0), -1, "window"),
     (dict(delta=math.nan), -1, "NaN"),
     (dict(tau=math.nan), -1, "NaN"),
-    (dict(B=64, Hq=64, Hkv=8, S=65536, D=128), -2, "2^31"),
+    (dict(Hq=1, Hkv=1, S=1 << 23, D=128), -2, "2^30"),        # one head: S*D = 2^30
+    (dict(B=1 << 20, Hq=512, Hkv=1, S=64, D=64), -2, "2^29"),  # launch grid
 ])
 def test_attn_validation(lib, kw, code, text):
     assert _fwd(lib, **kw) == code
@@ -69,6 +70,9 @@ def test_attn_validation(lib, kw, code, text):
 
 def test_other_entry_points_validate(lib):
     assert lib.lamp_quantize_qk(None, ALIGNED, 1, 1, 1, 64, 64, ALIGNED, ALIGNED, ALIGNED, ALIGNED) == -1
+    # the quantisation export's maxima pass: one grid row per (batch, head), at most 65535
+    assert lib.lamp_quantize_qk(ALIGNED, ALIGNED, 1000, 64, 8, 64, 64, ALIGNED, ALIGNED, ALIGNED, ALIGNED) == -2
+    assert "65535" in lamp.lamp_last_error()
     assert lib.lamp_subblock_stats(None, 1, 1, 64, 1, 0, ALIGNED) == -1
     assert lib.lamp_subblock_stats(ALIGNED, 1, 1, 64, 0, 8, ALIGNED) == -1
     assert lib.lamp_debug_convert(None, 10, None, None, None, None) == -1
