@@ -5,6 +5,7 @@
     python bench.py --copy-calibrate      # plain 1 GiB device copy (counter calibration)
     python bench.py --grid [--workload W] # speed/recompute curve over (delta, tau)
     python bench.py --workload qwen3-8b-decode   # split-KV decode (lamp_attn_decode)
+    python bench.py --workload qwen3-8b-decode --kept-amax   # decode with kept K maxima
 
 A step is one lamp_attn_fwd call (quantisation pass, V transpose and the fused
 attention kernel) over one batch of seeded synthetic input already resident
@@ -271,16 +272,23 @@ def decode_subblock_entries(Sq, Skv, causal, window):
     return vis.sum(axis=0).reshape(nT, 4, 16).sum(axis=2)
 
 
-def measure_decode(lamp, torch, tensors, shape, causal, window, delta, tau, tps, steps, warmup, settle_ms=0.0):
+def measure_decode(lamp, torch, tensors, shape, causal, window, delta, tau, tps, steps, warmup, settle_ms=0.0,
+                   kept=None):
     """Time `steps` lamp_attn_decode calls after `warmup`; returns the step
     time, the decode kernel time and the amax and scale pass time (HIP
     events on the library's stream; the merge of the splits is in the step
-    only), FLOP counts and the recompute counts."""
+    only), FLOP counts and the recompute counts.  With kept = (state, k_new)
+    a step folds the newest keys k_new into the kept K maxima and decodes with
+    them (lamp_kv_amax_update + lamp_attn_decode_with_amax)."""
     qd, kd, vd, out, mask = tensors
     B, Hq, Hkv, Sq, Skv, D = shape
 
     def step():
-        lamp.lamp_attn_decode(qd, kd, vd, out, causal, window, delta, tau, tps, mask)
+        if kept is None:
+            lamp.lamp_attn_decode(qd, kd, vd, out, causal, window, delta, tau, tps, mask)
+        else:
+            lamp.lamp_kv_amax_update(kept[1], kept[0])
+            lamp.lamp_attn_decode_with_amax(qd, kd, vd, out, kept[0], causal, window, delta, tau, tps, mask)
 
     settle(torch, step, settle_ms)
     for _ in range(warmup):
@@ -385,8 +393,15 @@ def run_decode(args, cfg, q, k, v):
     nT = lamp.n_tiles(Skv)
     out = torch.empty((B, Hq, Sq, D), dtype=torch.float32, device=dev)
     mask = torch.empty((B, Hq, nT), dtype=torch.uint8, device=dev)
+    kept = None
+    if args.kept_amax:
+        # the cache's kept K maxima, built once; each step folds in the Sq
+        # newest keys (the positions the queries sit at) and decodes
+        state = torch.zeros((B, Hkv), dtype=torch.int32, device=dev)
+        lamp.lamp_kv_amax_update(kd, state)
+        kept = (state, kd[:, :, Skv - Sq:].contiguous())
     m = measure_decode(lamp, torch, (qd, kd, vd, out, mask), (B, Hq, Hkv, Sq, Skv, D), causal, window,
-                       args.delta, args.tau, tps, args.steps, args.warmup, settle_ms=args.settle_ms)
+                       args.delta, args.tau, tps, args.steps, args.warmup, settle_ms=args.settle_ms, kept=kept)
     n_split = (nT + tps - 1) // tps
     # algorithmic bytes of the decode kernel: K and V read once (bf16), Q
     # read, the split results and the mask bytes written
@@ -413,7 +428,9 @@ def run_decode(args, cfg, q, k, v):
         "data": "synthetic",
         "config": {"workload": f"{args.workload}: {cfg['desc']}", "B": B, "Hq": Hq, "Hkv": Hkv,
                    "Sq": Sq, "Skv": Skv, "D": D, "causal": causal, "window": window,
-                   "delta": args.delta, "tau": args.tau, "tiles_per_split": tps, "splits": n_split},
+                   "delta": args.delta, "tau": args.tau, "tiles_per_split": tps, "splits": n_split,
+                   "k_scales": "kept maxima, the Sq newest keys folded in per step" if args.kept_amax
+                   else "amax pass over the cache per step"},
         "roofline": {"bound": "hbm", "achieved": achieved / 1e9, "peak": PEAK_HBM / 1e9, "unit": "GB/s",
                      "frac": achieved / PEAK_HBM, "traffic": traffic},
         "kernel_ms": {"decode": m["attn_ms"], "amax_and_scales": m["prep_ms"]},
@@ -535,6 +552,8 @@ def main():
     ap.add_argument("--settle-ms", type=float, default=300.0,
                     help="run the step this long before the warm-up steps (clock settling)")
     ap.add_argument("--copy-calibrate", action="store_true")
+    ap.add_argument("--kept-amax", action="store_true",
+                    help="decode workloads: K scales from kept maxima (lamp_attn_decode_with_amax)")
     ap.add_argument("--grid", action="store_true",
                     help="time the (delta, tau) grid and the two endpoints instead of one point")
     args = ap.parse_args()

@@ -138,6 +138,37 @@ int lamp_attn_decode(const void* q, const void* k, const void* v, float* out,
                      int causal, int window, float delta, float tau,
                      int tiles_per_split, uint8_t* subblock_mask_out);
 
+/* lamp_attn_decode with the per-head K scales taken from kept maxima instead of
+ * a pass over all Skv cached keys ("LampAttention", abstract: 8-bit formats
+ * for the key-query products; the scale of a K head is its largest magnitude
+ * over 448).  A serving loop keeps, per (batch, kv head), the largest bf16
+ * magnitude of the keys in its cache, folding in each appended key with
+ * lamp_kv_amax_update; the scales, and so the results, are then those of
+ * lamp_attn_decode bit for bit.
+ *   k_amax_state  uint32 device array [B * Hkv], 4-byte aligned: per (batch,
+ *             kv head) the largest magnitude bits (bf16 bits & 0x7FFF) over all
+ *             Skv cached keys, as lamp_kv_amax_update leaves it.  Read only.
+ * Other arguments, layout, sizes and errors as lamp_attn_decode. */
+int lamp_attn_decode_with_amax(const void* q, const void* k, const void* v, float* out,
+                               int B, int Hq, int Hkv, int Sq, int Skv, int D,
+                               int causal, int window, float delta, float tau,
+                               int tiles_per_split, const uint32_t* k_amax_state,
+                               uint8_t* subblock_mask_out);
+
+/* Folds new keys into kept K maxima (the state lamp_attn_decode_with_amax
+ * reads): k_amax_state[b * Hkv + h] becomes the larger of itself and the
+ * largest bf16 magnitude bits (bits & 0x7FFF) of k_new[b, h, :, :].  The
+ * caller zero-fills the state of an empty cache.  Integer maxima are exact and
+ * independent of order, so passing a cache's keys in any number of pieces
+ * leaves the amax of all of them.
+ *   k_new     bf16 device tensor [B, Hkv, S_new, D], 16-byte aligned.
+ *   k_amax_state  uint32 device array [B * Hkv], 4-byte aligned, updated in place.
+ * Sizes: B, Hkv, S_new >= 1; D in {64, 128, 256}; S_new*D < 2^30; B*Hkv <= 65535
+ * (LAMP_ERR_UNSUPPORTED otherwise).  Calls that update one state on different
+ * streams race only in the order of their updates, not in the result. */
+int lamp_kv_amax_update(const void* k_new, int B, int Hkv, int S_new, int D,
+                        uint32_t* k_amax_state);
+
 /* The tiles_per_split lamp_attn_decode uses when passed 0: the fewest tiles per
  * split that still give one workgroup slot of the current device a split (two
  * per compute unit, one when Hq/Hkv > 4 or D = 256); a negative error code for

@@ -9,6 +9,7 @@ package only marshals torch tensors into the C entry points (see _lib.py) and
 allocates outputs.
 """
 from ._lib import (LAMP_STATS_LEN, LampError, declared_symbols, lamp_attn_decode,  # noqa: F401
+                   lamp_attn_decode_with_amax, lamp_kv_amax_update,
                    lamp_attn_fwd, lamp_attn_fwd_bf16, lamp_attn_fwd_logit8, lamp_attn_fwd_noalloc, lamp_debug_attn_dump,
                    lamp_decode_tiles_per_split, lamp_debug_fp8_dot,
                    lamp_debug_attn_dump_logit8, lamp_debug_convert, lamp_last_error,

@@ -49,6 +49,11 @@ def load():
     lib.lamp_attn_decode.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, i32, f32, f32,
                                      i32, vp]
     lib.lamp_attn_decode.restype = i32
+    lib.lamp_attn_decode_with_amax.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, i32, f32,
+                                               f32, i32, vp, vp]
+    lib.lamp_attn_decode_with_amax.restype = i32
+    lib.lamp_kv_amax_update.argtypes = [vp, i32, i32, i32, i32, vp]
+    lib.lamp_kv_amax_update.restype = i32
     lib.lamp_decode_tiles_per_split.argtypes = [i32, i32, i32, i32, i32, i32]
     lib.lamp_decode_tiles_per_split.restype = i32
     lib.lamp_attn_fwd_bf16.restype = i32
@@ -258,6 +263,50 @@ def lamp_attn_decode(q, k, v, out, causal=1, window=0, delta=2.0 ** -8, tau=2.0 
     _check(lib.lamp_attn_decode(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, Hq, Hkv, Sq, Skv, D,
                                 int(causal), int(window), float(delta), float(tau),
                                 int(tiles_per_split), _ptr(subblock_mask_out)))
+
+
+def lamp_attn_decode_with_amax(q, k, v, out, k_amax_state, causal=1, window=0, delta=2.0 ** -8,
+                               tau=2.0 ** -1, tiles_per_split=0, subblock_mask_out=None):
+    """lamp_attn_decode with the K scales from kept maxima: k_amax_state is an
+    int32 (uint32 bits) device tensor [B, Hkv] as lamp_kv_amax_update leaves it."""
+    import torch
+    lib = load()
+    if q is None or not isinstance(q, torch.Tensor) or q.dim() != 4:
+        _invalid("q must be a 4-d tensor [B, Hq, Sq, D]")
+    if k is None or not isinstance(k, torch.Tensor) or k.dim() != 4:
+        _invalid("k must be a 4-d tensor [B, Hkv, Skv, D]")
+    B, Hq, Sq, D = q.shape
+    Hkv, Skv = k.shape[1], k.shape[2]
+    _expect(q, "q", torch.bfloat16, (B, Hq, Sq, D))
+    _expect(k, "k", torch.bfloat16, (B, Hkv, Skv, D))
+    _expect(v, "v", torch.bfloat16, (B, Hkv, Skv, D))
+    if Hkv < 1 or Hq % Hkv != 0:
+        _invalid(f"Hq ({Hq}) must be a multiple of Hkv ({Hkv})")
+    _expect(out, "out", torch.float32, (B, Hq, Sq, D))
+    _expect(k_amax_state, "k_amax_state", torch.int32, (B, Hkv))
+    if subblock_mask_out is not None:
+        _expect(subblock_mask_out, "subblock_mask_out", torch.uint8, (B, Hq, _n_tiles(Skv)))
+    _on_gpu([("q", q), ("k", k), ("v", v), ("out", out), ("k_amax_state", k_amax_state),
+             ("subblock_mask_out", subblock_mask_out)])
+    _sync_stream(lib)
+    _check(lib.lamp_attn_decode_with_amax(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, Hq, Hkv, Sq, Skv, D,
+                                          int(causal), int(window), float(delta), float(tau),
+                                          int(tiles_per_split), _ptr(k_amax_state), _ptr(subblock_mask_out)))
+
+
+def lamp_kv_amax_update(k_new, k_amax_state):
+    """Fold new keys k_new [B, Hkv, S_new, D] (bf16) into the kept maxima
+    k_amax_state [B, Hkv] (int32 device tensor holding uint32 bits)."""
+    import torch
+    lib = load()
+    if k_new is None or not isinstance(k_new, torch.Tensor) or k_new.dim() != 4:
+        _invalid("k_new must be a 4-d tensor [B, Hkv, S_new, D]")
+    B, Hkv, S_new, D = k_new.shape
+    _expect(k_new, "k_new", torch.bfloat16, (B, Hkv, S_new, D))
+    _expect(k_amax_state, "k_amax_state", torch.int32, (B, Hkv))
+    _on_gpu([("k_new", k_new), ("k_amax_state", k_amax_state)])
+    _sync_stream(lib)
+    _check(lib.lamp_kv_amax_update(_ptr(k_new), B, Hkv, S_new, D, _ptr(k_amax_state)))
 
 
 def lamp_decode_tiles_per_split(B, Hq, Hkv, Sq, Skv, D):

@@ -94,6 +94,18 @@ hipError_t launch_decode_scales(const DecodeShape& sh, const uint16_t* q, const 
                                 uint32_t* partial, float* q_scale, float* q_inv, float* k_scale,
                                 float* k_inv, hipStream_t st);
 
+// Kept K magnitudes: state[s] = max(state[s], max over slab s of k of the bf16
+// magnitude bits), for n_slabs slabs of slab_len values (one atomic max per
+// 8192-value chunk).
+hipError_t launch_kv_amax_update(const uint16_t* k, int n_slabs, int slab_len, uint32_t* state,
+                                 hipStream_t st);
+
+// The decode scales with the K maxima taken from kept state (B * Hkv values)
+// instead of a pass over K.
+hipError_t launch_decode_scales_kept(const DecodeShape& sh, const uint16_t* q, const uint32_t* k_amax,
+                                     float* q_scale, float* q_inv, float* k_scale, float* k_inv,
+                                     hipStream_t st);
+
 // The decode kernel (one workgroup per batch, kv head and split) and the merge
 // of the splits into out.
 // The decode kernel (split results into the workspace), then the merge of

@@ -371,6 +371,87 @@ static int attn_fwd_impl(const void* q, const void* k, const void* v, float* out
     return LAMP_OK;
 }
 
+// lamp_attn_decode, with the K scales from kept maxima (k_amax, B*Hkv values)
+// instead of a pass over K when k_amax is not null.
+static int decode_impl(const void* q, const void* k, const void* v, float* out, int B, int Hq, int Hkv,
+                       int Sq, int Skv, int D, int causal, int window, float delta, float tau,
+                       int tiles_per_split, const uint32_t* k_amax, uint8_t* subblock_mask_out) {
+    if (!q || !k || !v || !out) return fail(LAMP_ERR_INVALID, "q, k, v and out must be non-null");
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
+        return fail(LAMP_ERR_INVALID, "q, k, v and out must be 16-byte aligned");
+    int rc = check_decode(B, Hq, Hkv, Sq, Skv, D);
+    if (rc != LAMP_OK) return rc;
+    if (causal != 0 && causal != 1) return fail(LAMP_ERR_INVALID, "causal must be 0 or 1 (got %d)", causal);
+    if (window < 0) return fail(LAMP_ERR_INVALID, "window must be >= 0 (got %d)", window);
+    if (window > 0 && !causal) return fail(LAMP_ERR_INVALID, "a sliding window requires causal = 1");
+    if (std::isnan(delta) || std::isnan(tau)) return fail(LAMP_ERR_INVALID, "delta and tau must not be NaN");
+    if (tiles_per_split < 0)
+        return fail(LAMP_ERR_INVALID, "tiles_per_split must be >= 0 (got %d)", tiles_per_split);
+
+    lamp::DecodeShape sh;
+    sh.B = B; sh.Hq = Hq; sh.Hkv = Hkv; sh.Sq = Sq; sh.Skv = Skv; sh.D = D;
+    sh.nT = (Skv + 63) / 64;
+    sh.tps = tiles_per_split > 0 ? (tiles_per_split < sh.nT ? tiles_per_split : sh.nT)
+                                 : decode_tiles_per_split(B, Hq, Hkv, Skv, D);
+    if (sh.tps > kMaxTilesPerSplit)
+        return fail(LAMP_ERR_UNSUPPORTED, "tiles_per_split %d exceeds %d", sh.tps, kMaxTilesPerSplit);
+    sh.n_split = (sh.nT + sh.tps - 1) / sh.tps;
+
+    size_t off = 0;
+    auto take = [&](size_t bytes) { size_t o = off; off = round_up(off + bytes, 256); return o; };
+    const size_t o_partial = take(k_amax ? 0 : (size_t)B * Hkv * lamp::amax_chunks(Skv, D) * sizeof(uint32_t));
+    const size_t o_qs = take((size_t)B * Hq * sizeof(float));
+    const size_t o_qi = take((size_t)B * Hq * sizeof(float));
+    const size_t o_ks = take((size_t)B * Hkv * sizeof(float));
+    const size_t o_ki = take((size_t)B * Hkv * sizeof(float));
+    const size_t o_po = take((size_t)B * Hq * sh.n_split * Sq * D * sizeof(float));
+    const size_t o_ml = take((size_t)B * Hq * sh.n_split * Sq * 2 * sizeof(float));
+    void* ws = nullptr;
+    rc = get_workspace(off, &ws);
+    if (rc != LAMP_OK) return rc;
+    uint8_t* base = static_cast<uint8_t*>(ws);
+
+    lamp::DecodeParams p;
+    p.q16 = static_cast<const uint16_t*>(q);
+    p.k16 = static_cast<const uint16_t*>(k);
+    p.v16 = static_cast<const uint16_t*>(v);
+    p.q_scale = reinterpret_cast<float*>(base + o_qs);
+    p.q_inv = reinterpret_cast<float*>(base + o_qi);
+    p.k_scale = reinterpret_cast<float*>(base + o_ks);
+    p.k_inv = reinterpret_cast<float*>(base + o_ki);
+    p.part_o = reinterpret_cast<float*>(base + o_po);
+    p.part_ml = reinterpret_cast<float*>(base + o_ml);
+    p.out = out;
+    p.mask = subblock_mask_out;
+    p.log2e_over_sqrt_d = kLog2e / std::sqrt((double)D);
+    p.e_delta = exponential_threshold(delta);
+    p.t2 = (float)(16.0 * (double)tau * kLog2e);
+    p.causal = causal;
+    p.window = window;
+
+    hipEvent_t* ev = timing_slot();
+    if (ev) (void)hipEventRecord(ev[0], g_stream);
+    hipError_t e =
+        k_amax ? lamp::launch_decode_scales_kept(sh, p.q16, k_amax, reinterpret_cast<float*>(base + o_qs),
+                                                 reinterpret_cast<float*>(base + o_qi),
+                                                 reinterpret_cast<float*>(base + o_ks),
+                                                 reinterpret_cast<float*>(base + o_ki), g_stream)
+               : lamp::launch_decode_scales(sh, p.q16, p.k16, reinterpret_cast<uint32_t*>(base + o_partial),
+                                            reinterpret_cast<float*>(base + o_qs),
+                                            reinterpret_cast<float*>(base + o_qi),
+                                            reinterpret_cast<float*>(base + o_ks),
+                                            reinterpret_cast<float*>(base + o_ki), g_stream);
+    if (e != hipSuccess) return hip_fail(e, "decode scale launch");
+    if (ev) (void)hipEventRecord(ev[1], g_stream);
+    e = lamp::launch_decode(sh, p, g_stream);
+    if (e != hipSuccess) return hip_fail(e, "decode launch");
+    if (ev) timing_commit(ev);
+    e = lamp::launch_decode_merge(sh, p, g_stream);
+    if (e != hipSuccess) return hip_fail(e, "decode merge launch");
+    return LAMP_OK;
+}
+
+
 extern "C" {
 
 int lamp_attn_fwd(const void* q, const void* k, const void* v, float* out, int B, int Hq, int Hkv,
@@ -432,73 +513,38 @@ int lamp_decode_tiles_per_split(int B, int Hq, int Hkv, int Sq, int Skv, int D) 
 int lamp_attn_decode(const void* q, const void* k, const void* v, float* out, int B, int Hq, int Hkv,
                      int Sq, int Skv, int D, int causal, int window, float delta, float tau,
                      int tiles_per_split, uint8_t* subblock_mask_out) {
-    if (!q || !k || !v || !out) return fail(LAMP_ERR_INVALID, "q, k, v and out must be non-null");
-    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
-        return fail(LAMP_ERR_INVALID, "q, k, v and out must be 16-byte aligned");
-    int rc = check_decode(B, Hq, Hkv, Sq, Skv, D);
-    if (rc != LAMP_OK) return rc;
-    if (causal != 0 && causal != 1) return fail(LAMP_ERR_INVALID, "causal must be 0 or 1 (got %d)", causal);
-    if (window < 0) return fail(LAMP_ERR_INVALID, "window must be >= 0 (got %d)", window);
-    if (window > 0 && !causal) return fail(LAMP_ERR_INVALID, "a sliding window requires causal = 1");
-    if (std::isnan(delta) || std::isnan(tau)) return fail(LAMP_ERR_INVALID, "delta and tau must not be NaN");
-    if (tiles_per_split < 0)
-        return fail(LAMP_ERR_INVALID, "tiles_per_split must be >= 0 (got %d)", tiles_per_split);
+    return decode_impl(q, k, v, out, B, Hq, Hkv, Sq, Skv, D, causal, window, delta, tau, tiles_per_split,
+                       nullptr, subblock_mask_out);
+}
 
-    lamp::DecodeShape sh;
-    sh.B = B; sh.Hq = Hq; sh.Hkv = Hkv; sh.Sq = Sq; sh.Skv = Skv; sh.D = D;
-    sh.nT = (Skv + 63) / 64;
-    sh.tps = tiles_per_split > 0 ? (tiles_per_split < sh.nT ? tiles_per_split : sh.nT)
-                                 : decode_tiles_per_split(B, Hq, Hkv, Skv, D);
-    if (sh.tps > kMaxTilesPerSplit)
-        return fail(LAMP_ERR_UNSUPPORTED, "tiles_per_split %d exceeds %d", sh.tps, kMaxTilesPerSplit);
-    sh.n_split = (sh.nT + sh.tps - 1) / sh.tps;
+int lamp_attn_decode_with_amax(const void* q, const void* k, const void* v, float* out, int B, int Hq,
+                               int Hkv, int Sq, int Skv, int D, int causal, int window, float delta,
+                               float tau, int tiles_per_split, const uint32_t* k_amax_state,
+                               uint8_t* subblock_mask_out) {
+    if (!k_amax_state) return fail(LAMP_ERR_INVALID, "k_amax_state must be non-null");
+    if (reinterpret_cast<uintptr_t>(k_amax_state) % 4 != 0)
+        return fail(LAMP_ERR_INVALID, "k_amax_state must be 4-byte aligned");
+    return decode_impl(q, k, v, out, B, Hq, Hkv, Sq, Skv, D, causal, window, delta, tau, tiles_per_split,
+                       k_amax_state, subblock_mask_out);
+}
 
-    size_t off = 0;
-    auto take = [&](size_t bytes) { size_t o = off; off = round_up(off + bytes, 256); return o; };
-    const size_t o_partial = take((size_t)B * Hkv * lamp::amax_chunks(Skv, D) * sizeof(uint32_t));
-    const size_t o_qs = take((size_t)B * Hq * sizeof(float));
-    const size_t o_qi = take((size_t)B * Hq * sizeof(float));
-    const size_t o_ks = take((size_t)B * Hkv * sizeof(float));
-    const size_t o_ki = take((size_t)B * Hkv * sizeof(float));
-    const size_t o_po = take((size_t)B * Hq * sh.n_split * Sq * D * sizeof(float));
-    const size_t o_ml = take((size_t)B * Hq * sh.n_split * Sq * 2 * sizeof(float));
-    void* ws = nullptr;
-    rc = get_workspace(off, &ws);
-    if (rc != LAMP_OK) return rc;
-    uint8_t* base = static_cast<uint8_t*>(ws);
-
-    lamp::DecodeParams p;
-    p.q16 = static_cast<const uint16_t*>(q);
-    p.k16 = static_cast<const uint16_t*>(k);
-    p.v16 = static_cast<const uint16_t*>(v);
-    p.q_scale = reinterpret_cast<float*>(base + o_qs);
-    p.q_inv = reinterpret_cast<float*>(base + o_qi);
-    p.k_scale = reinterpret_cast<float*>(base + o_ks);
-    p.k_inv = reinterpret_cast<float*>(base + o_ki);
-    p.part_o = reinterpret_cast<float*>(base + o_po);
-    p.part_ml = reinterpret_cast<float*>(base + o_ml);
-    p.out = out;
-    p.mask = subblock_mask_out;
-    p.log2e_over_sqrt_d = kLog2e / std::sqrt((double)D);
-    p.e_delta = exponential_threshold(delta);
-    p.t2 = (float)(16.0 * (double)tau * kLog2e);
-    p.causal = causal;
-    p.window = window;
-
-    hipEvent_t* ev = timing_slot();
-    if (ev) (void)hipEventRecord(ev[0], g_stream);
-    hipError_t e = lamp::launch_decode_scales(sh, p.q16, p.k16, reinterpret_cast<uint32_t*>(base + o_partial),
-                                              reinterpret_cast<float*>(base + o_qs),
-                                              reinterpret_cast<float*>(base + o_qi),
-                                              reinterpret_cast<float*>(base + o_ks),
-                                              reinterpret_cast<float*>(base + o_ki), g_stream);
-    if (e != hipSuccess) return hip_fail(e, "decode scale launch");
-    if (ev) (void)hipEventRecord(ev[1], g_stream);
-    e = lamp::launch_decode(sh, p, g_stream);
-    if (e != hipSuccess) return hip_fail(e, "decode launch");
-    if (ev) timing_commit(ev);
-    e = lamp::launch_decode_merge(sh, p, g_stream);
-    if (e != hipSuccess) return hip_fail(e, "decode merge launch");
+int lamp_kv_amax_update(const void* k_new, int B, int Hkv, int S_new, int D, uint32_t* k_amax_state) {
+    if (!k_new || !k_amax_state) return fail(LAMP_ERR_INVALID, "k_new and k_amax_state must be non-null");
+    if (!aligned16(k_new)) return fail(LAMP_ERR_INVALID, "k_new must be 16-byte aligned");
+    if (reinterpret_cast<uintptr_t>(k_amax_state) % 4 != 0)
+        return fail(LAMP_ERR_INVALID, "k_amax_state must be 4-byte aligned");
+    if (B < 1 || Hkv < 1 || S_new < 1)
+        return fail(LAMP_ERR_INVALID, "sizes must be >= 1 (B=%d Hkv=%d S_new=%d)", B, Hkv, S_new);
+    if (D != 64 && D != 128 && D != 256)
+        return fail(LAMP_ERR_UNSUPPORTED, "head dimension D=%d (supported: 64, 128, 256)", D);
+    if (product_reaches({S_new, D}, (int64_t)1 << 30))
+        return fail(LAMP_ERR_UNSUPPORTED, "S_new*D reaches 2^30 (S_new=%d D=%d)", S_new, D);
+    // one grid row per (batch, kv head)
+    if ((int64_t)B * Hkv > 65535)
+        return fail(LAMP_ERR_UNSUPPORTED, "B*Hkv must be <= 65535 (B=%d Hkv=%d)", B, Hkv);
+    hipError_t e = lamp::launch_kv_amax_update(static_cast<const uint16_t*>(k_new), B * Hkv, S_new * D,
+                                               k_amax_state, g_stream);
+    if (e != hipSuccess) return hip_fail(e, "amax update launch");
     return LAMP_OK;
 }
 

@@ -72,6 +72,27 @@ __global__ __launch_bounds__(kThreads) void amax_kernel(const uint16_t* __restri
     amax_block(q, k, partial, n_q_slabs, slab_len, nch, blockIdx.y, blockIdx.x, red);
 }
 
+// Kept K magnitudes of a KV cache: state[slab] becomes the larger of itself
+// and the largest bf16 magnitude (bits & 0x7FFF, the integer the amax pass
+// reduces) of the slab's new keys.  blockIdx.y = slab, blockIdx.x = chunk;
+// one atomic max per block.  Integer maxima do not depend on their order, so
+// the state equals the amax of every key passed so far, exactly.
+__global__ __launch_bounds__(kThreads) void amax_update_kernel(const uint16_t* __restrict__ k,
+                                                               uint32_t* __restrict__ state, int slab_len) {
+    __shared__ uint32_t red[kThreads / 64];
+    const uint16_t* src = k + (size_t)blockIdx.y * slab_len;
+    const int begin = blockIdx.x * kChunk;
+    const int end = min(begin + kChunk, slab_len);
+    uint32_t m = 0;
+#pragma unroll
+    for (int j = 0; j < kChunk / (kThreads * 8); ++j) {
+        const int i = begin + (j * kThreads + (int)threadIdx.x) * 8;
+        if (i < end) m = max(m, max_bf16_mag(*reinterpret_cast<const u32x4*>(src + i)));
+    }
+    m = block_max_u32(m, red);
+    if (threadIdx.x == 0) atomicMax(state + blockIdx.y, m);
+}
+
 // One block per (slab, output chunk), slab-major: Q slabs first with
 // q_chunks blocks each, then K slabs with k_chunks each.  Output slabs have
 // rows_out rows of D codes; rows >= S are written as zero.  With q8 null
@@ -306,6 +327,23 @@ hipError_t launch_decode_scales(const DecodeShape& sh, const uint16_t* q, const 
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(decode_scales_kernel, dim3(nq + nk), dim3(kThreads), 0, st, q, partial, q_scale, q_inv,
                        k_scale, k_inv, nq, sh.Sq * sh.D, nch);
+    return hipGetLastError();
+}
+
+hipError_t launch_kv_amax_update(const uint16_t* k, int n_slabs, int slab_len, uint32_t* state,
+                                 hipStream_t st) {
+    const int nch = (slab_len + kChunk - 1) / kChunk;
+    hipLaunchKernelGGL(amax_update_kernel, dim3(nch, n_slabs), dim3(kThreads), 0, st, k, state, slab_len);
+    return hipGetLastError();
+}
+
+hipError_t launch_decode_scales_kept(const DecodeShape& sh, const uint16_t* q, const uint32_t* k_amax,
+                                     float* q_scale, float* q_inv, float* k_scale, float* k_inv,
+                                     hipStream_t st) {
+    const int nq = sh.B * sh.Hq, nk = sh.B * sh.Hkv;
+    // the kept maxima stand in for the partial maxima, one per K slab
+    hipLaunchKernelGGL(decode_scales_kernel, dim3(nq + nk), dim3(kThreads), 0, st, q, k_amax, q_scale, q_inv,
+                       k_scale, k_inv, nq, sh.Sq * sh.D, 1);
     return hipGetLastError();
 }
 

@@ -76,6 +76,18 @@ def test_other_entry_points_validate(lib):
     assert lib.lamp_subblock_stats(None, 1, 1, 64, 1, 0, ALIGNED) == -1
     assert lib.lamp_subblock_stats(ALIGNED, 1, 1, 64, 0, 8, ALIGNED) == -1
     assert lib.lamp_debug_convert(None, 10, None, None, None, None) == -1
+    # kept K maxima: null or misaligned state, bad sizes (before any HIP call)
+    assert lib.lamp_kv_amax_update(ALIGNED, 1, 1, 64, 128, None) == -1
+    assert lib.lamp_kv_amax_update(ALIGNED, 1, 1, 64, 128, ALIGNED + 2) == -1
+    assert lib.lamp_kv_amax_update(ALIGNED + 2, 1, 1, 64, 128, ALIGNED) == -1
+    assert lib.lamp_kv_amax_update(ALIGNED, 0, 1, 64, 128, ALIGNED) == -1
+    assert lib.lamp_kv_amax_update(ALIGNED, 1, 1, 64, 96, ALIGNED) == -2
+    assert lib.lamp_kv_amax_update(ALIGNED, 1, 1, 1 << 23, 128, ALIGNED) == -2
+    assert lib.lamp_kv_amax_update(ALIGNED, 300, 300, 64, 128, ALIGNED) == -2
+    assert lib.lamp_attn_decode_with_amax(ALIGNED, ALIGNED, ALIGNED, ALIGNED, 1, 4, 1, 8, 100, 128, 1, 0,
+                                          2.0 ** -8, 0.5, 0, None, None) == -1
+    assert lib.lamp_attn_decode_with_amax(ALIGNED, ALIGNED, ALIGNED, ALIGNED, 1, 4, 1, 17, 100, 128, 1, 0,
+                                          2.0 ** -8, 0.5, 0, ALIGNED, None) == -2
     assert lib.lamp_debug_convert(None, 0, None, None, None, None) == 0
     assert lib.lamp_set_stream(None) == 0
 

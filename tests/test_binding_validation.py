@@ -90,3 +90,29 @@ def test_dump_stats_quantize_convert_rejections():
                               torch.zeros(B * HQ), torch.zeros(B * HKV))
     with pytest.raises(LampError, match="exp2 must have shape"):
         lamp.lamp_debug_convert(torch.zeros(10), exp2=torch.zeros(9))
+
+
+def test_kept_amax_rejections():
+    Sq, Skv = 4, 100
+    q = torch.zeros(B, HQ, Sq, D, dtype=torch.bfloat16)
+    k = torch.zeros(B, HKV, Skv, D, dtype=torch.bfloat16)
+    out = torch.zeros(B, HQ, Sq, D, dtype=torch.float32)
+    state = torch.zeros(B, HKV, dtype=torch.int32)
+
+    def rejects(match, fn, *args):
+        with pytest.raises(LampError, match=match) as e:
+            fn(*args)
+        assert e.value.code == LAMP_ERR_INVALID
+
+    rejects("k_amax_state must have dtype", lamp.lamp_attn_decode_with_amax, q, k, k, out,
+            torch.zeros(B, HKV, dtype=torch.int64))
+    rejects("k_amax_state must have shape", lamp.lamp_attn_decode_with_amax, q, k, k, out,
+            torch.zeros(B, HKV + 1, dtype=torch.int32))
+    rejects("k_amax_state must not be None", lamp.lamp_attn_decode_with_amax, q, k, k, out, None)
+    rejects("v must have shape", lamp.lamp_attn_decode_with_amax, q, k, k[:, :, :50].contiguous(), out, state)
+    rejects("must be on a GPU", lamp.lamp_attn_decode_with_amax, q, k, k, out, state)
+    rejects("k_new must have dtype", lamp.lamp_kv_amax_update, k.float(), state)
+    rejects("k_amax_state must have shape", lamp.lamp_kv_amax_update, k, torch.zeros(B, dtype=torch.int32))
+    rejects("k_new must be contiguous", lamp.lamp_kv_amax_update, k.transpose(2, 3).contiguous().transpose(2, 3),
+            state)
+    rejects("must be on a GPU", lamp.lamp_kv_amax_update, k, state)

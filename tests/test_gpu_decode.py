@@ -104,3 +104,53 @@ def test_decode_full_size():
     assert_parity_decode(compare_decode(q, k, v, 1, 0, 2 ** -8, 2 ** -1, tps, heads=heads,
                                         gpu=(out.cpu().numpy(), mask.cpu().numpy()),
                                         label=f"qwen3-8b-decode sampled, {tps} tiles per split"))
+
+
+KEPT = [
+    # B, Hq, Hkv, Sq, Skv, D, causal, window, pieces of the cache, structure, seed
+    (2, 8, 2, 16, 3000, 128, 1, 0, (1000, 1984, 16), "channels", 231),
+    (1, 4, 1, 1, 777, 64, 1, 0, (777,), "channels", 232),
+    (1, 8, 4, 5, 1300, 256, 1, 400, (1, 650, 649), "sinks", 233),
+]
+
+
+@pytest.mark.parametrize("case", KEPT)
+def test_decode_with_kept_amax(case):
+    """Kept K maxima, folded in from the cache in pieces, equal the oracle's
+    per-head amax; decode with them equals lamp_attn_decode bit for bit, and
+    folding in the newest keys again changes nothing."""
+    import mixed_precision_attention_lamp_amd as lamp
+    B, Hq, Hkv, Sq, Skv, D, causal, window, pieces, st, seed = case
+    assert sum(pieces) == Skv
+    q, k, v = make_inputs(B, Hq, Hkv, Skv, D, seed, st, Sq=Sq)
+    qd, kd, vd = to_device(q), to_device(k), to_device(v)
+    state = torch.zeros((B, Hkv), dtype=torch.int32, device="cuda")
+    start = 0
+    for n in pieces:
+        lamp.lamp_kv_amax_update(kd[:, :, start:start + n].contiguous(), state)
+        start += n
+    torch.cuda.synchronize()
+    # the oracle's per-head scales come from the same maxima
+    scale, _ = L.head_scales(k)
+    kept = state.cpu().numpy().astype(np.uint32)
+    amax = (kept.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    assert np.array_equal(np.where(amax > 0, (amax / 448.0).astype(np.float32), np.float32(1.0)),
+                          np.asarray(scale, dtype=np.float32).reshape(B, Hkv))
+    nT = L.n_tiles(Skv)
+    res = []
+    for fn in ("full", "kept"):
+        out = torch.full((B, Hq, Sq, D), float("nan"), dtype=torch.float32, device="cuda")
+        mask = torch.full((B, Hq, nT), 0x55, dtype=torch.uint8, device="cuda")
+        if fn == "full":
+            lamp.lamp_attn_decode(qd, kd, vd, out, causal, window, 2 ** -8, 2 ** -1, 0, mask)
+        else:
+            lamp.lamp_attn_decode_with_amax(qd, kd, vd, out, state, causal, window, 2 ** -8, 2 ** -1, 0, mask)
+        torch.cuda.synchronize()
+        res.append((out.cpu().numpy(), mask.cpu().numpy()))
+    lamp.lamp_kv_amax_update(kd[:, :, Skv - Sq:].contiguous(), state)
+    torch.cuda.synchronize()
+    again = np.array_equal(state.cpu().numpy().astype(np.uint32), kept)
+    say(f"[decode-kept] {case}: scales equal the oracle's; outputs equal {np.array_equal(res[0][0], res[1][0])}, "
+        f"masks equal {np.array_equal(res[0][1], res[1][1])}, state unchanged by the newest keys {again}")
+    assert np.isfinite(res[0][0]).all()
+    assert np.array_equal(res[0][0], res[1][0]) and np.array_equal(res[0][1], res[1][1]) and again
