@@ -78,6 +78,21 @@ for args in [(1, 4, 1, 16, 16384, 128), (0, 4, 1, 16, 100, 128), (1, 4, 1, 16, I
              (INT_MAX, INT_MAX, 1, 16, INT_MAX, 256)]:
     lib.lamp_decode_tiles_per_split(*[I(x) for x in args])
 
+# kept K maxima and decode with them
+for (B, Hkv, S, D) in [(0, 1, 64, 128), (1, 0, 64, 128), (1, 1, 0, 128), (1, 1, 64, 96), (1, 1, INT_MAX, 128),
+                       (INT_MAX, INT_MAX, 64, 128), (300, 300, 64, 128)]:
+    call("lamp_kv_amax_update", VP(b0), I(B), I(Hkv), I(S), I(D), VP(b0), expect="fail")
+call("lamp_kv_amax_update", VP(None), I(1), I(1), I(64), I(128), VP(b0), expect="fail")
+call("lamp_kv_amax_update", VP(b0), I(1), I(1), I(64), I(128), VP(b0 + 2), expect="fail")
+call("lamp_kv_amax_update", VP(b0), I(2), I(4), I(100), I(128), VP(b0))
+for state in [None, b0 + 2]:
+    call("lamp_attn_decode_with_amax", VP(b0), VP(b0), VP(b0), VP(b0), I(1), I(4), I(1), I(8), I(100), I(128),
+         I(1), I(0), F(2 ** -8), F(0.5), I(0), VP(state), VP(b0), expect="fail")
+call("lamp_attn_decode_with_amax", VP(b0), VP(b0), VP(b0), VP(b0), I(1), I(4), I(1), I(17), I(100), I(128),
+     I(1), I(0), F(2 ** -8), F(0.5), I(0), VP(b0), VP(b0), expect="fail")
+call("lamp_attn_decode_with_amax", VP(b0), VP(b0), VP(b0), VP(b0), I(2), I(8), I(2), I(16), I(3000), I(128),
+     I(1), I(0), F(2 ** -8), F(0.5), I(0), VP(b0), VP(b0))
+
 # statistics, quantisation, hooks
 for (B, Hq, S) in [(0, 1, 64), (1, 1, 0), (1, 1, INT_MAX), (INT_MAX, INT_MAX, 64)]:
     call("lamp_subblock_stats", VP(b0), I(B), I(Hq), I(S), I(1), I(0), VP(b0), expect="fail")
