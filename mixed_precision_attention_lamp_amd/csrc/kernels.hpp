@@ -96,7 +96,7 @@ hipError_t launch_decode_scales(const DecodeShape& sh, const uint16_t* q, const 
 
 // Kept K magnitudes: state[s] = max(state[s], max over slab s of k of the bf16
 // magnitude bits), for n_slabs slabs of slab_len values (one atomic max per
-// 8192-value chunk).
+// 16384-value chunk).
 hipError_t launch_kv_amax_update(const uint16_t* k, int n_slabs, int slab_len, uint32_t* state,
                                  hipStream_t st);
 

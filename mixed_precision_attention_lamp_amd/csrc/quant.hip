@@ -19,7 +19,7 @@ namespace lamp {
 
 namespace {
 
-constexpr int kChunk = 8192;       // bf16 values per amax / quantise block (4 loads per thread)
+constexpr int kChunk = 16384;      // bf16 values per amax / quantise block (8 loads per thread)
 constexpr int kThreads = 256;
 
 __device__ __forceinline__ uint32_t max_bf16_mag(u32x4 w) {
