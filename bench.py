@@ -523,8 +523,7 @@ def roofline_of(m):
 def run_grid(args, lamp, torch, tensors, shape, causal, window, cfg):
     """One JSON line per (delta, tau) of the grid and per endpoint."""
     runs = [(d, t, "") for d in GRID_DELTAS for t in GRID_TAUS] + list(GRID_ENDPOINTS)
-    if shape[4] <= 128:
-        runs.append((0.0, 0.0, PLAIN_NOTE))
+    runs.append((0.0, 0.0, PLAIN_NOTE))
     runs += [(d, t, LOGIT8_NOTE) for d, t in LOGIT8_POINTS]
     for delta, tau, note in runs:
         m = measure(lamp, torch, tensors, shape, causal, window, delta, tau, args.steps, args.warmup,

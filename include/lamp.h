@@ -181,7 +181,7 @@ int lamp_decode_tiles_per_split(int B, int Hq, int Hkv, int Sq, int Skv, int D);
  * from them, exponentials are rounded to bf16, and P.V runs in bf16 with fp32
  * accumulation.  Arguments, layout and errors as lamp_attn_fwd without delta
  * and tau; subblock_mask_out gets 0x8F for every visited tile (all four
- * sub-blocks in 16-bit).  D in {64, 128} (LAMP_ERR_UNSUPPORTED otherwise). */
+ * sub-blocks in 16-bit).  Sizes as lamp_attn_fwd (D in {64, 128, 256}). */
 int lamp_attn_fwd_bf16(const void* q, const void* k, const void* v, float* out,
                        int B, int Hq, int Hkv, int S, int D,
                        int causal, int window, uint8_t* subblock_mask_out);

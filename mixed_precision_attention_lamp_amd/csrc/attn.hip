@@ -122,7 +122,7 @@ struct Cfg {
 // kMode: 0 = no test (second stage off), 1 = both stages, 2 = second stage
 // only, 3 = plain bf16 FlashAttention (the 16-bit baseline: no 8-bit pass,
 // Q.K^T of every sub-block on the bf16 matrix cores, exponentials rounded to
-// bf16; ping-pong schedule only); 4 + (0, 1, 2): the test modes 0-2 with
+// bf16; at D = 256 its K16 tiles take the K8 slots); 4 + (0, 1, 2): the test modes 0-2 with
 // 8-bit logits (the log2-domain logit c8 acc itself rounded to e4m3 before the
 // running max, the exponentials and the test read it); 9: mode 1 with the
 // per-entry test in vector form (for small tau, where most waves need it).
@@ -133,7 +133,6 @@ __global__ __launch_bounds__(kThreads, 1) void lamp_attn_kernel(AttnArgs a) {
     constexpr bool kDense = (kMode & 8) != 0;
     constexpr int kTest = kMode & 3;
     using C = Cfg<D, kPlain>;
-    static_assert(!kPlain || C::kPP, "the plain bf16 mode runs on the ping-pong schedule");
     constexpr int kQG = C::kQG;
     constexpr int kWaveRows = C::kWaveRows;
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
@@ -831,11 +830,14 @@ __global__ __launch_bounds__(kThreads, 1) void lamp_attn_kernel(AttnArgs a) {
         // there only after the closing barrier.  Waves 0-3 issue at a raised
         // priority, so that the wave sharing their SIMD falls behind and runs
         // its matrix products under their vector work rather than beside them.
-        constexpr int kAfterK8 = kK16Ch + kVtCh;    // copies issued after a tile's K8 copies
+        // (the plain bf16 mode stages its Q.K^T operand, K16, in the K8 slots
+        // and copies no separate K16 tiles)
+        constexpr int kK16Copies = kPlain ? 0 : kK16Ch;
+        constexpr int kAfterK8 = kK16Copies + kVtCh;    // copies issued after a tile's K8 copies
         static_assert(kAfterK8 < 16, "vmcnt immediate");
-        static_assert(kAfterK8 == C::kDB / 2, "one copy per four output blocks of P.V");
+        static_assert(kAfterK8 <= C::kDB / 2, "one copy per four output blocks of P.V");
         dma_qk(t_begin, t_begin & 1);
-        dma_k16(t_begin, t_begin & 1);
+        if constexpr (!kPlain) dma_k16(t_begin, t_begin & 1);
         wait_copies();
         lds_barrier();
         if (work(t_begin)) qk(S, t_begin & 1);
@@ -847,10 +849,11 @@ __global__ __launch_bounds__(kThreads, 1) void lamp_attn_kernel(AttnArgs a) {
             const bool w_prev = work(t - 1), w_cur = work(t), w_next = work(t + 1);
             const bool full = full_tile(t);
             auto copy = [&](int k) __attribute__((always_inline)) {
-                if (k < kK16Ch) {
-                    if (t + 1 <= t_end) dma_k16_i(t + 1, sn, k);
+                if (k < kK16Copies) {
+                    if constexpr (!kPlain)
+                        if (t + 1 <= t_end) dma_k16_i(t + 1, sn, k);
                 } else if (k < kAfterK8) {
-                    dma_vt_i(t, sc, k - kK16Ch);
+                    dma_vt_i(t, sc, k - kK16Copies);
                 }
             };
             // P.V of tile t-1 reads P before the exponentials of tile t overwrite it
@@ -865,7 +868,8 @@ __global__ __launch_bounds__(kThreads, 1) void lamp_attn_kernel(AttnArgs a) {
                 round_logits(S);
                 if (full) softmax(S, P, t, kFull);
                 else softmax(S, P, t, kPart);
-                flags = full ? test(S, kFull) : test(S, kPart);
+                if constexpr (kPlain) flags = 0xFu;   // every sub-block in 16-bit
+                else flags = full ? test(S, kFull) : test(S, kPart);
             }
             // the waves of a 64-row block OR their flags
             uint32_t* flag_slot = reinterpret_cast<uint32_t*>(lds + C::kK8Off + sc * C::kQKBytes);
@@ -878,9 +882,11 @@ __global__ __launch_bounds__(kThreads, 1) void lamp_attn_kernel(AttnArgs a) {
 #pragma unroll
             for (int w = 0; w < C::kWavesPerBlock; ++w) flags |= flag_slot[blk * C::kWavesPerBlock + w];
             flags = __builtin_amdgcn_readfirstlane(flags);
-            if (w_cur && flags != 0) {
-                if (full) recompute(P, flags, kFull, sc);
-                else recompute(P, flags, kPart, sc);
+            if constexpr (!kPlain) {
+                if (w_cur && flags != 0) {
+                    if (full) recompute(P, flags, kFull, sc);
+                    else recompute(P, flags, kPart, sc);
+                }
             }
             // Q.K^T of tile t+1 runs on the matrix cores under what follows
             if (w_next) qk(S, sn);
@@ -959,12 +965,8 @@ hipError_t launch_d(const Shape& sh, const AttnParams& p, hipStream_t st) {
     if (!p.logit8 && !p.plain && a.test_mode == 1 && a.t2 + a.x_delta <= -5.0f)
         fn = dump ? lamp_attn_kernel<D, true, 9> : lamp_attn_kernel<D, false, 9>;
     if (p.plain) {
-        if constexpr (Cfg<D>::kPP) {
-            fn = dump ? lamp_attn_kernel<D, true, 3> : lamp_attn_kernel<D, false, 3>;
-            lds = Cfg<D, true>::kLdsBytes;
-        } else {
-            return hipErrorInvalidValue;
-        }
+        fn = dump ? lamp_attn_kernel<D, true, 3> : lamp_attn_kernel<D, false, 3>;
+        lds = Cfg<D, true>::kLdsBytes;
     }
     hipError_t e = hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;

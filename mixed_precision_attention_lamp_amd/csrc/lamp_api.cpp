@@ -312,7 +312,6 @@ static int attn_fwd_impl(const void* q, const void* k, const void* v, float* out
     if (window > 0 && !causal) return fail(LAMP_ERR_INVALID, "a sliding window requires causal = 1");
     if (!plain && (std::isnan(delta) || std::isnan(tau)))
         return fail(LAMP_ERR_INVALID, "delta and tau must not be NaN");
-    if (plain && D > 128) return fail(LAMP_ERR_UNSUPPORTED, "the plain bf16 mode needs D <= 128 (got %d)", D);
 
     const lamp::Shape sh = make_shape(B, Hq, Hkv, S, D);
     const Layout L = workspace_layout(sh);

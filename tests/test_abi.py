@@ -111,10 +111,9 @@ def test_binding_raises_on_error():
 
 
 def test_bf16_baseline_rejects_before_hip(lib):
-    # D = 256 is not supported by the plain bf16 baseline; a bad size is
-    # rejected as for lamp_attn_fwd; neither touches the GPU
-    assert lib.lamp_attn_fwd_bf16(ALIGNED, ALIGNED, ALIGNED, ALIGNED, 1, 2, 1, 128, 256, 1, 0, None) == -2
-    assert "D <= 128" in lib.lamp_last_error().decode()
+    # bad sizes are rejected as for lamp_attn_fwd, before any HIP call
+    assert lib.lamp_attn_fwd_bf16(ALIGNED, ALIGNED, ALIGNED, ALIGNED, 1, 2, 1, 128, 96, 1, 0, None) == -2
+    assert "D=96" in lib.lamp_last_error().decode()
     assert lib.lamp_attn_fwd_bf16(ALIGNED, ALIGNED, ALIGNED, ALIGNED, 1, 3, 2, 128, 128, 1, 0, None) == -1
 
 

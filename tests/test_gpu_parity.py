@@ -326,6 +326,9 @@ PLAIN = [
     (1, 3, 3, 130, 64, 0, 0, "channels", 84),      # non-causal
     (1, 2, 2, 333, 128, 1, 100, "channels", 85),   # sliding window
     (1, 1, 1, 1, 128, 1, 0, "plain", 86),          # S = 1
+    (1, 4, 2, 300, 256, 1, 0, "channels", 87),     # D = 256: one-loop schedule, ragged tail
+    (1, 2, 2, 333, 256, 1, 100, "channels", 88),   # D = 256 with a sliding window
+    (1, 2, 1, 130, 256, 0, 0, "channels", 89),     # D = 256, non-causal
 ]
 
 
@@ -343,11 +346,13 @@ def test_plain_bf16_parity_full_size():
                                       label="qwen3-8b sampled"))
 
 
-def test_plain_bf16_rejects_d256():
-    import mixed_precision_attention_lamp_amd as lamp
-    q, k, v = make_inputs(1, 1, 1, 64, 256, 87, "plain")
-    with pytest.raises(lamp.LampError):
-        lamp.attention_bf16(to_device(q), to_device(k), to_device(v), True, 0)
+def test_plain_bf16_parity_full_size_d256():
+    """The plain bf16 baseline at D = 256 (one-loop schedule, K16 tiles in
+    the K8 slots) on the Gemma-3-12B-shaped workload, sampled units."""
+    q, k, v, cfg = _workload("gemma3-12b")
+    units = _sample_units(cfg["B"], cfg["Hq"], cfg["S"], 6, 11)
+    assert_parity_plain(compare_plain(q, k, v, cfg["causal"], cfg["window"], units=units,
+                                      label="gemma3-12b sampled"))
 
 
 # --------------------------------------------------------------------------
