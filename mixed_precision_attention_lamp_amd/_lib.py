@@ -32,12 +32,19 @@ class LampError(RuntimeError):
 def load():
     """Load liblamp.so once (raises if it has not been built)."""
     global _lib
-    if _lib is not None:
-        return _lib
-    if not os.path.exists(LIB_PATH):
-        raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+    if _lib is None:
+        _lib = load_library(LIB_PATH)
+    return _lib
+
+
+def load_library(path):
+    """A ctypes handle on a built copy of the library at `path` (liblamp.so,
+    or the test build liblamp_sync.so), with the entry points' signatures set;
+    raises if the file is missing."""
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with "
                            "`python -m mixed_precision_attention_lamp_amd.build`")
-    lib = ctypes.CDLL(LIB_PATH)
+    lib = ctypes.CDLL(path)
     vp, i32, f32, i64 = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_int64
     lib.lamp_attn_fwd.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, f32, f32, vp]
     lib.lamp_attn_fwd.restype = i32
@@ -84,7 +91,6 @@ def load():
     lib.lamp_release_workspace.restype = None
     lib.lamp_version.argtypes = []
     lib.lamp_version.restype = i32
-    _lib = lib
     return lib
 
 

@@ -18,7 +18,12 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "liblamp.so")
+# A second library for the LDS-race test: the same sources with every copy
+# into LDS waited for where it is issued (and decode's stores fenced by a
+# barrier); its outputs must equal liblamp.so's bit for bit.
+LIB_SYNC = os.path.join(PKG, "liblamp_sync.so")
 SOURCES = ["quant.hip", "attn.hip", "decode.hip", "stats.hip", "lamp_api.cpp"]
+SYNC_SOURCES = ["attn.hip", "decode.hip"]
 # Device sources: inputs are finite (documented in lamp.h), so max/min need no
 # NaN quieting.  Not for lamp_api.cpp, whose argument checks test for NaN.
 DEVICE_FLAGS = {"quant.hip": ["-fno-honor-nans"], "attn.hip": ["-fno-honor-nans"],
@@ -35,8 +40,8 @@ FLAGS = [
 ]
 
 
-def _compile(src, obj):
-    cmd = [HIPCC, *FLAGS, *DEVICE_FLAGS.get(src, []), "-x", "hip", "-c", os.path.join(CSRC, src),
+def _compile(src, obj, extra=()):
+    cmd = [HIPCC, *FLAGS, *DEVICE_FLAGS.get(src, []), *extra, "-x", "hip", "-c", os.path.join(CSRC, src),
            "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     noise = "is not a recognized feature for this target"
@@ -44,13 +49,27 @@ def _compile(src, obj):
     return r.returncode, " ".join(cmd), err
 
 
+def _link(objs, out, tmp):
+    out_tmp = os.path.join(tmp, os.path.basename(out))
+    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", out_tmp]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stderr}")
+    shutil.copyfile(out_tmp, out + ".tmp")
+    os.replace(out + ".tmp", out)
+
+
 def build(verbose=False):
-    """Compile every source and link liblamp.so; raises RuntimeError on failure."""
+    """Compile every source and link liblamp.so and liblamp_sync.so; raises
+    RuntimeError on failure."""
     tmp = tempfile.mkdtemp(prefix="lamp_build_")
     try:
-        objs = [os.path.join(tmp, s + ".o") for s in SOURCES]
-        with cf.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
-            results = list(ex.map(_compile, SOURCES, objs))
+        objs = {s: os.path.join(tmp, s + ".o") for s in SOURCES}
+        sync_objs = {s: os.path.join(tmp, s + ".sync.o") for s in SYNC_SOURCES}
+        jobs = [(s, objs[s], ()) for s in SOURCES] + [(s, sync_objs[s], ("-DLAMP_EXTRA_SYNC",))
+                                                      for s in SYNC_SOURCES]
+        with cf.ThreadPoolExecutor(max_workers=min(8, len(jobs))) as ex:
+            results = list(ex.map(lambda j: _compile(*j), jobs))
         for rc, cmd, err in results:
             if verbose or rc != 0:
                 print(cmd, file=sys.stderr)
@@ -58,13 +77,8 @@ def build(verbose=False):
                     print(err, file=sys.stderr)
             if rc != 0:
                 raise RuntimeError(f"hipcc failed: {cmd}\n{err}")
-        out_tmp = os.path.join(tmp, "liblamp.so")
-        cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", out_tmp]
-        r = subprocess.run(cmd, capture_output=True, text=True)
-        if r.returncode != 0:
-            raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stderr}")
-        shutil.copyfile(out_tmp, LIB + ".tmp")
-        os.replace(LIB + ".tmp", LIB)
+        _link([objs[s] for s in SOURCES], LIB, tmp)
+        _link([sync_objs.get(s, objs[s]) for s in SOURCES], LIB_SYNC, tmp)
     finally:
         shutil.rmtree(tmp, ignore_errors=True)
     return LIB

@@ -806,6 +806,9 @@ __global__ __launch_bounds__(kThreads, 1) void lamp_attn_kernel(AttnArgs a) {
             wait_copies();
 #pragma unroll
             for (int k = 0; k < kDmaSteps; ++k) dma_step(k, t + 2, s_n2, t + 3, s_cur);
+#ifdef LAMP_EXTRA_SYNC
+            wait_copies();   // test build: the copies land within the phase that issues them
+#endif
             if (w_cur && a.mask && wib == 0 && lane == 0)
                 a.mask[(q_head * a.nT + r) * a.nT + t] = (uint8_t)(0x80u | flags);
             __builtin_amdgcn_s_setprio(0);
@@ -846,6 +849,9 @@ __global__ __launch_bounds__(kThreads, 1) void lamp_attn_kernel(AttnArgs a) {
         for (int t = t_begin; t <= t_end; ++t) {
             const int sc = t & 1, sn = sc ^ 1;
             if (t + 1 <= t_end) dma_qk(t + 1, sn);
+#ifdef LAMP_EXTRA_SYNC
+            wait_copies();   // test build: every copy lands where it is issued
+#endif
             const bool w_prev = work(t - 1), w_cur = work(t), w_next = work(t + 1);
             const bool full = full_tile(t);
             auto copy = [&](int k) __attribute__((always_inline)) {
@@ -863,6 +869,9 @@ __global__ __launch_bounds__(kThreads, 1) void lamp_attn_kernel(AttnArgs a) {
 #pragma unroll
                 for (int k = 0; k < kAfterK8; ++k) copy(k);
             }
+#ifdef LAMP_EXTRA_SYNC
+            wait_copies();
+#endif
             uint32_t flags = 0u;
             if (w_cur) {
                 round_logits(S);

@@ -486,6 +486,9 @@ __global__ __launch_bounds__(kW * 64, 2) void lamp_decode_kernel(DecodeArgs a) {
         for (int t = t_first; t <= t_end; ++t) {
             const int so = ((t - t_first) & 1) * kSlot;
             store(rkA, rvA, kSlot - so);
+#ifdef LAMP_EXTRA_SYNC
+            lds_barrier();   // test build: every wave's stores of t+1 before any reads of t
+#endif
             load(min(t + 2, t_end), rkA, rvA);
             tile(t, so);
             if (((t - t_first) & 63) == 63 || t == t_end) {
