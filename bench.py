@@ -39,10 +39,10 @@ COPY_BYTES = 1 << 30       # size of the calibration copy
 # the kernel source whose hash is recorded; any change to it makes the figure
 # null.
 TRAFFIC = [
-    {"kernel_hash": "4c07cc11aa798461", "workload": "qwen3-8b", "delta": 2.0 ** -8, "tau": 2.0 ** -1,
-     "bytes_per_launch": 130207210.4},
-    {"kernel_hash": "4c07cc11aa798461", "workload": "gemma3-12b", "delta": 2.0 ** -8, "tau": 2.0 ** -1,
-     "bytes_per_launch": 421108929.8},
+    {"kernel_hash": "5cbb6fd19a640bf4", "workload": "qwen3-8b", "delta": 2.0 ** -8, "tau": 2.0 ** -1,
+     "bytes_per_launch": 130241168.9},
+    {"kernel_hash": "5cbb6fd19a640bf4", "workload": "gemma3-12b", "delta": 2.0 ** -8, "tau": 2.0 ** -1,
+     "bytes_per_launch": 420301276.5},
 ]
 
 
@@ -53,9 +53,9 @@ TRAFFIC = [
 # of issue), i.e. the launch time if the vector units were never idle.  Valid
 # only for the recorded kernel source.
 VALU_CEILING = [
-    {"kernel_hash": "4c07cc11aa798461", "workload": "qwen3-8b", "delta": 2.0 ** -8, "tau": 2.0 ** -1,
+    {"kernel_hash": "5cbb6fd19a640bf4", "workload": "qwen3-8b", "delta": 2.0 ** -8, "tau": 2.0 ** -1,
      "cycles_per_simd": 208704.3, "clock_hz": 2.4e9, "source": "profiles/attn_qwen3_8b_sq_counters.md"},
-    {"kernel_hash": "4c07cc11aa798461", "workload": "gemma3-12b", "delta": 2.0 ** -8, "tau": 2.0 ** -1,
+    {"kernel_hash": "5cbb6fd19a640bf4", "workload": "gemma3-12b", "delta": 2.0 ** -8, "tau": 2.0 ** -1,
      "cycles_per_simd": 586975.4, "clock_hz": 2.4e9, "source": "profiles/attn_gemma3_12b_counters.md"},
 ]
 
@@ -71,8 +71,8 @@ def _record(records, args, kernel_hash):
 
 # The same for the decode kernel on the qwen3-8b-decode workload
 # (profiles/decode_qwen3_8b_hbm_traffic.md), library split.
-TRAFFIC_DECODE = {"kernel_hash": "2ba6da197ceae8ff", "workload": "qwen3-8b-decode", "delta": 2.0 ** -8,
-                  "tau": 2.0 ** -1, "bytes_per_launch": 555066974.7}
+TRAFFIC_DECODE = {"kernel_hash": "1939cba10673f971", "workload": "qwen3-8b-decode", "delta": 2.0 ** -8,
+                  "tau": 2.0 ** -1, "bytes_per_launch": 555052289.2}
 
 
 def decode_source_hash():

@@ -16,6 +16,8 @@ struct Shape {
 
 // Number of amax partial maxima (chunks) for a slab of S*D bf16 values.
 int amax_chunks(int S, int D);
+// The same for the K pass of a decode step (launch_decode_scales).
+int decode_amax_chunks(int Skv, int D);
 
 // Quantisation pass (Q and K): per-(batch, head) amax partial maxima, then
 // scales and e4m3 codes.  q8 / k8 are written with `rows_out` rows per head
@@ -89,7 +91,7 @@ struct DecodeParams {
 
 // Per-head scales and inverse scales of the decode inputs: Q heads over
 // their Sq rows, K heads over all Skv rows (partial must hold
-// B * Hkv * amax_chunks(Skv, D) uint32 values).
+// B * Hkv * decode_amax_chunks(Skv, D) uint32 values).
 hipError_t launch_decode_scales(const DecodeShape& sh, const uint16_t* q, const uint16_t* k,
                                 uint32_t* partial, float* q_scale, float* q_inv, float* k_scale,
                                 float* k_inv, hipStream_t st);

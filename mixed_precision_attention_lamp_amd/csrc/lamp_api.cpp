@@ -398,7 +398,7 @@ static int decode_impl(const void* q, const void* k, const void* v, float* out, 
 
     size_t off = 0;
     auto take = [&](size_t bytes) { size_t o = off; off = round_up(off + bytes, 256); return o; };
-    const size_t o_partial = take(k_amax ? 0 : (size_t)B * Hkv * lamp::amax_chunks(Skv, D) * sizeof(uint32_t));
+    const size_t o_partial = take(k_amax ? 0 : (size_t)B * Hkv * lamp::decode_amax_chunks(Skv, D) * sizeof(uint32_t));
     const size_t o_qs = take((size_t)B * Hq * sizeof(float));
     const size_t o_qi = take((size_t)B * Hq * sizeof(float));
     const size_t o_ks = take((size_t)B * Hkv * sizeof(float));

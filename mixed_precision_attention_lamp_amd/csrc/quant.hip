@@ -20,6 +20,8 @@ namespace lamp {
 namespace {
 
 constexpr int kChunk = 16384;      // bf16 values per amax / quantise block (8 loads per thread)
+// the decode step's pass over K (a few large slabs) streams faster in half the chunk
+constexpr int kDecodeChunk = 8192;
 constexpr int kThreads = 256;
 
 __device__ __forceinline__ uint32_t max_bf16_mag(u32x4 w) {
@@ -46,16 +48,17 @@ __device__ __forceinline__ uint32_t block_max_u32(uint32_t v, uint32_t* red) {
 
 // Partial max |x| of chunk `chunk` of slab `slab` (Q heads first, then K
 // heads) into partial[slab * nch + chunk].
+template <int kCh>
 __device__ __forceinline__ void amax_block(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                                            uint32_t* __restrict__ partial, int n_q_slabs, int slab_len,
                                            int nch, int slab, int chunk, uint32_t* red) {
     const uint16_t* src = slab < n_q_slabs ? q + (size_t)slab * slab_len
                                            : k + (size_t)(slab - n_q_slabs) * slab_len;
-    const int begin = chunk * kChunk;
-    const int end = min(begin + kChunk, slab_len);
+    const int begin = chunk * kCh;
+    const int end = min(begin + kCh, slab_len);
     uint32_t m = 0;
 #pragma unroll
-    for (int j = 0; j < kChunk / (kThreads * 8); ++j) {
+    for (int j = 0; j < kCh / (kThreads * 8); ++j) {
         const int i = begin + (j * kThreads + (int)threadIdx.x) * 8;
         if (i < end) m = max(m, max_bf16_mag(*reinterpret_cast<const u32x4*>(src + i)));
     }
@@ -63,13 +66,14 @@ __device__ __forceinline__ void amax_block(const uint16_t* __restrict__ q, const
     if (threadIdx.x == 0) partial[(size_t)slab * nch + chunk] = m;
 }
 
-// blockIdx.y = slab (Q heads first, then K heads); blockIdx.x = chunk.
+// blockIdx.y = slab (Q heads first, then K heads); blockIdx.x = chunk of kCh values.
+template <int kCh>
 __global__ __launch_bounds__(kThreads) void amax_kernel(const uint16_t* __restrict__ q,
                                                         const uint16_t* __restrict__ k,
                                                         uint32_t* __restrict__ partial,
                                                         int n_q_slabs, int slab_len, int nch) {
     __shared__ uint32_t red[kThreads / 64];
-    amax_block(q, k, partial, n_q_slabs, slab_len, nch, blockIdx.y, blockIdx.x, red);
+    amax_block<kCh>(q, k, partial, n_q_slabs, slab_len, nch, blockIdx.y, blockIdx.x, red);
 }
 
 // Kept K magnitudes of a KV cache: state[slab] becomes the larger of itself
@@ -213,7 +217,7 @@ __global__ __launch_bounds__(kThreads) void amax_transpose_kernel(
     __shared__ uint16_t tile[kTileKeys * kTrStride<D>];
     const int bid = blockIdx.x;
     if (bid < n_amax) {
-        amax_block(q, k, partial, n_q_slabs, slab_len, nch, bid / nch, bid % nch, red);
+        amax_block<kChunk>(q, k, partial, n_q_slabs, slab_len, nch, bid / nch, bid % nch, red);
         return;
     }
     const int tb = bid - n_amax;
@@ -270,6 +274,7 @@ __global__ void debug_convert_kernel(const float* __restrict__ x, int64_t n, uin
 }  // namespace
 
 int amax_chunks(int S, int D) { return (S * D + kChunk - 1) / kChunk; }
+int decode_amax_chunks(int Skv, int D) { return (Skv * D + kDecodeChunk - 1) / kDecodeChunk; }
 
 hipError_t launch_quantize_codes(const Shape& sh, const uint16_t* q, const uint16_t* k,
                                  const uint32_t* partial, float* q_scale, float* k_scale, float* q_inv,
@@ -289,7 +294,7 @@ hipError_t launch_quantize(const Shape& sh, const uint16_t* q, const uint16_t* k
                            uint8_t* q8, uint8_t* k8, int rows_out, hipStream_t st) {
     const int nq = sh.B * sh.Hq, nk = sh.B * sh.Hkv;
     const int nch = amax_chunks(sh.S, sh.D);
-    hipLaunchKernelGGL(amax_kernel, dim3(nch, nq + nk), dim3(kThreads), 0, st, q, k, partial, nq,
+    hipLaunchKernelGGL(amax_kernel<kChunk>, dim3(nch, nq + nk), dim3(kThreads), 0, st, q, k, partial, nq,
                        sh.S * sh.D, nch);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -320,9 +325,10 @@ hipError_t launch_decode_scales(const DecodeShape& sh, const uint16_t* q, const 
                                 uint32_t* partial, float* q_scale, float* q_inv, float* k_scale,
                                 float* k_inv, hipStream_t st) {
     const int nq = sh.B * sh.Hq, nk = sh.B * sh.Hkv;
-    const int nch = amax_chunks(sh.Skv, sh.D);
+    const int nch = decode_amax_chunks(sh.Skv, sh.D);
     // K partial maxima (every slab is a K slab)
-    hipLaunchKernelGGL(amax_kernel, dim3(nch, nk), dim3(kThreads), 0, st, q, k, partial, 0, sh.Skv * sh.D, nch);
+    hipLaunchKernelGGL(amax_kernel<kDecodeChunk>, dim3(nch, nk), dim3(kThreads), 0, st, q, k, partial, 0,
+                       sh.Skv * sh.D, nch);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(decode_scales_kernel, dim3(nq + nk), dim3(kThreads), 0, st, q, partial, q_scale, q_inv,
