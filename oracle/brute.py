@@ -102,6 +102,28 @@ def _exp2_f32(x):
         return math.inf
 
 
+# The polynomial exp2 of the bit-reproducible variant, step by step on exact
+# rationals: clamp at -30, n = rint(x) (ties to even), f = x - n, Horner's
+# rule from the degree-5 coefficient down with every multiply-add rounded once
+# to fp32, then scaled by 2^n.  The coefficients are the fp32 values
+# m * 2^e below (24-bit integer m).
+_POLY_C = [Fraction(0xB17215, 2 ** 24), Fraction(0xF5FCD7, 2 ** 26), Fraction(0xE35B27, 2 ** 28),
+           Fraction(0x9E7733, 2 ** 30), Fraction(0xAE086A, 2 ** 33)]
+
+
+def exp2_poly(x):
+    """The variant's exp2 of an fp32 value x (a float), as a Fraction."""
+    xf = Fraction(-30) if x == -math.inf else max(Fraction(x), Fraction(-30))
+    fl = math.floor(xf)
+    rest = xf - fl
+    n = fl + 1 if rest > Fraction(1, 2) or (rest == Fraction(1, 2) and fl % 2 == 1) else fl
+    f = xf - n
+    p = _POLY_C[4]
+    for c in (_POLY_C[3], _POLY_C[2], _POLY_C[1], _POLY_C[0], Fraction(1)):
+        p = to_f32(p * f + c)
+    return p * Fraction(2) ** n
+
+
 def _bf16(bits):
     """Exact value of a bfloat16 bit pattern."""
     bits = int(bits)
@@ -113,12 +135,13 @@ def _bf16(bits):
     return sign * (1 + Fraction(m, 128)) * Fraction(2) ** (ef - 127)
 
 
-def brute_lamp(q_bits, k_bits, v_bits, causal, window, delta, tau, logit8=False):
+def brute_lamp(q_bits, k_bits, v_bits, causal, window, delta, tau, logit8=False, exp_poly=False):
     """Whole forward pass; returns (out as nested lists of float, mask dict).
 
     mask[(b, hq, r, t)] = byte for visited tiles only.  ``logit8``: the
     variant whose log2-domain logits are rounded to e4m3 before the running
-    max, the exponentials and the second stage read them.
+    max, the exponentials and the second stage read them.  ``exp_poly``: the
+    variant whose 8-bit exponentials come from the polynomial exp2.
     """
     B, Hq, S, D = (len(q_bits), len(q_bits[0]), len(q_bits[0][0]), len(q_bits[0][0][0]))
     Hkv = len(k_bits[0])
@@ -186,7 +209,7 @@ def brute_lamp(q_bits, k_bits, v_bits, causal, window, delta, tau, logit8=False)
                     p, flags = {}, [False] * 4
                     for (i, j), a in acc8.items():
                         arg = s2[i, j] - m_new[i] if logit8 else a * c8 - m_new[i]
-                        e = _exp2_f32(to_f32(arg))
+                        e = exp2_poly(to_f32(arg)) if exp_poly else _exp2_f32(to_f32(arg))
                         p8 = to_e4m3(e)
                         p[i, j] = p8
                         active = (delta <= 0) or (p8 >= Fraction(delta))

@@ -131,6 +131,37 @@ def fma32(a, b, c):
     return out.reshape(shape)
 
 
+# The polynomial exp2 of the bit-reproducible variant (abstract: the
+# exponentials are taken in 8-bit formats; the pages do not say how they are
+# evaluated).  Read here as a function defined by its steps, each an fp32
+# operation rounded to nearest-even, so that any implementation of the same
+# steps gives the same bits:
+#   x <- max(x, -30)      (2^-30 and everything below it round to 0 in e4m3)
+#   n = rint(x)           (ties to even), f = x - n (exact, |f| <= 1/2)
+#   p = 1 + f(c1 + f(c2 + f(c3 + f(c4 + f c5))))  by Horner's rule, every step
+#       one fused multiply-add rounded once to fp32, innermost first
+#   result = p * 2^n      (exact: p in [0.7, 1.5], n >= -30, so it stays normal)
+# c1..c5 are a minimax fit of the relative error of 2^f on [-1/2, 1/2] with
+# the constant term fixed at 1, each rounded to fp32; the fp32 evaluation
+# stays within 2^-22 of 2^x, relative.
+EXP2_POLY_XMIN = -30.0
+EXP2_POLY_C = tuple(float.fromhex(h) for h in (
+    "0x1.62e42ap-1", "0x1.ebf9aep-3", "0x1.c6b64ep-5", "0x1.3cee66p-7", "0x1.5c10d4p-10"))
+
+
+def exp2_poly_f32(x):
+    """The polynomial exp2 above, on fp32 arguments (held in fp64); NaN
+    arguments take the clamp's value, as an IEEE maxNum does."""
+    x = np.fmax(np.asarray(x, dtype=np.float64), EXP2_POLY_XMIN)
+    n = np.rint(x)
+    f = x - n
+    c1, c2, c3, c4, c5 = EXP2_POLY_C
+    p = fma32(c5, f, c4)
+    for c in (c3, c2, c1, 1.0):
+        p = fma32(p, f, c)
+    return np.ldexp(p, n.astype(np.int64))
+
+
 def exp2_f32(x):
     """fp32 exp2: the fp64 exp2 of an fp32 argument, rounded to fp32.
 

@@ -39,6 +39,11 @@ e4m3 (saturating at 448) before anything uses it.  The running max, the
 exponential's argument s8 - m (exact: both are e4m3 values) and the second
 stage all read the 8-bit logit; the 16-bit recompute is unchanged.
 
+A third variant (``exp_poly``) makes the 8-bit exponentials bit-reproducible:
+they come from ``formats.exp2_poly_f32``, a degree-5 polynomial exp2 defined
+by its fp32 steps, instead of the correctly rounded exp2; everything else is
+unchanged (the 16-bit recompute keeps the correctly rounded exp2).
+
 Masking: causal (key j visible to query i iff j <= i) and an optional sliding
 window W (additionally i - j < W).  GQA: query head hq reads kv head hq // G.
 """
@@ -46,7 +51,7 @@ import math
 
 import numpy as np
 
-from .formats import (bf16_bits_to_f64, e4m3_encode, exp2_f32, fl32, fma32,
+from .formats import (bf16_bits_to_f64, e4m3_encode, exp2_f32, exp2_poly_f32, fl32, fma32,
                       round_bf16, round_e4m3)
 
 LOG2E = 1.4426950408889634          # fp64 nearest to log2(e)
@@ -227,7 +232,8 @@ def run_unit(ctx, b, hq, r, flag_override=None, trace=None, tiles=None):
             x = np.where(vis, fl32(s32 - safe_m[:, None]), -np.inf)
         else:
             x = np.where(vis, fma32(acc8, c8, -safe_m[:, None]), -np.inf)
-        e = np.where(vis, exp2_f32(x), 0.0)
+        with np.errstate(invalid="ignore"):
+            e = np.where(vis, exp2_poly_f32(x) if ctx.get("exp_poly") else exp2_f32(x), 0.0)
         p8 = round_e4m3(e)
         # (d) look-ahead test, first and second stage
         active = stage_one(p8, vis, delta)
@@ -357,10 +363,11 @@ class PerHead:
         return self._cache[key][tuple(idx[2:])]
 
 
-def prepare(q_bits, k_bits, v_bits, causal, window, delta, tau, logit8=False):
+def prepare(q_bits, k_bits, v_bits, causal, window, delta, tau, logit8=False, exp_poly=False):
     """Scales of Q and K, and per-head access to everything the units read
     (the e4m3 values of Q and K, and the bf16 values of Q, K and V).
-    ``logit8`` selects the variant whose log2-domain logits are e4m3 values.
+    ``logit8`` selects the variant whose log2-domain logits are e4m3 values,
+    ``exp_poly`` the one whose 8-bit exponentials use the polynomial exp2.
     Q may hold fewer rows than K and V (decode): they are then the last
     positions of the sequence."""
     B, Hq, Sq, D = q_bits.shape
@@ -378,7 +385,7 @@ def prepare(q_bits, k_bits, v_bits, causal, window, delta, tau, logit8=False):
 
     return dict(B=B, Hq=Hq, Hkv=Hkv, S=S, D=D, G=Hq // Hkv, Sq=Sq, q_off=S - Sq,
                 causal=bool(causal), window=int(window),
-                delta=float(delta), T2=tau_threshold(tau), logit8=bool(logit8),
+                delta=float(delta), T2=tau_threshold(tau), logit8=bool(logit8), exp_poly=bool(exp_poly),
                 q8=PerHead(e4m3_slab(q_bits, iq)), k8=PerHead(e4m3_slab(k_bits, ik)), sq=sq, sk=sk,
                 q16=PerHead(bf16_slab(q_bits)), k16=PerHead(bf16_slab(k_bits)),
                 v=PerHead(bf16_slab(v_bits)))
@@ -390,16 +397,17 @@ def all_units(B, Hq, S):
 
 
 def lamp_forward(q_bits, k_bits, v_bits, causal=True, window=0, delta=2.0 ** -8,
-                 tau=2.0 ** -1, units=None, flag_override=None, logit8=False):
+                 tau=2.0 ** -1, units=None, flag_override=None, logit8=False, exp_poly=False):
     """The LampAttention forward pass over ``units`` (default: all).
 
     q_bits [B, Hq, S, D], k_bits / v_bits [B, Hkv, S, D]: bf16 bit patterns.
     Returns (out fp32 [B, Hq, S, D] (rows of units not computed are NaN),
     mask uint8 [B, Hq, nT, nT]).  ``flag_override`` is a mask array of the
     same shape whose low 4 bits replace the computed flags of visited tiles.
-    ``logit8``: the variant with e4m3 logits.
+    ``logit8``: the variant with e4m3 logits; ``exp_poly``: the variant with
+    the polynomial exp2 for the 8-bit exponentials.
     """
-    ctx = prepare(q_bits, k_bits, v_bits, causal, window, delta, tau, logit8)
+    ctx = prepare(q_bits, k_bits, v_bits, causal, window, delta, tau, logit8, exp_poly)
     B, Hq, S, D = ctx["B"], ctx["Hq"], ctx["S"], ctx["D"]
     nT = n_tiles(S)
     out = np.full((B, Hq, S, D), np.nan, dtype=np.float32)
