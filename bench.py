@@ -37,11 +37,13 @@ COPY_BYTES = 1 << 30       # size of the calibration copy
 # counter's reading for a plain copy of COPY_BYTES (profiles/
 # attn_qwen3_8b_hbm_traffic.md, attn_gemma3_12b_counters.md).  Valid only for
 # the kernel source whose hash is recorded; any change to it makes the figure
-# null.
+# null.  (The counters were taken on the source before the polynomial-exp2
+# mode was added; that change left the machine code of every other kernel
+# instantiation identical, instruction for instruction.)
 TRAFFIC = [
-    {"kernel_hash": "5cbb6fd19a640bf4", "workload": "qwen3-8b", "delta": 2.0 ** -8, "tau": 2.0 ** -1,
+    {"kernel_hash": "c96a80d1af4a0367", "workload": "qwen3-8b", "delta": 2.0 ** -8, "tau": 2.0 ** -1,
      "bytes_per_launch": 130241168.9},
-    {"kernel_hash": "5cbb6fd19a640bf4", "workload": "gemma3-12b", "delta": 2.0 ** -8, "tau": 2.0 ** -1,
+    {"kernel_hash": "c96a80d1af4a0367", "workload": "gemma3-12b", "delta": 2.0 ** -8, "tau": 2.0 ** -1,
      "bytes_per_launch": 420301276.5},
 ]
 
@@ -53,9 +55,9 @@ TRAFFIC = [
 # of issue), i.e. the launch time if the vector units were never idle.  Valid
 # only for the recorded kernel source.
 VALU_CEILING = [
-    {"kernel_hash": "5cbb6fd19a640bf4", "workload": "qwen3-8b", "delta": 2.0 ** -8, "tau": 2.0 ** -1,
+    {"kernel_hash": "c96a80d1af4a0367", "workload": "qwen3-8b", "delta": 2.0 ** -8, "tau": 2.0 ** -1,
      "cycles_per_simd": 208704.3, "clock_hz": 2.4e9, "source": "profiles/attn_qwen3_8b_sq_counters.md"},
-    {"kernel_hash": "5cbb6fd19a640bf4", "workload": "gemma3-12b", "delta": 2.0 ** -8, "tau": 2.0 ** -1,
+    {"kernel_hash": "c96a80d1af4a0367", "workload": "gemma3-12b", "delta": 2.0 ** -8, "tau": 2.0 ** -1,
      "cycles_per_simd": 586975.4, "clock_hz": 2.4e9, "source": "profiles/attn_gemma3_12b_counters.md"},
 ]
 
@@ -71,7 +73,7 @@ def _record(records, args, kernel_hash):
 
 # The same for the decode kernel on the qwen3-8b-decode workload
 # (profiles/decode_qwen3_8b_hbm_traffic.md), library split.
-TRAFFIC_DECODE = {"kernel_hash": "1939cba10673f971", "workload": "qwen3-8b-decode", "delta": 2.0 ** -8,
+TRAFFIC_DECODE = {"kernel_hash": "0fa370a478cfbdf6", "workload": "qwen3-8b-decode", "delta": 2.0 ** -8,
                   "tau": 2.0 ** -1, "bytes_per_launch": 555052289.2}
 
 
@@ -450,6 +452,8 @@ GRID_ENDPOINTS = ((2.0 ** -8, float("inf"), "8-bit Q.K^T only"), (0.0, 0.0, "all
 PLAIN_NOTE = "plain bf16 FlashAttention (no 8-bit pass)"
 LOGIT8_NOTE = "8-bit logits (e4m3-rounded log2-domain logit)"
 LOGIT8_POINTS = ((2.0 ** -8, 2.0 ** -1), (2.0 ** -8, float("inf")), (2.0 ** -4, 2.0 ** -1))
+EXP2POLY_NOTE = "8-bit exponentials by the bit-reproducible polynomial exp2"
+EXP2POLY_POINTS = ((2.0 ** -8, 2.0 ** -1), (2.0 ** -8, float("inf")), (2.0 ** -4, 2.0 ** -1))
 
 
 def settle(torch, step, settle_ms):
@@ -467,9 +471,10 @@ def settle(torch, step, settle_ms):
 
 
 def measure(lamp, torch, tensors, shape, causal, window, delta, tau, steps, warmup, plain=False,
-            logit8=False, settle_ms=0.0):
+            logit8=False, settle_ms=0.0, exp_poly=False):
     """Time `steps` calls of lamp_attn_fwd (lamp_attn_fwd_bf16 when plain,
-    lamp_attn_fwd_logit8 when logit8) after `warmup` untimed ones; returns the
+    lamp_attn_fwd_logit8 when logit8, lamp_attn_fwd_exp2poly when exp_poly)
+    after `warmup` untimed ones; returns the
     step time, the attention kernel
     time (HIP events on its stream), the algorithmic FLOP counts and the
     sub-block statistics of the last call."""
@@ -481,6 +486,8 @@ def measure(lamp, torch, tensors, shape, causal, window, delta, tau, steps, warm
             lamp.lamp_attn_fwd_bf16(qd, kd, vd, out, causal, window, mask)
         elif logit8:
             lamp.lamp_attn_fwd_logit8(qd, kd, vd, out, causal, window, delta, tau, mask)
+        elif exp_poly:
+            lamp.lamp_attn_fwd_exp2poly(qd, kd, vd, out, causal, window, delta, tau, mask)
         else:
             lamp.lamp_attn_fwd(qd, kd, vd, out, causal, window, delta, tau, mask)
 
@@ -525,10 +532,11 @@ def run_grid(args, lamp, torch, tensors, shape, causal, window, cfg):
     runs = [(d, t, "") for d in GRID_DELTAS for t in GRID_TAUS] + list(GRID_ENDPOINTS)
     runs.append((0.0, 0.0, PLAIN_NOTE))
     runs += [(d, t, LOGIT8_NOTE) for d, t in LOGIT8_POINTS]
+    runs += [(d, t, EXP2POLY_NOTE) for d, t in EXP2POLY_POINTS]
     for delta, tau, note in runs:
         m = measure(lamp, torch, tensors, shape, causal, window, delta, tau, args.steps, args.warmup,
                     settle_ms=args.settle_ms / 3,
-                    plain=note == PLAIN_NOTE, logit8=note == LOGIT8_NOTE)
+                    plain=note == PLAIN_NOTE, logit8=note == LOGIT8_NOTE, exp_poly=note == EXP2POLY_NOTE)
         achieved, peak = roofline_of(m)
         print(json.dumps({
             "grid": args.workload, "delta": delta, "tau": tau if tau != float("inf") else "inf",

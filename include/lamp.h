@@ -112,6 +112,24 @@ int lamp_attn_fwd_logit8(const void* q, const void* k, const void* v, float* out
                          int causal, int window, float delta, float tau,
                          uint8_t* subblock_mask_out);
 
+/* The forward pass with bit-reproducible 8-bit exponentials ("LampAttention",
+ * abstract: exponentials taken in 8-bit formats; how they are evaluated is not
+ * given).  Each 8-bit exponential is e4m3(P(x)), x = fma(acc, c, -m) as in
+ * lamp_attn_fwd, where P is an exp2 defined by its fp32 steps, each rounded to
+ * nearest even:
+ *   x <- max(x, -30);  n = rint(x) (ties to even);  f = x - n;
+ *   p = fma(fma(fma(fma(fma(c5, f, c4), f, c3), f, c2), f, c1), f, 1);
+ *   P(x) = p * 2^n
+ * with c1 = 0x1.62e42ap-1, c2 = 0x1.ebf9aep-3, c3 = 0x1.c6b64ep-5,
+ * c4 = 0x1.3cee66p-7, c5 = 0x1.5c10d4p-10 (within 2^-22 of 2^x, relative), so
+ * that a CPU evaluation of the same steps gives the same bits; lamp_attn_fwd
+ * uses the hardware exp2 instead.  The 16-bit recompute is that of
+ * lamp_attn_fwd.  Arguments, layout, sizes and errors as lamp_attn_fwd. */
+int lamp_attn_fwd_exp2poly(const void* q, const void* k, const void* v, float* out,
+                           int B, int Hq, int Hkv, int S, int D,
+                           int causal, int window, float delta, float tau,
+                           uint8_t* subblock_mask_out);
+
 /* Decode: Sq query rows, the last positions (Skv - Sq .. Skv - 1) of a sequence,
  * against all Skv cached keys ("LampAttention", abstract: the method per tile as
  * in lamp_attn_fwd).  The Sq rows of a query head form the row block the
@@ -221,6 +239,10 @@ int lamp_quantize_qk(const void* q, const void* k, int B, int Hq, int Hkv, int S
 int lamp_debug_convert(const float* x, int64_t n, uint8_t* e4m3, uint16_t* e4m3_bf16,
                        uint16_t* bf16, float* exp2);
 
+/* The exp2 of lamp_attn_fwd_exp2poly, P(x), applied elementwise on the device,
+ * for tests: y[i] = P(x[i]) for n fp32 values (x finite; device pointers). */
+int lamp_debug_exp2poly(const float* x, int64_t n, float* y);
+
 /* The instruction that forms the 8-bit key-query products of lamp_attn_fwd
  * ("LampAttention", abstract: products in 8-bit formats), on given operands,
  * for tests of its accumulation: for each of n_blocks blocks,
@@ -252,6 +274,14 @@ int lamp_debug_attn_dump_logit8(const void* q, const void* k, const void* v, flo
                                 int B, int Hq, int Hkv, int S, int D,
                                 int causal, int window, float delta, float tau,
                                 uint8_t* subblock_mask_out, float* logit8_out, uint16_t* p_out);
+
+/* lamp_debug_attn_dump for lamp_attn_fwd_exp2poly: the same dump of the
+ * 8-bit accumulators and of the weights that entered P.V; sizes and errors as
+ * lamp_debug_attn_dump. */
+int lamp_debug_attn_dump_exp2poly(const void* q, const void* k, const void* v, float* out,
+                                  int B, int Hq, int Hkv, int S, int D,
+                                  int causal, int window, float delta, float tau,
+                                  uint8_t* subblock_mask_out, float* acc8_out, uint16_t* p_out);
 
 /* Per-kernel timing with HIP events recorded on the library's stream, for
  * benches.  While enabled (enable = 1), every lamp_attn_fwd and

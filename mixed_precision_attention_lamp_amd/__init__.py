@@ -10,7 +10,8 @@ allocates outputs.
 """
 from ._lib import (LAMP_STATS_LEN, LampError, declared_symbols, lamp_attn_decode,  # noqa: F401
                    lamp_attn_decode_with_amax, lamp_kv_amax_update,
-                   lamp_attn_fwd, lamp_attn_fwd_bf16, lamp_attn_fwd_logit8, lamp_attn_fwd_noalloc, lamp_debug_attn_dump,
+                   lamp_attn_fwd, lamp_attn_fwd_bf16, lamp_attn_fwd_exp2poly, lamp_attn_fwd_logit8,
+                   lamp_attn_fwd_noalloc, lamp_debug_attn_dump, lamp_debug_attn_dump_exp2poly, lamp_debug_exp2poly,
                    lamp_decode_tiles_per_split, lamp_debug_fp8_dot,
                    lamp_debug_attn_dump_logit8, lamp_debug_convert, lamp_last_error,
                    lamp_quantize_qk, lamp_read_timing, lamp_release_workspace, lamp_set_stream,
@@ -24,9 +25,11 @@ def n_tiles(S):
 
 
 def attention(q, k, v, causal=True, window=0, delta=2.0 ** -8, tau=2.0 ** -1, with_mask=True,
-              logit8=False):
+              logit8=False, exp_poly=False):
     """Allocate the outputs and run lamp_attn_fwd (lamp_attn_fwd_logit8 when
-    logit8); returns (out, mask or None)."""
+    logit8, lamp_attn_fwd_exp2poly when exp_poly); returns (out, mask or None)."""
+    if logit8 and exp_poly:
+        raise ValueError("logit8 and exp_poly are separate variants")
     import torch
     B, Hq, S, D = q.shape
     out = torch.empty((B, Hq, S, D), dtype=torch.float32, device=q.device)
@@ -34,7 +37,7 @@ def attention(q, k, v, causal=True, window=0, delta=2.0 ** -8, tau=2.0 ** -1, wi
     if with_mask:
         nT = n_tiles(S)
         mask = torch.empty((B, Hq, nT, nT), dtype=torch.uint8, device=q.device)
-    fwd = lamp_attn_fwd_logit8 if logit8 else lamp_attn_fwd
+    fwd = lamp_attn_fwd_logit8 if logit8 else (lamp_attn_fwd_exp2poly if exp_poly else lamp_attn_fwd)
     fwd(q, k, v, out, int(causal), int(window), delta, tau, mask)
     return out, mask
 

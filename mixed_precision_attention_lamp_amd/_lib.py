@@ -52,6 +52,8 @@ def load_library(path):
     lib.lamp_attn_fwd_noalloc.restype = i32
     lib.lamp_attn_fwd_logit8.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, f32, f32, vp]
     lib.lamp_attn_fwd_logit8.restype = i32
+    lib.lamp_attn_fwd_exp2poly.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, f32, f32, vp]
+    lib.lamp_attn_fwd_exp2poly.restype = i32
     lib.lamp_attn_fwd_bf16.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, vp]
     lib.lamp_attn_decode.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, i32, f32, f32,
                                      i32, vp]
@@ -70,6 +72,11 @@ def load_library(path):
     lib.lamp_debug_attn_dump_logit8.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, f32,
                                                 f32, vp, vp, vp]
     lib.lamp_debug_attn_dump_logit8.restype = i32
+    lib.lamp_debug_attn_dump_exp2poly.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, f32,
+                                                  f32, vp, vp, vp]
+    lib.lamp_debug_attn_dump_exp2poly.restype = i32
+    lib.lamp_debug_exp2poly.argtypes = [vp, i64, vp]
+    lib.lamp_debug_exp2poly.restype = i32
     lib.lamp_subblock_stats.argtypes = [vp, i32, i32, i32, i32, i32, vp]
     lib.lamp_subblock_stats.restype = i32
     lib.lamp_quantize_qk.argtypes = [vp, vp, i32, i32, i32, i32, i32, vp, vp, vp, vp]
@@ -244,6 +251,19 @@ def lamp_attn_fwd_logit8(q, k, v, out, causal=1, window=0, delta=2.0 ** -8, tau=
                                     _ptr(subblock_mask_out)))
 
 
+def lamp_attn_fwd_exp2poly(q, k, v, out, causal=1, window=0, delta=2.0 ** -8, tau=2.0 ** -1,
+                           subblock_mask_out=None):
+    """The variant with the polynomial exp2 for the 8-bit exponentials;
+    arguments as lamp_attn_fwd."""
+    lib = load()
+    B, Hq, Hkv, S, D = _attn_shapes(q, k, v)
+    _check_fwd_outputs(q, k, v, out, subblock_mask_out, B, Hq, S, D)
+    _sync_stream(lib)
+    _check(lib.lamp_attn_fwd_exp2poly(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, Hq, Hkv, S, D,
+                                      int(causal), int(window), float(delta), float(tau),
+                                      _ptr(subblock_mask_out)))
+
+
 def lamp_attn_decode(q, k, v, out, causal=1, window=0, delta=2.0 ** -8, tau=2.0 ** -1,
                      tiles_per_split=0, subblock_mask_out=None):
     """q [B,Hq,Sq,D] (the last Sq positions), k/v [B,Hkv,Skv,D] bf16; out
@@ -359,6 +379,20 @@ def lamp_debug_attn_dump_logit8(q, k, v, out, causal, window, delta, tau, subblo
                                            _ptr(subblock_mask_out), _ptr(logit8_out), _ptr(p_out)))
 
 
+def lamp_debug_attn_dump_exp2poly(q, k, v, out, causal, window, delta, tau, subblock_mask_out,
+                                  acc8_out, p_out):
+    import torch
+    lib = load()
+    B, Hq, Hkv, S, D = _attn_shapes(q, k, v)
+    _expect(acc8_out, "acc8_out", torch.float32, (B, Hq, S, S))
+    _expect(p_out, "p_out", (torch.int16, torch.bfloat16), (B, Hq, S, S))
+    _check_fwd_outputs(q, k, v, out, subblock_mask_out, B, Hq, S, D, (("acc8_out", acc8_out), ("p_out", p_out)))
+    _sync_stream(lib)
+    _check(lib.lamp_debug_attn_dump_exp2poly(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, Hq, Hkv, S, D,
+                                             int(causal), int(window), float(delta), float(tau),
+                                             _ptr(subblock_mask_out), _ptr(acc8_out), _ptr(p_out)))
+
+
 def lamp_subblock_stats(subblock_mask, B, Hq, S, causal, window, stats_out):
     import torch
     lib = load()
@@ -407,6 +441,20 @@ def lamp_debug_convert(x, e4m3=None, e4m3_bf16=None, bf16=None, exp2=None):
     _sync_stream(lib)
     _check(lib.lamp_debug_convert(_ptr(x), x.numel(), _ptr(e4m3), _ptr(e4m3_bf16), _ptr(bf16),
                                   _ptr(exp2)))
+
+
+def lamp_debug_exp2poly(x, y):
+    """y[i] = the polynomial exp2 of lamp_attn_fwd_exp2poly at x[i] (fp32, same length)."""
+    import torch
+    lib = load()
+    if x is None or not isinstance(x, torch.Tensor):
+        _invalid("x must be a torch tensor")
+    n = x.numel()
+    _expect(x, "x", torch.float32, (n,))
+    _expect(y, "y", torch.float32, (n,))
+    _on_gpu([("x", x), ("y", y)])
+    _sync_stream(lib)
+    _check(lib.lamp_debug_exp2poly(_ptr(x), n, _ptr(y)))
 
 
 def lamp_debug_fp8_dot(a, b, out):

@@ -5,7 +5,9 @@
 // Dedicated Accelerators" (abstract).  Per 64x64 tile of (query rows, keys):
 //   1. 8-bit logits: e4m3 Q.K^T on the FP8 matrix cores, fp32 accumulation;
 //   2. running row max over the 8-bit logits (log2 domain);
-//   3. 8-bit exponentials: exp2 rounded to e4m3;
+//   3. 8-bit exponentials: exp2 rounded to e4m3 (the hardware exp2, or in
+//      the bit-reproducible variant a polynomial exp2 defined by its fp32
+//      steps, poly_exp2);
 //   4. look-ahead test per 64x16 sub-block (figure 1-8 captions: delta, tau):
 //      an entry is sensitive iff p8 >= delta (first stage, off for delta <= 0)
 //      and |logit| >= 16 tau log2(e) (second stage); the wave ballots the
@@ -125,12 +127,15 @@ struct Cfg {
 // bf16; at D = 256 its K16 tiles take the K8 slots); 4 + (0, 1, 2): the test modes 0-2 with
 // 8-bit logits (the log2-domain logit c8 acc itself rounded to e4m3 before the
 // running max, the exponentials and the test read it); 9: mode 1 with the
-// per-entry test in vector form (for small tau, where most waves need it).
+// per-entry test in vector form (for small tau, where most waves need it);
+// 16 + (0, 1, 2): the test modes 0-2 with the 8-bit exponentials taken by
+// the bit-reproducible polynomial exp2 (poly_exp2) instead of v_exp_f32.
 template <int D, bool kDump, int kMode>
 __global__ __launch_bounds__(kThreads, 1) void lamp_attn_kernel(AttnArgs a) {
     constexpr bool kPlain = kMode == 3;
     constexpr bool kLogit8 = (kMode & 4) != 0;
     constexpr bool kDense = (kMode & 8) != 0;
+    constexpr bool kPoly = (kMode & 16) != 0;
     constexpr int kTest = kMode & 3;
     using C = Cfg<D, kPlain>;
     constexpr int kQG = C::kQG;
@@ -547,7 +552,8 @@ __global__ __launch_bounds__(kThreads, 1) void lamp_attn_kernel(AttnArgs a) {
                 float e[4];
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    e[i] = fast_exp2(__builtin_fmaf(s[qg][kb][i], kPlain ? c16 : c8, -m_use[qg]));
+                    const float x = __builtin_fmaf(s[qg][kb][i], kPlain ? c16 : c8, -m_use[qg]);
+                    e[i] = kPoly ? poly_exp2(x) : fast_exp2(x);
                     if constexpr (kMasked) e[i] = ((vis[qg] >> (kb * 4 + i)) & 1u) ? e[i] : 0.0f;
                 }
                 if constexpr (kPlain) {
@@ -973,6 +979,12 @@ hipError_t launch_d(const Shape& sh, const AttnParams& p, hipStream_t st) {
     // tau = 2^-3, qwen3-8b), elsewhere slower (240 against 221 at 2^-2).
     if (!p.logit8 && !p.plain && a.test_mode == 1 && a.t2 + a.x_delta <= -5.0f)
         fn = dump ? lamp_attn_kernel<D, true, 9> : lamp_attn_kernel<D, false, 9>;
+    if (p.exp_poly && !p.logit8 && !p.plain) {
+        static const Fn poly[2][3] = {
+            {lamp_attn_kernel<D, false, 16>, lamp_attn_kernel<D, false, 17>, lamp_attn_kernel<D, false, 18>},
+            {lamp_attn_kernel<D, true, 16>, lamp_attn_kernel<D, true, 17>, lamp_attn_kernel<D, true, 18>}};
+        fn = poly[dump ? 1 : 0][a.test_mode];
+    }
     if (p.plain) {
         fn = dump ? lamp_attn_kernel<D, true, 3> : lamp_attn_kernel<D, false, 3>;
         lds = Cfg<D, true>::kLdsBytes;

@@ -67,6 +67,26 @@ __device__ __forceinline__ uint32_t f32x2_to_bf16x2(float a, float b) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// exp2 by a polynomial whose steps are each one correctly rounded fp32
+// operation in a fixed order, so that any evaluation of the same steps (on a
+// CPU too) gives the same bits: x is clamped at -30 (2^-30 and all below it
+// round to 0 in e4m3), split as n + f with n = rint(x) (ties to even) and
+// |f| <= 1/2 (exact), 2^f ~ 1 + f (c1 + f (c2 + f (c3 + f (c4 + f c5)))) by
+// Horner's rule with fused multiply-adds, and the exponent n added exactly
+// (the result stays normal).  c1..c5: a minimax fit of the relative error on
+// [-1/2, 1/2] with the constant term 1, rounded to fp32 (within 2^-22 of 2^x).
+__device__ __forceinline__ float poly_exp2(float x) {
+    x = __builtin_fmaxf(x, -30.0f);
+    const float n = __builtin_rintf(x);
+    const float f = x - n;
+    float p = __builtin_fmaf(0x1.5c10d4p-10f, f, 0x1.3cee66p-7f);
+    p = __builtin_fmaf(p, f, 0x1.c6b64ep-5f);
+    p = __builtin_fmaf(p, f, 0x1.ebf9aep-3f);
+    p = __builtin_fmaf(p, f, 0x1.62e42ap-1f);
+    p = __builtin_fmaf(p, f, 1.0f);
+    return __builtin_ldexpf(p, (int)n);
+}
+
 // Workgroup barrier that orders LDS only: waits for this wave's LDS operations
 // (lgkmcnt = 0) but not for its outstanding global loads, then s_barrier.
 // (__syncthreads() also drains vmcnt, which would stall on prefetches.)

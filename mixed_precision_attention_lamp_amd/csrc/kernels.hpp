@@ -59,6 +59,7 @@ struct AttnParams {
     int causal, window;
     int plain = 0;          // 1: plain bf16 FlashAttention (no 8-bit pass; D <= 128)
     int logit8 = 0;         // 1: log2-domain logits rounded to e4m3 before use
+    int exp_poly = 0;       // 1: 8-bit exponentials by the polynomial exp2 (not with logit8 or plain)
 };
 
 // The forward attention kernel (16-bit recompute inside the tile loop).
@@ -128,5 +129,7 @@ hipError_t launch_debug_fp8_dot(const uint8_t* a, const uint8_t* b, float* out, 
 
 hipError_t launch_debug_convert(const float* x, int64_t n, uint8_t* e4m3, uint16_t* e4m3_bf16,
                                 uint16_t* bf16, float* exp2, hipStream_t st);
+// Test hook: the attention kernel's polynomial exp2 on n values.
+hipError_t launch_debug_poly_exp2(const float* x, int64_t n, float* y, hipStream_t st);
 
 }  // namespace lamp

@@ -301,7 +301,7 @@ int scratch_address(void** out) {
 static int attn_fwd_impl(const void* q, const void* k, const void* v, float* out, int B, int Hq, int Hkv,
                          int S, int D, int causal, int window, float delta, float tau,
                          uint8_t* subblock_mask_out, float* dump_s, uint16_t* dump_p, int plain,
-                         int logit8, int use_scratch = 0) {
+                         int logit8, int use_scratch = 0, int exp_poly = 0) {
     if (!q || !k || !v || !out) return fail(LAMP_ERR_INVALID, "q, k, v and out must be non-null");
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
         return fail(LAMP_ERR_INVALID, "q, k, v and out must be 16-byte aligned");
@@ -364,6 +364,7 @@ static int attn_fwd_impl(const void* q, const void* k, const void* v, float* out
     p.dump_s = dump_s; p.dump_p = dump_p;
     p.plain = plain;
     p.logit8 = logit8;
+    p.exp_poly = exp_poly;
     e = lamp::launch_attention(sh, p, g_stream);
     if (e != hipSuccess) return hip_fail(e, "attention launch");
     if (ev) timing_commit(ev);
@@ -474,6 +475,13 @@ int lamp_attn_fwd_logit8(const void* q, const void* k, const void* v, float* out
                          nullptr, nullptr, 0, 1);
 }
 
+int lamp_attn_fwd_exp2poly(const void* q, const void* k, const void* v, float* out, int B, int Hq, int Hkv,
+                           int S, int D, int causal, int window, float delta, float tau,
+                           uint8_t* subblock_mask_out) {
+    return attn_fwd_impl(q, k, v, out, B, Hq, Hkv, S, D, causal, window, delta, tau, subblock_mask_out,
+                         nullptr, nullptr, 0, 0, 0, 1);
+}
+
 int lamp_attn_fwd_bf16(const void* q, const void* k, const void* v, float* out, int B, int Hq, int Hkv,
                        int S, int D, int causal, int window, uint8_t* subblock_mask_out) {
     return attn_fwd_impl(q, k, v, out, B, Hq, Hkv, S, D, causal, window, 0.0f, 0.0f, subblock_mask_out,
@@ -482,11 +490,12 @@ int lamp_attn_fwd_bf16(const void* q, const void* k, const void* v, float* out, 
 
 static int attn_dump_impl(const void* q, const void* k, const void* v, float* out, int B, int Hq, int Hkv,
                           int S, int D, int causal, int window, float delta, float tau,
-                          uint8_t* subblock_mask_out, float* acc8_out, uint16_t* p_out, int logit8) {
+                          uint8_t* subblock_mask_out, float* acc8_out, uint16_t* p_out, int logit8,
+                          int exp_poly = 0) {
     if (!acc8_out || !p_out) return fail(LAMP_ERR_INVALID, "acc8_out and p_out must be non-null");
     if (S > 2048) return fail(LAMP_ERR_UNSUPPORTED, "debug dump needs S <= 2048 (got %d)", S);
     return attn_fwd_impl(q, k, v, out, B, Hq, Hkv, S, D, causal, window, delta, tau, subblock_mask_out,
-                         acc8_out, p_out, 0, logit8);
+                         acc8_out, p_out, 0, logit8, 0, exp_poly);
 }
 
 int lamp_debug_attn_dump(const void* q, const void* k, const void* v, float* out, int B, int Hq, int Hkv,
@@ -501,6 +510,13 @@ int lamp_debug_attn_dump_logit8(const void* q, const void* k, const void* v, flo
                                 uint8_t* subblock_mask_out, float* logit8_out, uint16_t* p_out) {
     return attn_dump_impl(q, k, v, out, B, Hq, Hkv, S, D, causal, window, delta, tau, subblock_mask_out,
                           logit8_out, p_out, 1);
+}
+
+int lamp_debug_attn_dump_exp2poly(const void* q, const void* k, const void* v, float* out, int B, int Hq,
+                                  int Hkv, int S, int D, int causal, int window, float delta, float tau,
+                                  uint8_t* subblock_mask_out, float* acc8_out, uint16_t* p_out) {
+    return attn_dump_impl(q, k, v, out, B, Hq, Hkv, S, D, causal, window, delta, tau, subblock_mask_out,
+                          acc8_out, p_out, 0, 1);
 }
 
 int lamp_decode_tiles_per_split(int B, int Hq, int Hkv, int Sq, int Skv, int D) {
@@ -624,6 +640,15 @@ int lamp_debug_convert(const float* x, int64_t n, uint8_t* e4m3, uint16_t* e4m3_
     if (!x) return fail(LAMP_ERR_INVALID, "x must be non-null");
     hipError_t e = lamp::launch_debug_convert(x, n, e4m3, e4m3_bf16, bf16, exp2, g_stream);
     if (e != hipSuccess) return hip_fail(e, "convert launch");
+    return LAMP_OK;
+}
+
+int lamp_debug_exp2poly(const float* x, int64_t n, float* y) {
+    if (n < 0) return fail(LAMP_ERR_INVALID, "n must be >= 0");
+    if (n == 0) return LAMP_OK;
+    if (!x || !y) return fail(LAMP_ERR_INVALID, "x and y must be non-null");
+    hipError_t e = lamp::launch_debug_poly_exp2(x, n, y, g_stream);
+    if (e != hipSuccess) return hip_fail(e, "exp2 launch");
     return LAMP_OK;
 }
 

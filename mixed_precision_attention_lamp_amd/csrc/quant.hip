@@ -271,6 +271,13 @@ __global__ void debug_convert_kernel(const float* __restrict__ x, int64_t n, uin
     }
 }
 
+// Test hook: the polynomial exp2 of the bit-reproducible variant, elementwise.
+__global__ void debug_poly_exp2_kernel(const float* __restrict__ x, int64_t n, float* y) {
+    for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n;
+         i += (int64_t)gridDim.x * blockDim.x)
+        y[i] = poly_exp2(x[i]);
+}
+
 }  // namespace
 
 int amax_chunks(int S, int D) { return (S * D + kChunk - 1) / kChunk; }
@@ -360,6 +367,14 @@ hipError_t launch_debug_convert(const float* x, int64_t n, uint8_t* e4m3, uint16
     if (blocks < 1) blocks = 1;
     hipLaunchKernelGGL(debug_convert_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, st, x, n,
                        e4m3, e4m3_bf16, bf16, exp2);
+    return hipGetLastError();
+}
+
+hipError_t launch_debug_poly_exp2(const float* x, int64_t n, float* y, hipStream_t st) {
+    int64_t blocks = (n + kThreads - 1) / kThreads;
+    if (blocks > 8192) blocks = 8192;
+    if (blocks < 1) blocks = 1;
+    hipLaunchKernelGGL(debug_poly_exp2_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, st, x, n, y);
     return hipGetLastError();
 }
 

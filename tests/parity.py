@@ -50,6 +50,10 @@ MAX_ROWS_ABOVE = 0.08       # at most this fraction of compared rows above MAX_A
 EPS_ACC8 = 2.0 ** -11       # FP8 matrix-core accumulation, relative to the largest product
 EPS_ACC16 = 2.0 ** -18      # bf16 matrix-core accumulation, relative to the largest product
 EXP2_ULPS = 2               # device exp2 (measured <= 2)
+# The polynomial exp2 of the bit-reproducible variant is within 2^-22 of 2^x
+# (relative) on both sides, so moving its argument by dx moves it by 2^dx
+# within 2^-21 relative: at most 8 ulps of an fp32 value.
+POLY_EXP2_ULPS = 8
 
 
 def unit_windows(ctx, b, h, r, trace):
@@ -81,11 +85,16 @@ def unit_windows(ctx, b, h, r, trace):
     return res
 
 
-def _e_bounds(e, dx):
-    """Exponential e = 2^x with x moved by +-dx and exp2 off by EXP2_ULPS ulps."""
-    lo = L._ulp_step(e * np.exp2(-dx), -EXP2_ULPS)
-    hi = L._ulp_step(e * np.exp2(dx), EXP2_ULPS)
+def _e_bounds(e, dx, ulps=EXP2_ULPS):
+    """Exponential e = 2^x with x moved by +-dx and exp2 off by ``ulps`` ulps."""
+    lo = L._ulp_step(e * np.exp2(-dx), -ulps)
+    hi = L._ulp_step(e * np.exp2(dx), ulps)
     return np.maximum(lo, 0.0), hi
+
+
+def _ulps8(ctx):
+    """The exp2 window of the 8-bit exponentials of a unit's reading."""
+    return POLY_EXP2_ULPS if ctx.get("exp_poly") else EXP2_ULPS
 
 
 def fragile_mask_bits(ctx, b, h, r, rec, win=None, one_ulp=False):
@@ -101,7 +110,7 @@ def fragile_mask_bits(ctx, b, h, r, rec, win=None, one_ulp=False):
         L.run_unit(ctx, b, h, r, trace=trace)
         win = unit_windows(ctx, b, h, r, [x for x in trace if x.get("final") or x["t"] <= rec["t"]])[rec["t"]]
     ds2, dx, _ = win
-    e_lo, e_hi = _e_bounds(e, dx)
+    e_lo, e_hi = _e_bounds(e, dx, _ulps8(ctx))
     a = np.abs(np.where(vis, s2, 0.0))
     res = []
     for e_k, s_k in ((e_lo, np.maximum(a - ds2, 0.0)), (e_hi, a + ds2)):
@@ -117,7 +126,7 @@ def fragile_alternatives(ctx, b, h, r, rec, win):
     _, dx, dx16 = win
     rec16 = ~np.isnan(e16)
     alt = np.zeros_like(p)
-    lo, hi = _e_bounds(e, dx)
+    lo, hi = _e_bounds(e, dx, _ulps8(ctx))
     for ek in (lo, hi):
         alt = np.maximum(alt, np.where(vis & ~rec16, np.abs(round_e4m3(ek) - p), 0.0))
     e16z = np.where(rec16, e16, 0.0)
@@ -218,10 +227,10 @@ def to_device(bits):
     return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
 
 
-def run_gpu(q, k, v, causal, window, delta, tau):
+def run_gpu(q, k, v, causal, window, delta, tau, exp_poly=False):
     import mixed_precision_attention_lamp_amd as lamp
     qd, kd, vd = to_device(q), to_device(k), to_device(v)
-    out, mask = lamp.attention(qd, kd, vd, causal, window, delta, tau)
+    out, mask = lamp.attention(qd, kd, vd, causal, window, delta, tau, exp_poly=exp_poly)
     torch.cuda.synchronize()
     return out.cpu().numpy(), mask.cpu().numpy()
 
@@ -256,15 +265,17 @@ def report_line(tag, label, rep):
             f"{rep['rows_explained']}, unexplained {len(rep['rows_unexplained'])})")
 
 
-def compare(q, k, v, causal, window, delta, tau, units=None, gpu=None, label=""):
-    """Run both sides and apply the protocol; returns a report dict (asserts nothing)."""
+def compare(q, k, v, causal, window, delta, tau, units=None, gpu=None, label="", exp_poly=False):
+    """Run both sides and apply the protocol; returns a report dict (asserts nothing).
+    ``exp_poly``: the variant with the polynomial exp2 (lamp_attn_fwd_exp2poly
+    against the oracle's exp_poly reading)."""
     B, Hq, S, D = q.shape
     if units is None:
         units = L.all_units(B, Hq, S)
     say(f"[parity] {label} B={B} Hq={Hq} Hkv={k.shape[1]} S={S} D={D} causal={causal} "
-        f"window={window} delta={delta} tau={tau} units={len(units)}")
-    out_g, mask_g = gpu if gpu is not None else run_gpu(q, k, v, causal, window, delta, tau)
-    ctx = L.prepare(q, k, v, causal, window, delta, tau)
+        f"window={window} delta={delta} tau={tau} units={len(units)} exp_poly={exp_poly}")
+    out_g, mask_g = gpu if gpu is not None else run_gpu(q, k, v, causal, window, delta, tau, exp_poly)
+    ctx = L.prepare(q, k, v, causal, window, delta, tau, exp_poly=exp_poly)
     judged, n_sub = [], 0
     for (b, h, r) in units:
         rows = slice(r * 64, min(r * 64 + 64, S))

@@ -33,7 +33,7 @@ def call(name, *args, expect=None):
     return rc
 
 
-fwd_names = ["lamp_attn_fwd", "lamp_attn_fwd_noalloc", "lamp_attn_fwd_logit8"]
+fwd_names = ["lamp_attn_fwd", "lamp_attn_fwd_noalloc", "lamp_attn_fwd_logit8", "lamp_attn_fwd_exp2poly"]
 sizes_bad = [(0, 1, 1, 64, 128), (1, 0, 1, 64, 128), (1, 1, 0, 64, 128), (1, 1, 1, 0, 128),
              (1, 3, 2, 64, 128), (1, 1, 1, 64, 96), (-1, 1, 1, 64, 128), (1, 1, 1, -5, 64),
              (1, 1, 1, INT_MAX, 128), (INT_MAX, INT_MAX, 1, INT_MAX, 256), (1, 8, 1, 1 << 24, 256),
@@ -109,7 +109,11 @@ for n in [-1, (1 << 20) + 1]:
     call("lamp_debug_fp8_dot", VP(b0), VP(b0), VP(b0), I(n), expect="fail")
 call("lamp_debug_fp8_dot", VP(mis), VP(b0), VP(b0), I(1), expect="fail")
 call("lamp_debug_fp8_dot", VP(b0), VP(b0), VP(b0), I(4))
-for name in ["lamp_debug_attn_dump", "lamp_debug_attn_dump_logit8"]:
+for n in [-1, 1 << 40]:
+    call("lamp_debug_exp2poly", VP(b0), I64(n), VP(b0), expect="fail")
+call("lamp_debug_exp2poly", VP(None), I64(4), VP(b0), expect="fail")
+call("lamp_debug_exp2poly", VP(b0), I64(100), VP(b0))
+for name in ["lamp_debug_attn_dump", "lamp_debug_attn_dump_logit8", "lamp_debug_attn_dump_exp2poly"]:
     for S in [0, 4096, INT_MAX]:
         call(name, VP(b0), VP(b0), VP(b0), VP(b0), I(1), I(1), I(1), I(S), I(64), I(1), I(0), F(2 ** -8),
              F(0.5), VP(b0), VP(b0), VP(b0), expect="fail")

@@ -24,7 +24,8 @@ def test_exports_every_declared_symbol(lib):
             "lamp_last_error", "lamp_release_workspace", "lamp_version",
             "lamp_debug_convert", "lamp_set_timing", "lamp_read_timing",
             "lamp_debug_attn_dump", "lamp_attn_fwd_bf16", "lamp_attn_fwd_logit8",
-            "lamp_debug_attn_dump_logit8"} <= set(names)
+            "lamp_debug_attn_dump_logit8", "lamp_attn_fwd_exp2poly", "lamp_debug_attn_dump_exp2poly",
+            "lamp_debug_exp2poly"} <= set(names)
     out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
     exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
@@ -128,6 +129,21 @@ def test_logit8_variant_rejects_before_hip(lib):
     assert d(ALIGNED, ALIGNED, ALIGNED, ALIGNED, 1, 1, 1, 64, 64, 1, 0, 0.0, 0.5, None, None, ALIGNED) == -1
     assert d(ALIGNED, ALIGNED, ALIGNED, ALIGNED, 1, 1, 1, 4096, 64, 1, 0, 0.0, 0.5, None, ALIGNED,
              ALIGNED) == -2
+
+
+def test_exp2poly_variant_rejects_before_hip(lib):
+    # the bit-reproducible variant validates its arguments as lamp_attn_fwd does
+    f = lib.lamp_attn_fwd_exp2poly
+    assert f(ALIGNED, ALIGNED, ALIGNED, ALIGNED, 1, 2, 1, 128, 96, 1, 0, 0.0039, 0.5, None) == -2
+    assert f(ALIGNED, ALIGNED, ALIGNED, ALIGNED, 1, 2, 1, 128, 128, 1, 0, 0.0039, math.nan, None) == -1
+    assert f(ALIGNED, None, ALIGNED, ALIGNED, 1, 2, 1, 128, 128, 1, 0, 0.0039, 0.5, None) == -1
+    d = lib.lamp_debug_attn_dump_exp2poly
+    assert d(ALIGNED, ALIGNED, ALIGNED, ALIGNED, 1, 1, 1, 4096, 64, 1, 0, 0.0, 0.5, None, ALIGNED,
+             ALIGNED) == -2
+    e = lib.lamp_debug_exp2poly
+    assert e(ALIGNED, -1, ALIGNED) == -1
+    assert e(None, 4, ALIGNED) == -1
+    assert e(None, 0, None) == 0
 
 
 def test_decode_rejects_before_hip(lib):

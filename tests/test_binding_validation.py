@@ -32,7 +32,7 @@ def _rejects(fn, match, **over):
     assert e.value.code == LAMP_ERR_INVALID
 
 
-FWD = [lamp.lamp_attn_fwd, lamp.lamp_attn_fwd_logit8, lamp.lamp_attn_fwd_bf16]
+FWD = [lamp.lamp_attn_fwd, lamp.lamp_attn_fwd_logit8, lamp.lamp_attn_fwd_exp2poly, lamp.lamp_attn_fwd_bf16]
 
 
 @pytest.mark.parametrize("fn", FWD, ids=lambda f: f.__name__)
@@ -90,6 +90,14 @@ def test_dump_stats_quantize_convert_rejections():
                               torch.zeros(B * HQ), torch.zeros(B * HKV))
     with pytest.raises(LampError, match="exp2 must have shape"):
         lamp.lamp_debug_convert(torch.zeros(10), exp2=torch.zeros(9))
+    with pytest.raises(LampError, match="y must have shape"):
+        lamp.lamp_debug_exp2poly(torch.zeros(10), torch.zeros(9))
+    with pytest.raises(LampError, match="must be on a GPU"):
+        lamp.lamp_debug_exp2poly(torch.zeros(10), torch.zeros(10))
+    with pytest.raises(LampError, match="acc8_out must have shape"):
+        lamp.lamp_debug_attn_dump_exp2poly(a["q"], a["k"], a["v"], a["out"], 1, 0, 2.0 ** -8, 0.5,
+                                           a["subblock_mask_out"], torch.zeros(B, HQ, S, S - 1),
+                                           torch.zeros(B, HQ, S, S, dtype=torch.int16))
 
 
 def test_kept_amax_rejections():
