@@ -518,6 +518,36 @@ def measure(lamp, torch, tensors, shape, causal, window, delta, tau, steps, warm
                 f_qk8=f_qk8, f_pv=f_pv, f_qk16=f_qk16, stats=stats, settle_steps=settle_steps)
 
 
+def graph_step_ms(lamp, torch, tensors, causal, window, delta, tau, steps):
+    """The same step captured once in a HIP graph (lamp_attn_fwd_noalloc: no
+    allocation, no memset) and replayed `steps` times; returns ms per replay,
+    or None when the workspace exceeds the entry point's fixed scratch array."""
+    qd, kd, vd, out, mask = tensors
+    try:
+        lamp.lamp_attn_fwd_noalloc(qd, kd, vd, out, causal, window, delta, tau, mask)
+    except lamp.LampError:
+        return None
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g, stream=side, capture_error_mode="relaxed"):
+            lamp.lamp_attn_fwd_noalloc(qd, kd, vd, out, causal, window, delta, tau, mask)
+    torch.cuda.current_stream().wait_stream(side)
+    for _ in range(20):
+        g.replay()
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(steps):
+        g.replay()
+    end.record()
+    torch.cuda.synchronize()
+    del g
+    return start.elapsed_time(end) / steps
+
+
 def roofline_of(m):
     """Blended matrix-core roofline of the attention kernel for one measurement."""
     f_alg = m["f_qk8"] + m["f_pv"] + m["f_qk16"]
@@ -657,6 +687,9 @@ def main():
         "recompute": {"r_sb": stats["r_sb"], "r_e": stats["r_e"], "hist_0_to_4": stats["hist"],
                       "tiles_0_1_2plus": stats["pages_buckets"]},
     }
+    # the same step as one HIP-graph replay (after the timed region, not part of `value`)
+    res["graph_ms_per_step"] = graph_step_ms(lamp, torch, tensors, causal, window, args.delta, args.tau,
+                                             args.steps)
     res["parity"] = parity
     res["cpu_baseline"] = cb
     print(json.dumps(res), flush=True)
