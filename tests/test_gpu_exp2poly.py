@@ -133,6 +133,10 @@ SMALL = [
     (1, 3, 1, 129, 64, 0, 0, 0.0, 2 ** -3, "channels", 85),
     (1, 2, 1, 70, 128, 1, 0, 2 ** -8, np.inf, "sinks", 86),
     (1, 1, 1, 1, 64, 1, 0, 2 ** -8, 2 ** -1, "plain", 87),
+    (1, 8, 1, 140, 128, 1, 0, 2 ** -8, 2 ** -2, "sinks", 89),          # G = 8
+    (2, 2, 2, 257, 64, 1, 100, 2 ** -4, 2 ** -1, "channels+drift", 90),  # D = 64, window, ragged
+    (1, 2, 1, 64, 128, 1, 0, 0.0, 0.0, "channels", 91),                 # one tile, all 16-bit
+    (1, 2, 2, 190, 256, 0, 0, 2 ** -8, 2 ** -3, "sinks", 92),           # D = 256, non-causal
 ]
 
 
@@ -144,13 +148,26 @@ def test_exp2poly_parity_small(case):
     assert_parity(rep)
 
 
-def test_exp2poly_parity_full_size():
-    """The Qwen3-8B-shaped workload in one call, sampled units against the oracle."""
-    q, k, v, _ = make_config_inputs("qwen3-8b")
+def test_exp2poly_deterministic():
+    """Two calls on the same inputs give the same bits (outputs and mask)."""
+    q, k, v = make_inputs(1, 4, 2, 300, 128, 93, "channels")
+    import mixed_precision_attention_lamp_amd as lamp
+    qd, kd, vd = to_device(q), to_device(k), to_device(v)
+    o1, m1 = lamp.attention(qd, kd, vd, True, 0, 2 ** -8, 2 ** -1, exp_poly=True)
+    o2, m2 = lamp.attention(qd, kd, vd, True, 0, 2 ** -8, 2 ** -1, exp_poly=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(m1, m2)
+
+
+@pytest.mark.parametrize("name,n", [("qwen3-8b", 8), ("gemma3-12b", 4)])
+def test_exp2poly_parity_full_size(name, n):
+    """Full-size workloads in one call each, sampled units against the oracle."""
+    q, k, v, cfg = make_config_inputs(name)
     B, Hq, S, _ = q.shape
     nT = L.n_tiles(S)
     rng = np.random.default_rng(88)
-    units = sorted({(0, 0, nT - 1), (0, Hq - 1, 0)} |
-                   {(0, int(rng.integers(Hq)), int(rng.integers(nT))) for _ in range(6)})
-    rep = compare(q, k, v, 1, 0, 2 ** -8, 2 ** -1, units=units, label="exp2poly qwen3-8b", exp_poly=True)
+    units = sorted({(0, 0, nT - 1), (B - 1, Hq - 1, 0)} |
+                   {(int(rng.integers(B)), int(rng.integers(Hq)), int(rng.integers(nT))) for _ in range(n - 2)})
+    rep = compare(q, k, v, cfg["causal"], cfg["window"], 2 ** -8, 2 ** -1, units=units,
+                  label=f"exp2poly {name}", exp_poly=True)
     assert_parity(rep)
