@@ -652,6 +652,10 @@ def main():
     prep_bytes = 2.0 * (nq + nk) + 3.0 * nk + 4.0 * nk
     t_mfma = m["f_qk8"] / PEAK_FP8 + (m["f_pv"] + m["f_qk16"]) / PEAK_BF16
     t_roof = t_mfma + quant_bytes / PEAK_HBM
+    # the stricter form: the attention kernel bounded by the larger of its
+    # matrix-core time and its minimum HBM traffic (Q8, Q16 and the fp32
+    # output; K8, K16 and V: 7 Nq + 5 Nk bytes), plus the quantisation pass
+    t_roof_strict = max(t_mfma, (7.0 * nq + 5.0 * nk) / PEAK_HBM) + quant_bytes / PEAK_HBM
     valu_ceiling = None
     vrec = _record(VALU_CEILING, args, kernel_source_hash())
     if vrec is not None:
@@ -680,6 +684,8 @@ def main():
                      "unit": "TFLOP/s", "frac": achieved / blended_peak, "traffic": traffic},
         "valu_ceiling": valu_ceiling,
         "blended_roofline_frac": t_roof / (ms_per_step * 1e-3),
+        "strict_roofline_frac": t_roof_strict / (ms_per_step * 1e-3),
+        "executed_tflops": (f_nom + m["f_qk16"]) / (attn_ms_avg * 1e-3) / 1e12,
         "kernel_ms": {"attention": attn_ms_avg, "quantise_and_transpose": prep_ms_avg},
         "prep_hbm": {"bytes": prep_bytes, "GB/s": prep_bytes / (prep_ms_avg * 1e-3) / 1e9,
                      "frac": prep_bytes / (prep_ms_avg * 1e-3) / PEAK_HBM},
