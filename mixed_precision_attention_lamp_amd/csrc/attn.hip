@@ -86,6 +86,7 @@ struct AttnArgs {
     int n_rg;            // row-block groups
     int paired;          // 1: a workgroup runs row-block groups n_rg-1-level and level
     int n_wg;
+    int rot_shift;       // unpaired: level l shifts the unit order by l >> rot_shift
 };
 
 template <int D, bool kPlain = false>
@@ -151,21 +152,22 @@ __global__ __launch_bounds__(kThreads, 1) void lamp_attn_kernel(AttnArgs a) {
     const int wib = wave % C::kWavesPerBlock;   // rows wib*kWaveRows .. of that block
 
     // ---- workgroup -> (batch, kv head, head group) unit and row-block group(s)
-    // Workgroups are dispatched in index order, round-robin over the XCDs.
-    // Index order is longest (causal) rows first; consecutive indices are
-    // consecutive units, so with 8 units per level each XCD keeps to one unit
-    // and its K/V tiles stay in that XCD's L2.  Unpaired launches with D <= 128
-    // offset the units by the level's parity, so that each XCD alternates
-    // between two units: units differ in how much they recompute, and two
-    // share the load while each K/V tile is fetched into two L2s only.  At
-    // D = 256 a unit's tiles outgrow an XCD's L2 by themselves, and one unit
-    // per XCD measured faster.
+    // Workgroups are dispatched in index order, round-robin over the XCDs
+    // (index i to XCD i mod 8), so each XCD receives a fixed eighth of them
+    // whatever their cost.  Index order is longest (causal) rows first;
+    // consecutive indices are consecutive units, so with 8 units per level
+    // each XCD would keep to one unit and its K/V tiles would stay in that
+    // XCD's L2 -- but units differ in how much they recompute (their keys
+    // differ), and an XCD holding a heavy unit would finish last.  Unpaired
+    // launches therefore shift the unit order by one every 2^rot_shift levels:
+    // each XCD cycles through the units, a run of 2^rot_shift consecutive
+    // row blocks of one unit at a time (those share most K/V tiles, in L2).
     const int wg = blockIdx.x;
     const int n_hg = a.G / a.heads_per_wg;
     const int n_lv = a.paired ? (a.n_rg + 1) / 2 : a.n_rg;
     const int n_u = a.n_wg / n_lv;
     const int level = wg / n_u;
-    int u = (wg % n_u + (a.paired || D == 256 ? 0 : (level & 1))) % n_u;
+    int u = (wg % n_u + (a.paired ? 0 : level >> a.rot_shift)) % n_u;
     const int hg = u % n_hg;
     u /= n_hg;
     const int hk = u % a.Hkv;
@@ -964,6 +966,10 @@ hipError_t launch_d(const Shape& sh, const AttnParams& p, hipStream_t st) {
     const int n_u = sh.B * sh.Hkv * (a.G / a.heads_per_wg);
     a.paired = Cfg<D>::kPP && p.causal && p.window == 0 && n_u * a.n_rg <= 2 * cu_count() ? 1 : 0;
     a.n_wg = n_u * (a.paired ? (a.n_rg + 1) / 2 : a.n_rg);
+    // the run length of one unit on an XCD (measured: 16 row blocks at D = 256
+    // global and with few units, 4 with a window at D = 256, 1 with 16 units
+    // or more, where an XCD holds several units at every level anyway)
+    a.rot_shift = D == 256 ? (p.window > 0 ? 2 : 4) : (n_u >= 16 ? 0 : 4);
     size_t lds = Cfg<D>::kLdsBytes;
     const bool dump = p.dump_s != nullptr && p.dump_p != nullptr;
     using Fn = void (*)(AttnArgs);
