@@ -692,8 +692,13 @@ def main():
                       "tiles_0_1_2plus": stats["pages_buckets"]},
     }
     # the same step as one HIP-graph replay (after the timed region, not part of `value`)
-    res["graph_ms_per_step"] = graph_step_ms(lamp, torch, tensors, causal, window, args.delta, args.tau,
-                                             args.steps)
+    try:
+        res["graph_ms_per_step"] = graph_step_ms(lamp, torch, tensors, causal, window, args.delta, args.tau,
+                                                 args.steps)
+    except Exception as e:   # an informational figure: never lose the line for it
+        print(f"bench.py: graph replay not timed ({e})", file=sys.stderr)
+        torch.cuda.synchronize()
+        res["graph_ms_per_step"] = None
     res["parity"] = parity
     res["cpu_baseline"] = cb
     print(json.dumps(res), flush=True)
