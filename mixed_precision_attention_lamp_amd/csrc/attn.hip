@@ -286,6 +286,12 @@ __global__ __launch_bounds__(kThreads, 1) void lamp_attn_kernel(AttnArgs a) {
     };
 
     // ---- prologue: this wave's Q16 operand into registers, Q8 rows into its LDS ----
+    if constexpr (!C::kPP) {
+        // one-loop schedule (D = 256): the first tile's copies go out before
+        // the Q loads, so that their latencies overlap
+        dma_qk(t_begin, t_begin & 1);
+        if constexpr (!kPlain) dma_k16(t_begin, t_begin & 1);
+    }
     float m_run[kQG], c8 = 0.0f, inv_c8 = 0.0f, a2 = 0.0f, c8_log = 0.0f;
     const float c16 = (float)a.l_d;
     v8bf qb[C::kDC][kQG];     // bf16 operand of 16-query group qg, 32-deep step ch
@@ -847,8 +853,6 @@ __global__ __launch_bounds__(kThreads, 1) void lamp_attn_kernel(AttnArgs a) {
         constexpr int kAfterK8 = kK16Copies + kVtCh;    // copies issued after a tile's K8 copies
         static_assert(kAfterK8 < 16, "vmcnt immediate");
         static_assert(kAfterK8 <= C::kDB / 2, "one copy per four output blocks of P.V");
-        dma_qk(t_begin, t_begin & 1);
-        if constexpr (!kPlain) dma_k16(t_begin, t_begin & 1);
         wait_copies();
         lds_barrier();
         if (work(t_begin)) qk(S, t_begin & 1);
