@@ -594,7 +594,7 @@ def main():
                     help="time the (delta, tau) grid and the two endpoints instead of one point")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
+        print(f"bench.py: the kernels run on one GPU only (asked for --gpus {args.gpus}); "
               "the path is single-GPU by design", file=sys.stderr)
         sys.exit(2)
     if args.copy_calibrate:
