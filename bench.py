@@ -37,12 +37,12 @@ COPY_BYTES = 1 << 30       # size of the calibration copy
 # counter's reading for a plain copy of COPY_BYTES (profiles/
 # attn_qwen3_8b_hbm_traffic.md, attn_gemma3_12b_counters.md).  Valid only for
 # the kernel source whose hash is recorded; any change to it makes the figure
-# null.  (The qwen3-8b figures were taken on a source whose D = 128
-# kernels compile to the same instructions as this one's.)
+# null.  (Taken on sources that compile to the same instructions as this
+# one: later edits changed comments, or only other kernels.)
 TRAFFIC = [
-    {"kernel_hash": "5f1db55337afbaa0", "workload": "qwen3-8b", "delta": 2.0 ** -8, "tau": 2.0 ** -1,
+    {"kernel_hash": "4dc6632fac05b9a8", "workload": "qwen3-8b", "delta": 2.0 ** -8, "tau": 2.0 ** -1,
      "bytes_per_launch": 130208276.1},
-    {"kernel_hash": "5f1db55337afbaa0", "workload": "gemma3-12b", "delta": 2.0 ** -8, "tau": 2.0 ** -1,
+    {"kernel_hash": "4dc6632fac05b9a8", "workload": "gemma3-12b", "delta": 2.0 ** -8, "tau": 2.0 ** -1,
      "bytes_per_launch": 585246394.0},
 ]
 
@@ -54,9 +54,9 @@ TRAFFIC = [
 # of issue), i.e. the launch time if the vector units were never idle.  Valid
 # only for the recorded kernel source.
 VALU_CEILING = [
-    {"kernel_hash": "5f1db55337afbaa0", "workload": "qwen3-8b", "delta": 2.0 ** -8, "tau": 2.0 ** -1,
+    {"kernel_hash": "4dc6632fac05b9a8", "workload": "qwen3-8b", "delta": 2.0 ** -8, "tau": 2.0 ** -1,
      "cycles_per_simd": 208688.3, "clock_hz": 2.4e9, "source": "profiles/attn_qwen3_8b_sq_counters.md"},
-    {"kernel_hash": "5f1db55337afbaa0", "workload": "gemma3-12b", "delta": 2.0 ** -8, "tau": 2.0 ** -1,
+    {"kernel_hash": "4dc6632fac05b9a8", "workload": "gemma3-12b", "delta": 2.0 ** -8, "tau": 2.0 ** -1,
      "cycles_per_simd": 586847.4, "clock_hz": 2.4e9, "source": "profiles/attn_gemma3_12b_counters.md"},
 ]
 

@@ -285,10 +285,11 @@ __global__ __launch_bounds__(kThreads, 1) void lamp_attn_kernel(AttnArgs a) {
         }
     };
 
-    // ---- prologue: this wave's Q16 operand into registers, Q8 rows into its LDS ----
+    // ---- prologue: this wave's Q16 and Q8 operands into registers ----------------------
     if constexpr (!C::kPP) {
         // one-loop schedule (D = 256): the first tile's copies go out before
-        // the Q loads, so that their latencies overlap
+        // the Q loads, so that their latencies overlap (measured slower in the
+        // ping-pong schedule, whose prologue copies five tiles)
         dma_qk(t_begin, t_begin & 1);
         if constexpr (!kPlain) dma_k16(t_begin, t_begin & 1);
     }
