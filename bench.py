@@ -176,7 +176,7 @@ def single_core_tiny():
     return time.perf_counter() - t0
 
 
-def cpu_baseline(q, k, v, cfg, delta, tau, budget_s, cores, with_parity=True):
+def cpu_baseline(q, k, v, cfg, delta, tau, budget_s, cores, with_parity=True, exp_poly=False):
     """Time the oracle on sampled units of the same workload (reported
     baseline), then (untimed) compute the parity protocol's expectation of
     the units the bench compares with the device output afterwards."""
@@ -186,7 +186,7 @@ def cpu_baseline(q, k, v, cfg, delta, tau, budget_s, cores, with_parity=True):
     from oracle import lamp as L
     threadpool_limits(1)
     tiny_s = single_core_tiny()
-    _CTX = L.prepare(q, k, v, cfg["causal"], cfg["window"], delta, tau)
+    _CTX = L.prepare(q, k, v, cfg["causal"], cfg["window"], delta, tau, exp_poly=exp_poly)
     B, Hq, S, D = q.shape
     nT = L.n_tiles(S)
     rng = np.random.default_rng(123)
@@ -590,6 +590,9 @@ def main():
     ap.add_argument("--copy-calibrate", action="store_true")
     ap.add_argument("--kept-amax", action="store_true",
                     help="decode workloads: K scales from kept maxima (lamp_attn_decode_with_amax)")
+    ap.add_argument("--exp2poly", action="store_true",
+                    help="prefill workloads: the variant with the bit-reproducible polynomial exp2 "
+                         "(lamp_attn_fwd_exp2poly), against the oracle's reading of it")
     ap.add_argument("--grid", action="store_true",
                     help="time the (delta, tau) grid and the two endpoints instead of one point")
     args = ap.parse_args()
@@ -617,7 +620,8 @@ def main():
     if not args.no_cpu_baseline and not args.grid:
         # the machine's CPU share is 16 threads per GPU, whatever the host shows
         cores = max(1, min(len(os.sched_getaffinity(0)), 16))
-        cb, expectations = cpu_baseline(q, k, v, cfg, args.delta, args.tau, args.cpu_budget, cores)
+        cb, expectations = cpu_baseline(q, k, v, cfg, args.delta, args.tau, args.cpu_budget, cores,
+                                        exp_poly=args.exp2poly)
         cb.pop("wall_s", None)
 
     import torch
@@ -638,7 +642,7 @@ def main():
         run_grid(args, lamp, torch, tensors, shape, causal, window, cfg)
         return
     m = measure(lamp, torch, tensors, shape, causal, window, args.delta, args.tau, args.steps,
-                args.warmup, settle_ms=args.settle_ms)
+                args.warmup, settle_ms=args.settle_ms, exp_poly=args.exp2poly)
     parity = parity_block(expectations, out.cpu().numpy(), mask.cpu().numpy()) if expectations else None
     ms_per_step, attn_ms_avg, prep_ms_avg = m["ms_per_step"], m["attn_ms"], m["prep_ms"]
     stats, f_nom = m["stats"], m["f_nom"]
@@ -656,12 +660,13 @@ def main():
     # output; K8, K16 and V: 7 Nq + 5 Nk bytes), plus the quantisation pass
     t_roof_strict = max(t_mfma, (7.0 * nq + 5.0 * nk) / PEAK_HBM) + quant_bytes / PEAK_HBM
     valu_ceiling = None
-    vrec = _record(VALU_CEILING, args, kernel_source_hash())
+    # the records were taken on the default kernel, not on the variant
+    vrec = None if args.exp2poly else _record(VALU_CEILING, args, kernel_source_hash())
     if vrec is not None:
         t_valu = vrec["cycles_per_simd"] / vrec["clock_hz"]
         valu_ceiling = {"bound": "valu", "ceiling_ms": t_valu * 1e3, "frac": t_valu / (attn_ms_avg * 1e-3),
                         "source": "instruction counters, " + vrec["source"]}
-    trec = _record(TRAFFIC, args, kernel_source_hash())
+    trec = None if args.exp2poly else _record(TRAFFIC, args, kernel_source_hash())
     traffic = trec["bytes_per_launch"] if trec is not None else None
     res = {
         "metric": METRIC,
@@ -678,7 +683,9 @@ def main():
         "data": "synthetic",
         "config": {"workload": f"{args.workload}: {cfg['desc']}", "B": B, "Hq": Hq, "Hkv": Hkv,
                    "S": S, "D": D, "causal": causal, "window": window,
-                   "delta": args.delta, "tau": args.tau},
+                   "delta": args.delta, "tau": args.tau,
+                   "exp2": "bit-reproducible polynomial (lamp_attn_fwd_exp2poly)" if args.exp2poly
+                   else "hardware v_exp_f32"},
         "roofline": {"bound": "mfma", "achieved": achieved / 1e12, "peak": blended_peak / 1e12,
                      "unit": "TFLOP/s", "frac": achieved / blended_peak, "traffic": traffic},
         "valu_ceiling": valu_ceiling,
@@ -694,6 +701,8 @@ def main():
     }
     # the same step as one HIP-graph replay (after the timed region, not part of `value`)
     try:
+        if args.exp2poly:
+            raise RuntimeError("the graph replays the default entry point")
         res["graph_ms_per_step"] = graph_step_ms(lamp, torch, tensors, causal, window, args.delta, args.tau,
                                                  args.steps)
     except Exception as e:   # an informational figure: never lose the line for it
