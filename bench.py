@@ -608,8 +608,14 @@ def main():
 
     q, k, v, cfg = make_config_inputs(args.workload)
     if "Sq" in cfg:
+        if args.exp2poly:
+            print("bench.py: --exp2poly applies to the prefill workloads only", file=sys.stderr)
+            sys.exit(2)
         run_decode(args, cfg, q, k, v)
         return
+    if args.exp2poly and args.grid:
+        print("bench.py: --grid already times the polynomial-exp2 points; drop --exp2poly", file=sys.stderr)
+        sys.exit(2)
     B, Hq, S, D = q.shape
     Hkv = k.shape[1]
     causal, window = cfg["causal"], cfg["window"]
